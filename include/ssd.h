@@ -1,0 +1,126 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) SSD layer forward library, libssd.so.
+ *
+ * The operation is the forward pass of the SSD (structured state space duality)
+ * layer, as defined on the page "Transformers are SSMs: Generalized Models and
+ * Efficient Algorithms Through Structured State Space Duality" (paper summary):
+ *   - section 2.4 / section 5.1: per head a scalar-identity SSM, A_t = a_t I,
+ *     with head dimension P and state size N:
+ *         h_t = a_t h_{t-1} + x_t B_t^T      (h_t is P x N)
+ *         y_t = h_t C_t                      (y_t has P entries)
+ *     equivalently Y = (L o C B^T) X with the 1-semiseparable mask
+ *     L[i][j] = a_{j+1} ... a_i (i >= j), section 5.1;
+ *   - section 6 and Listing 1: it is computed by the block (chunk)
+ *     decomposition of that semiseparable matrix, with chunk length chunk_len;
+ *   - section 7.2: heads are grouped, head h reads B and C of group h / (H/G);
+ *   - section 8.3: a packed batch of variable-length sequences passes no state
+ *     between sequences.
+ * The result does not depend on chunk_len except through rounding.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensors are row-major and contiguous; "device" pointers are HIP device
+ *     memory of the current device; every pointer must be 16-byte aligned.
+ *   - a_t = exp(logA_t); logA is float32, finite and <= 0 (not checked: NaN or
+ *     positive values propagate into the outputs).
+ *   - The state before token 0 of a sequence is init_state (zeros when NULL); it
+ *     is decayed by a_0.  final_state is the state after the last token.
+ *   - The caller owns every buffer, including the workspace.  The library never
+ *     allocates device memory, keeps no state between calls, never synchronizes,
+ *     and enqueues all work on the given stream; results are valid once that
+ *     stream reaches the enqueued work.  Calls with distinct workspaces may run
+ *     concurrently.
+ *   - Errors are returned as ssd_status codes; arguments are validated on the
+ *     host before anything is enqueued, so a failing call enqueues nothing.
+ *     Device-resident values (logA, seq_offsets contents) are not validated.
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ssd_status {
+    SSD_OK = 0,
+    SSD_ERR_INVALID_ARG = -1,  /* null/misaligned/aliased pointer, bad dimension      */
+    SSD_ERR_UNSUPPORTED = -2,  /* dtype, chunk_len, headdim or dstate outside support */
+    SSD_ERR_WORKSPACE = -3,    /* workspace smaller than ssd_workspace_bytes()        */
+    SSD_ERR_HIP = -4           /* a HIP runtime call or kernel launch failed          */
+} ssd_status;
+
+typedef enum ssd_dtype {
+    SSD_DTYPE_F32 = 0,         /* X, B, C, Y in float32, fp32 MFMA                     */
+    SSD_DTYPE_BF16 = 1         /* X, B, C, Y in bfloat16, bf16 MFMA, fp32 accumulation */
+} ssd_dtype;
+
+/* Problem description.
+ *   batch     b  >= 1   rows of the batch (must be 1 when seq_offsets is given)
+ *   seqlen    T  >= 1   tokens per batch row (total packed tokens with seq_offsets)
+ *   nheads    H  >= 1
+ *   headdim   P         multiple of 16, 16 <= P <= 256
+ *   dstate    N         multiple of 16, 16 <= N <= 256
+ *   ngroups   G  >= 1   H % G == 0
+ *   chunk_len Q         one of 16, 32, 64, 128, 256 (the last chunk of a sequence
+ *                       may be shorter)
+ *   nseq                number of sequences: == batch without seq_offsets, else the
+ *                       number of packed sequences (>= 1)
+ *   dtype               an ssd_dtype value                                          */
+typedef struct ssd_problem {
+    int64_t batch;
+    int64_t seqlen;
+    int64_t nheads;
+    int64_t headdim;
+    int64_t dstate;
+    int64_t ngroups;
+    int64_t chunk_len;
+    int64_t nseq;
+    int32_t dtype;
+    int32_t reserved;   /* must be 0 */
+} ssd_problem;
+
+/* Checks a problem description without touching any device.
+ * Returns SSD_OK, SSD_ERR_INVALID_ARG (p NULL, a dimension out of range,
+ * H % G != 0, nseq inconsistent) or SSD_ERR_UNSUPPORTED. */
+int ssd_check_problem(const ssd_problem* p);
+
+/* Device workspace in bytes that ssd_forward needs for this problem, or 0 when
+ * ssd_check_problem(p) != SSD_OK.  Depends only on *p.  Host-only, no HIP call. */
+size_t ssd_workspace_bytes(const ssd_problem* p);
+
+/* The SSD forward pass (passages above).  Arguments, all device pointers unless noted:
+ *   p            host pointer to the problem description
+ *   X            [b, T, H, P]      dtype          input x
+ *   logA         [b, T, H]         float32        log of the per-token, per-head decay a_t
+ *   B            [b, T, G, N]      dtype          input projection B_t
+ *   C            [b, T, G, N]      dtype          output projection C_t
+ *   init_state   [nseq, H, P, N]   float32        state before token 0, or NULL for zeros
+ *   seq_offsets  [nseq + 1]        int32          packed sequence boundaries, or NULL;
+ *                                                 seq_offsets[0] = 0, seq_offsets[nseq] = T,
+ *                                                 non-decreasing (empty sequences allowed:
+ *                                                 their final state is their init state)
+ *   Y            [b, T, H, P]      dtype (out)    y, rounded to dtype (round to nearest even)
+ *   final_state  [nseq, H, P, N]   float32 (out)  state after the last token, or NULL to skip
+ *   workspace    >= ssd_workspace_bytes(p) bytes of device scratch, 256-byte aligned
+ *   hip_stream   hipStream_t to enqueue on (NULL = the default stream)
+ * Y and final_state must not overlap any input or each other.
+ * Returns SSD_OK or an ssd_status error code (see the enum). */
+int ssd_forward(const ssd_problem* p, const void* X, const float* logA, const void* B,
+                const void* C, const float* init_state, const int32_t* seq_offsets, void* Y,
+                float* final_state, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Static English text for a status code (never NULL). */
+const char* ssd_status_string(int status);
+
+/* ABI revision of this header; bumped on any incompatible change. */
+int ssd_abi_version(void);
+
+#define SSD_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H */

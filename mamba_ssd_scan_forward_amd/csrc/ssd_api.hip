@@ -1,0 +1,275 @@
+// ssd_api.hip -- host side of libssd.so: argument checks, workspace plan and the
+// two kernel launches of the SSD forward (declarations and contract in ssd.h).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "ssd.h"
+#include "ssd_kernels.h"
+
+namespace {
+
+constexpr int kLdsMax = 160 * 1024;   // LDS per workgroup on gfx950
+constexpr int kWalkThreads = 512;
+constexpr int kPrepThreads = 256;
+
+struct Plan {
+    int dtype;
+    int Q, Qp, nlb, ntile;
+    int PT, NP, ptiles, qb;
+    int64_t nslots, nitems;
+    size_t cs_off, cb_off, ws_bytes;
+    int lds_bytes, xs_off, xts_off, bs_off, hs_off, cs_lds_off;
+};
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int check_problem(const ssd_problem* p) {
+    if (!p) return SSD_ERR_INVALID_ARG;
+    if (p->batch < 1 || p->seqlen < 1 || p->nheads < 1 || p->headdim < 1 || p->dstate < 1 ||
+        p->ngroups < 1 || p->chunk_len < 1 || p->reserved != 0)
+        return SSD_ERR_INVALID_ARG;
+    if (p->nheads % p->ngroups != 0) return SSD_ERR_INVALID_ARG;
+    if (p->nseq < 1) return SSD_ERR_INVALID_ARG;
+    // int32 indexing limits of the kernels (token rows, element offsets use int64)
+    if (p->batch * p->seqlen > (int64_t)1 << 30 || p->nheads > (1 << 20) || p->nseq > (1 << 24))
+        return SSD_ERR_UNSUPPORTED;
+    if (p->dtype != SSD_DTYPE_F32 && p->dtype != SSD_DTYPE_BF16) return SSD_ERR_UNSUPPORTED;
+    const int64_t Q = p->chunk_len;
+    if (Q != 16 && Q != 32 && Q != 64 && Q != 128 && Q != 256) return SSD_ERR_UNSUPPORTED;
+    if (p->headdim % 16 != 0 || p->headdim > 256) return SSD_ERR_UNSUPPORTED;
+    if (p->dstate % 16 != 0 || p->dstate > 256) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+int lds_layout(Plan* pl, int es) {
+    const int pad = 16 / es;
+    const int XS = pl->PT + pad, BS = pl->NP + pad, HS = pl->NP + pad;
+    pl->xs_off = 0;
+    pl->xts_off = pl->xs_off + pl->Qp * XS * es;
+    pl->bs_off = pl->xts_off + pl->Qp * XS * es;
+    pl->hs_off = pl->bs_off + pl->qb * BS * es;
+    pl->cs_lds_off = pl->hs_off + pl->PT * HS * es;
+    pl->lds_bytes = pl->cs_lds_off + pl->Qp * 4;
+    return pl->lds_bytes;
+}
+
+// Workspace and launch plan.  `nseq_total` slots: batch mode has batch * ceil(T/Q)
+// chunks; a packed batch has at most ceil(T/Q) + nseq (one ragged chunk per sequence).
+int make_plan(const ssd_problem* p, Plan* pl) {
+    const int rc = check_problem(p);
+    if (rc != SSD_OK) return rc;
+    pl->dtype = p->dtype;
+    const int es = p->dtype == SSD_DTYPE_BF16 ? 2 : 4;
+    pl->Q = (int)p->chunk_len;
+    pl->Qp = (pl->Q + 31) / 32 * 32;
+    pl->nlb = pl->Qp / 32;
+    pl->ntile = pl->nlb * (pl->nlb + 1) / 2;
+    const int N = (int)p->dstate, P = (int)p->headdim;
+    pl->NP = N <= 32 ? 32 : N <= 64 ? 64 : N <= 128 ? 128 : 256;
+    pl->PT = (p->dtype == SSD_DTYPE_BF16 && P > 32) ? 64 : 32;
+    pl->ptiles = (P + pl->PT - 1) / pl->PT;
+    const int64_t nc = (p->seqlen + pl->Q - 1) / pl->Q;
+    // slots are sized for the larger of the two numberings, so one plan serves
+    // a call with or without seq_offsets
+    const int64_t slots_batch = p->batch * nc;
+    const int64_t slots_packed = nc + p->nseq;
+    pl->nslots = slots_batch > slots_packed ? slots_batch : slots_packed;
+    pl->nitems = p->nseq * p->nheads * pl->ptiles;
+    if (pl->nitems > ((int64_t)1 << 31) - 1) return SSD_ERR_UNSUPPORTED;
+    pl->cs_off = 0;
+    const size_t cs_bytes = (size_t)pl->nslots * p->nheads * pl->Qp * sizeof(float);
+    pl->cb_off = align_up(pl->cs_off + cs_bytes, 256);
+    const size_t cb_bytes = (size_t)pl->nslots * p->ngroups * pl->ntile * 1024 * es;
+    pl->ws_bytes = align_up(pl->cb_off + cb_bytes, 256);
+    pl->qb = pl->Qp;
+    while (lds_layout(pl, es) > kLdsMax && pl->qb > 32) pl->qb -= 32;
+    if (pl->lds_bytes > kLdsMax) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+typedef void (*walk_fn)(ssd::WalkArgs);
+typedef void (*prep_fn)(ssd::PrepArgs);
+
+template <typename T, int PT, int NP>
+walk_fn walk_instance() { return ssd::ssd_walk_kernel<T, PT, NP>; }
+
+template <typename T>
+walk_fn pick_walk(int PT, int NP) {
+    if (PT == 32) {
+        switch (NP) {
+            case 32: return walk_instance<T, 32, 32>();
+            case 64: return walk_instance<T, 32, 64>();
+            case 128: return walk_instance<T, 32, 128>();
+            case 256: return walk_instance<T, 32, 256>();
+        }
+    } else if (PT == 64) {
+        switch (NP) {
+            case 32: return walk_instance<T, 64, 32>();
+            case 64: return walk_instance<T, 64, 64>();
+            case 128: return walk_instance<T, 64, 128>();
+            case 256: return walk_instance<T, 64, 256>();
+        }
+    }
+    return nullptr;
+}
+
+// Raise the dynamic-LDS limit of a walk kernel to the full 160 KiB, once per kernel
+// per process (setting it twice is harmless, so a race only repeats the call).
+int ensure_lds_limit(const void* fn) {
+    static std::atomic<const void*> done[32] = {};
+    for (auto& d : done)
+        if (d.load(std::memory_order_acquire) == fn) return SSD_OK;
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax) != hipSuccess)
+        return SSD_ERR_HIP;
+    for (auto& d : done) {
+        const void* expected = nullptr;
+        if (d.compare_exchange_strong(expected, fn, std::memory_order_acq_rel)) break;
+        if (expected == fn) break;
+    }
+    return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+const char* ssd_status_string(int status) {
+    switch (status) {
+        case SSD_OK: return "ok";
+        case SSD_ERR_INVALID_ARG: return "invalid argument";
+        case SSD_ERR_UNSUPPORTED: return "unsupported problem (dtype, chunk_len, headdim or dstate)";
+        case SSD_ERR_WORKSPACE: return "workspace too small";
+        case SSD_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int ssd_check_problem(const ssd_problem* p) {
+    if (!p) return SSD_ERR_INVALID_ARG;
+    Plan pl;
+    return make_plan(p, &pl);
+}
+
+size_t ssd_workspace_bytes(const ssd_problem* p) {
+    Plan pl;
+    if (make_plan(p, &pl) != SSD_OK) return 0;
+    return pl.ws_bytes;
+}
+
+int ssd_forward(const ssd_problem* p, const void* X, const float* logA, const void* B,
+                const void* C, const float* init_state, const int32_t* seq_offsets, void* Y,
+                float* final_state, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    Plan pl;
+    int rc = make_plan(p, &pl);
+    if (rc != SSD_OK) return rc;
+    if (!X || !logA || !B || !C || !Y || !workspace) return SSD_ERR_INVALID_ARG;
+    if (seq_offsets) {
+        if (p->batch != 1) return SSD_ERR_INVALID_ARG;
+    } else if (p->nseq != p->batch) {
+        return SSD_ERR_INVALID_ARG;
+    }
+    const void* ptrs[] = {X, logA, B, C, init_state, seq_offsets, Y, final_state};
+    for (const void* q : ptrs)
+        if (q && !aligned16(q)) return SSD_ERR_INVALID_ARG;
+    if (((uintptr_t)workspace & 255u) != 0) return SSD_ERR_INVALID_ARG;
+    const size_t es = p->dtype == SSD_DTYPE_BF16 ? 2 : 4;
+    const int64_t b = p->batch, T = p->seqlen, H = p->nheads, P = p->headdim, N = p->dstate,
+                  G = p->ngroups;
+    const size_t nx = (size_t)(b * T * H * P) * es;
+    const size_t na = (size_t)(b * T * H) * sizeof(float);
+    const size_t nbc = (size_t)(b * T * G * N) * es;
+    const size_t ns = (size_t)(p->nseq * H * P * N) * sizeof(float);
+    const size_t no = seq_offsets ? (size_t)(p->nseq + 1) * sizeof(int32_t) : 0;
+    // outputs must not overlap inputs, each other or the workspace
+    const void* ins[] = {X, logA, B, C, init_state, seq_offsets, workspace};
+    const size_t nin[] = {nx, na, nbc, nbc, init_state ? ns : 0, no, workspace_bytes};
+    for (int i = 0; i < 7; ++i) {
+        if (overlap(Y, nx, ins[i], nin[i])) return SSD_ERR_INVALID_ARG;
+        if (final_state && overlap(final_state, ns, ins[i], nin[i])) return SSD_ERR_INVALID_ARG;
+    }
+    if (final_state && overlap(Y, nx, final_state, ns)) return SSD_ERR_INVALID_ARG;
+    if (workspace_bytes < pl.ws_bytes) return SSD_ERR_WORKSPACE;
+
+    walk_fn walk = p->dtype == SSD_DTYPE_BF16 ? pick_walk<__bf16>(pl.PT, pl.NP)
+                                              : pick_walk<float>(pl.PT, pl.NP);
+    prep_fn prep = p->dtype == SSD_DTYPE_BF16 ? ssd::ssd_prep_kernel<__bf16>
+                                              : ssd::ssd_prep_kernel<float>;
+    if (!walk) return SSD_ERR_UNSUPPORTED;
+    rc = ensure_lds_limit(reinterpret_cast<const void*>(walk));
+    if (rc != SSD_OK) return rc;
+
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    float* cs = reinterpret_cast<float*>(ws + pl.cs_off);
+    void* cb = ws + pl.cb_off;
+    // slots actually addressed by this call
+    const int64_t nc = (T + pl.Q - 1) / pl.Q;
+    const int64_t nslots = seq_offsets ? nc + p->nseq : b * nc;
+
+    ssd::PrepArgs pa;
+    pa.logA = logA;
+    pa.B = B;
+    pa.C = C;
+    pa.seq_offsets = seq_offsets;
+    pa.cs = cs;
+    pa.cb = cb;
+    pa.T = T;
+    pa.H = (int)H;
+    pa.N = (int)N;
+    pa.G = (int)G;
+    pa.Q = pl.Q;
+    pa.Qp = pl.Qp;
+    pa.ntile = pl.ntile;
+    pa.nseq = (int)p->nseq;
+    pa.hblocks = (int)((H + 3) / 4);
+    pa.cs_blocks = (int)(nslots * pa.hblocks);
+    const int64_t prep_blocks = nslots * pa.hblocks + nslots * G;
+    if (prep_blocks > INT32_MAX) return SSD_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(prep, dim3((unsigned)prep_blocks), dim3(kPrepThreads), 0, stream, pa);
+
+    ssd::WalkArgs wa;
+    wa.X = X;
+    wa.B = B;
+    wa.C = C;
+    wa.init = init_state;
+    wa.seq_offsets = seq_offsets;
+    wa.Y = Y;
+    wa.final_state = final_state;
+    wa.cs = cs;
+    wa.cb = cb;
+    wa.T = T;
+    wa.H = (int)H;
+    wa.P = (int)P;
+    wa.N = (int)N;
+    wa.G = (int)G;
+    wa.Q = pl.Q;
+    wa.Qp = pl.Qp;
+    wa.ntile = pl.ntile;
+    wa.nseq = (int)p->nseq;
+    wa.ptiles = pl.ptiles;
+    wa.nitems = (int)pl.nitems;
+    wa.qb = pl.qb;
+    wa.xs_off = pl.xs_off;
+    wa.xts_off = pl.xts_off;
+    wa.bs_off = pl.bs_off;
+    wa.hs_off = pl.hs_off;
+    wa.cs_off = pl.cs_lds_off;
+    hipLaunchKernelGGL(walk, dim3((unsigned)pl.nitems), dim3(kWalkThreads), pl.lds_bytes, stream, wa);
+    if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,135 @@
+"""The C-ABI boundary without a GPU: the library loads, exports every symbol that
+include/ssd.h declares, sizes workspaces, and rejects bad arguments on the host
+before anything is enqueued (no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mamba_ssd_scan_forward_amd as ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ssd.lib_path()),
+                                reason="libssd.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(["ssd_abi_version", "ssd_check_problem", "ssd_forward",
+                                           "ssd_status_string", "ssd_workspace_bytes"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(ssd.lib_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_and_status_strings():
+    assert ssd.ssd_abi_version() == ssd.ABI_VERSION
+    for code in (0, -1, -2, -3, -4):
+        assert ssd.ssd_status_string(code)
+    assert ssd.ssd_status_string(12345) == "unknown status"
+
+
+def prob(**kw):
+    d = dict(batch=2, seqlen=300, nheads=4, headdim=64, dstate=128, ngroups=2, chunk_len=64,
+             nseq=2, dtype=ssd.SSD_DTYPE_BF16)
+    d.update(kw)
+    return ssd.problem_for(**d)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, ssd.SSD_OK),
+    (dict(batch=0), ssd.SSD_ERR_INVALID_ARG),
+    (dict(seqlen=0), ssd.SSD_ERR_INVALID_ARG),
+    (dict(nheads=3), ssd.SSD_ERR_INVALID_ARG),           # H % G != 0
+    (dict(nseq=0), ssd.SSD_ERR_INVALID_ARG),
+    (dict(dtype=7), ssd.SSD_ERR_UNSUPPORTED),
+    (dict(chunk_len=48), ssd.SSD_ERR_UNSUPPORTED),
+    (dict(chunk_len=512), ssd.SSD_ERR_UNSUPPORTED),
+    (dict(headdim=40), ssd.SSD_ERR_UNSUPPORTED),
+    (dict(dstate=24), ssd.SSD_ERR_UNSUPPORTED),
+    (dict(dstate=272), ssd.SSD_ERR_UNSUPPORTED),
+    (dict(chunk_len=16, headdim=16, dstate=16, dtype=ssd.SSD_DTYPE_F32), ssd.SSD_OK),
+    (dict(headdim=256, dstate=256, dtype=ssd.SSD_DTYPE_F32), ssd.SSD_OK),
+])
+def test_check_problem(kw, code):
+    p = prob(**kw)
+    assert ssd.ssd_check_problem(p) == code
+    assert (ssd.ssd_workspace_bytes(p) > 0) == (code == ssd.SSD_OK)
+
+
+def test_workspace_grows_with_problem():
+    small = ssd.ssd_workspace_bytes(prob(seqlen=128))
+    large = ssd.ssd_workspace_bytes(prob(seqlen=4096))
+    assert 0 < small < large
+    assert ssd.ssd_workspace_bytes(prob()) % 256 == 0
+
+
+# Fake, aligned, non-overlapping addresses: every call below must fail validation on
+# the host, so nothing is dereferenced and no kernel is launched.
+GB = 1 << 30
+ADDR = dict(X=1 * GB, logA=2 * GB, B=3 * GB, C=4 * GB, init=5 * GB, off=6 * GB, Y=7 * GB,
+            final=8 * GB, ws=9 * GB)
+
+
+def call(p, ws_bytes=None, **over):
+    a = dict(ADDR)
+    a.update(over)
+    wsb = ssd.ssd_workspace_bytes(p) if ws_bytes is None else ws_bytes
+    return ssd.ssd_forward(p, a["X"], a["logA"], a["B"], a["C"], a["init"], a["off"], a["Y"],
+                           a["final"], a["ws"], wsb, None)
+
+
+def test_forward_rejects_invalid_problem():
+    assert call(prob(nheads=3), ws_bytes=1 << 20, off=None) == ssd.SSD_ERR_INVALID_ARG
+    assert call(prob(chunk_len=100), ws_bytes=1 << 20, off=None) == ssd.SSD_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ["X", "logA", "B", "C", "Y", "ws"])
+def test_forward_rejects_null_required_pointer(name):
+    assert call(prob(), off=None, **{name: None}) == ssd.SSD_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name", ["X", "logA", "B", "C", "init", "Y", "final"])
+def test_forward_rejects_misaligned_pointer(name):
+    assert call(prob(), off=None, **{name: ADDR[name] + 4}) == ssd.SSD_ERR_INVALID_ARG
+
+
+def test_forward_rejects_misaligned_workspace():
+    assert call(prob(), off=None, ws=ADDR["ws"] + 16) == ssd.SSD_ERR_INVALID_ARG
+
+
+def test_forward_rejects_seq_offsets_with_batch():
+    assert call(prob(batch=2, nseq=3)) == ssd.SSD_ERR_INVALID_ARG
+
+
+def test_forward_rejects_nseq_mismatch_without_offsets():
+    assert call(prob(batch=2, nseq=3), off=None) == ssd.SSD_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("out,inp", [("Y", "X"), ("final", "init"), ("Y", "B"), ("final", "ws"),
+                                     ("final", "Y")])
+def test_forward_rejects_aliased_outputs(out, inp):
+    assert call(prob(), off=None, **{out: ADDR[inp]}) == ssd.SSD_ERR_INVALID_ARG
+
+
+def test_forward_rejects_small_workspace():
+    p = prob()
+    assert call(p, ws_bytes=ssd.ssd_workspace_bytes(p) - 256, off=None) == ssd.SSD_ERR_WORKSPACE
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    X = torch.zeros(1, 4, 1, 16)
+    with pytest.raises(ValueError):
+        ssd.forward(X, torch.zeros(1, 4, 1), torch.zeros(1, 4, 1, 16), torch.zeros(1, 4, 1, 16), 16)

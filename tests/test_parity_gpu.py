@@ -1,0 +1,177 @@
+"""GPU parity of the HIP path against the float64 oracle (needs an MI355X).
+
+Metric, for Y and for the final state: max|out - ref| / max|ref| with ref the oracle's
+unrounded float64 result on the same (already quantized) inputs.  Bars:
+  float32 inputs  <= 1e-4
+  bfloat16 inputs <= 2e-2 (fp32 accumulation)
+Small cases compare every element; the five workload configurations run at full size in
+the launch configuration the benchmark times and are compared on every token of a
+sample of heads (the oracle computes heads independently).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import CONFIGS, make_inputs, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def dev(inp):
+    torch = _torch()
+    dt = torch.bfloat16 if inp.dtype == "bf16" else torch.float32
+    d = {
+        "X": torch.from_numpy(inp.X).to(dt).cuda(),
+        "logA": torch.from_numpy(inp.logA).cuda(),
+        "B": torch.from_numpy(inp.B).to(dt).cuda(),
+        "C": torch.from_numpy(inp.C).to(dt).cuda(),
+        "init": None if inp.init is None else torch.from_numpy(inp.init).cuda(),
+        "off": None if inp.seq_offsets is None else torch.from_numpy(inp.seq_offsets).cuda(),
+    }
+    return d
+
+
+def run_gpu(inp, Q, d=None):
+    import mamba_ssd_scan_forward_amd as ssd
+    torch = _torch()
+    d = d or dev(inp)
+    Y, F = ssd.forward(d["X"], d["logA"], d["B"], d["C"], Q, d["init"], d["off"])
+    torch.cuda.synchronize()
+    return Y.float().cpu().numpy().astype(np.float64), F.cpu().numpy().astype(np.float64)
+
+
+def rel_err(out, ref):
+    den = float(np.max(np.abs(ref)))
+    return float(np.max(np.abs(out - ref))) / max(den, 1e-30)
+
+
+def check(inp, Q, label=""):
+    print(f"[parity] {label} X{tuple(inp.X.shape)} G={inp.B.shape[2]} N={inp.B.shape[3]} "
+          f"Q={Q} {inp.dtype} init={inp.init is not None} varlen={inp.seq_offsets is not None}",
+          flush=True)
+    Y, F = run_gpu(inp, Q)
+    Yr, Fr = oracle.recurrence(inp.X, inp.logA, inp.B, inp.C, inp.init, inp.seq_offsets)
+    ey, ef = rel_err(Y, Yr), rel_err(F, Fr)
+    print(f"[parity]   err Y {ey:.3e}  final {ef:.3e}", flush=True)
+    assert np.all(np.isfinite(Y)) and np.all(np.isfinite(F))
+    assert ey <= TOL[inp.dtype], ey
+    assert ef <= TOL[inp.dtype], ef
+    return Y, F
+
+
+def test_cfg0_tiny_fp32_full():
+    w = CONFIGS["cfg0_tiny_f32"]
+    check(workload_inputs(w), w.chunk_len, w.name)
+
+
+@pytest.mark.parametrize("Q", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("init", [False, True])
+def test_bf16_chunk_sweep_ragged(Q, init):
+    inp = make_inputs(2, 300, 4, 64, 128, 2, "bf16", seed=100 + Q, init_state=init)
+    check(inp, Q, "bf16 ragged")
+
+
+@pytest.mark.parametrize("Q", [32, 64, 256])
+def test_fp32_ragged(Q):
+    inp = make_inputs(2, 200, 3, 32, 64, 1, "f32", seed=200 + Q, init_state=True)
+    check(inp, Q, "fp32 ragged")
+
+
+@pytest.mark.parametrize("P,N", [(16, 16), (32, 32), (48, 80), (64, 64), (128, 128), (64, 256),
+                                 (256, 32)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_head_and_state_sizes(P, N, dtype):
+    inp = make_inputs(1, 130, 2, P, N, 1, dtype, seed=300 + P + N, init_state=True)
+    check(inp, 64, "sizes")
+
+
+def test_varlen_ragged_with_empty_and_short_sequences():
+    lens = [5, 0, 300, 1, 64, 129, 33]
+    inp = make_inputs(1, sum(lens), 4, 64, 128, 2, "bf16", seed=400, init_state=True,
+                      seq_lengths=lens)
+    Y, F = check(inp, 64, "varlen")
+    # the empty sequence returns its initial state unchanged
+    np.testing.assert_array_equal(F[1], inp.init[1].astype(np.float64))
+
+
+def test_a_one_linear_attention():
+    inp = make_inputs(1, 200, 2, 64, 64, 1, "f32", seed=500, init_state=True)
+    inp.logA[:] = 0.0
+    check(inp, 64, "a=1")
+
+
+def test_a_zero_via_length_one_sequences():
+    """Every token its own sequence, zero initial state: y_t = (C_t . B_t) x_t, the a = 0
+    closed form, reached exactly through sequence boundaries."""
+    T = 70
+    inp = make_inputs(1, T, 2, 32, 32, 1, "f32", seed=600, seq_lengths=[1] * T)
+    Y, F = check(inp, 32, "a=0")
+    cb = np.einsum("tn,tn->t", inp.C[0, :, 0].astype(np.float64), inp.B[0, :, 0].astype(np.float64))
+    np.testing.assert_allclose(Y[0], cb[:, None, None] * inp.X[0].astype(np.float64), rtol=1e-4, atol=1e-5)
+
+
+def test_strong_decay_is_finite():
+    """logA down to -1e4: every off-diagonal term underflows to zero, nothing overflows."""
+    inp = make_inputs(1, 256, 2, 64, 128, 1, "bf16", seed=700)
+    inp.logA[:] = -1e4
+    check(inp, 128, "strong decay")
+
+
+def test_split_resume_matches_full_run():
+    inp = make_inputs(2, 512, 4, 64, 128, 1, "bf16", seed=800, init_state=True)
+    Y, F = run_gpu(inp, 256)
+    split = 200
+    import copy
+    a = copy.deepcopy(inp)
+    a.X, a.logA, a.B, a.C = inp.X[:, :split], inp.logA[:, :split], inp.B[:, :split], inp.C[:, :split]
+    Y1, F1 = run_gpu(a, 256)
+    b = copy.deepcopy(inp)
+    b.X, b.logA, b.B, b.C = inp.X[:, split:], inp.logA[:, split:], inp.B[:, split:], inp.C[:, split:]
+    b.init = F1.astype(np.float32)
+    Y2, F2 = run_gpu(b, 256)
+    assert rel_err(np.concatenate([Y1, Y2], axis=1), Y) <= 2e-2
+    assert rel_err(F2, F) <= 2e-2
+
+
+def test_bitwise_repeatable():
+    inp = make_inputs(2, 700, 4, 64, 128, 2, "bf16", seed=900, init_state=True)
+    d = dev(inp)
+    Y1, F1 = run_gpu(inp, 256, d)
+    Y2, F2 = run_gpu(inp, 256, d)
+    np.testing.assert_array_equal(Y1, Y2)
+    np.testing.assert_array_equal(F1, F2)
+
+
+SAMPLE_HEADS = {"cfg1_mamba2_2.7b_bf16": [0, 41, 79], "cfg2a_state64_bf16": [0, 31],
+                "cfg2b_state256_bf16": [5, 30], "cfg3_long16k_bf16": [0, 47, 79],
+                "cfg4_varlen32k_bf16": [0, 13, 79]}
+
+
+@pytest.mark.parametrize("name", list(SAMPLE_HEADS))
+def test_full_size_config_sampled_heads(name):
+    w = CONFIGS[name]
+    inp = workload_inputs(w)
+    print(f"[parity] {name} full size, sampled heads {SAMPLE_HEADS[name]}", flush=True)
+    Y, F = run_gpu(inp, w.chunk_len)
+    assert np.all(np.isfinite(Y)) and np.all(np.isfinite(F))
+    hpg = w.nheads // w.ngroups
+    for h in SAMPLE_HEADS[name]:
+        g = h // hpg
+        Yr, Fr = oracle.recurrence(inp.X[:, :, [h]], inp.logA[:, :, [h]], inp.B[:, :, [g]],
+                                   inp.C[:, :, [g]],
+                                   None if inp.init is None else inp.init[:, [h]], inp.seq_offsets)
+        ey, ef = rel_err(Y[:, :, [h]], Yr), rel_err(F[:, [h]], Fr)
+        print(f"[parity]   head {h}: err Y {ey:.3e} final {ef:.3e}", flush=True)
+        assert ey <= TOL[w.dtype] and ef <= TOL[w.dtype], (h, ey, ef)

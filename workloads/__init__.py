@@ -27,9 +27,9 @@ DTYPES = ("f32", "bf16")
 def bf16_round(a) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even); returned as float32."""
     f = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
-    u = f.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32).reshape(f.shape)
+    u = f.view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return r.view(np.float32).reshape(f.shape)
 
 
 def bf16_bits(a) -> np.ndarray:
