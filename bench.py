@@ -1,0 +1,247 @@
+"""Benchmark of the SSD layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one whole SSD forward (both launches: chunk cumsum + C B^T tiles, then the
+chunk walk) over one synthetic batch already resident in HBM.  Prints ONE JSON line
+on stdout; progress goes to stderr.
+
+Roofline: the dominant launch is the chunk walk.  Its algorithmic bytes are the
+minimum traffic of the layer: read X, B, C and logA once, write Y and the final state
+once (the per-token figure times the tokens of one launch, plus the states).  Its
+duration is measured here with HIP events around launches of that stage alone on the
+stream it runs on.  HBM traffic measured by counters is read from the committed
+counter summary when it was taken on the current kernel source, else null.
+
+``--mode copy`` runs only a plain device copy of known size; it is the calibration
+program for the FETCH_SIZE / WRITE_SIZE counters.
+"""
+import argparse
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SSD fwd tokens/s + MFMA util, bf16 H=80 P=64 N=128 T=2K batch 8"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 matrix/vector, published
+COUNTERS_JSON = os.path.join(ROOT, "profiles", "walk_cfg1_hbm_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "mamba_ssd_scan_forward_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w, es):
+    """Minimum HBM traffic of one forward: read X, B, C, logA (+ init), write Y, final."""
+    tokens = w.batch * w.seqlen
+    per_token = (2 * w.nheads * w.headdim * es          # X in, Y out
+                 + 2 * w.ngroups * w.dstate * es         # B, C in
+                 + w.nheads * 4)                         # logA in
+    nseq = w.nseq if w.varlen else w.batch
+    state = nseq * w.nheads * w.headdim * w.dstate * 4
+    return tokens * per_token + state * (2 if w.init_state else 1)
+
+
+def flops_pages(w, chunk_lens):
+    """Block-decomposition FLOPs counted as the pages count them (section 6.3 BMMs):
+    per chunk 2*[G*Q^2*N + H*(Q^2*P + 2*Q*N*P)], C B^T once per group."""
+    f = 0
+    for q in chunk_lens:
+        f += 2 * (w.ngroups * q * q * w.dstate + w.nheads * (q * q * w.headdim + 2 * q * w.dstate * w.headdim))
+    return f
+
+
+def chunk_lengths(w, lens):
+    out = []
+    for L in lens:
+        full, rem = divmod(L, w.chunk_len)
+        out += [w.chunk_len] * full + ([rem] if rem else [])
+    return out
+
+
+def run_copy_mode(steps):
+    import torch
+    n = 512 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "launches": steps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy"])
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the single-GPU hot path only; run it with --gpus 1 "
+              "(multi-GPU sharding of the SSD layer is designed, not built).", file=sys.stderr)
+        sys.exit(2)
+    if args.mode == "copy":
+        run_copy_mode(args.steps)
+        return
+
+    import numpy as np
+    import torch
+
+    import mamba_ssd_scan_forward_amd as ssd
+    from workloads import CONFIGS, HEADLINE, workload_inputs
+
+    name = args.workload or HEADLINE
+    w = CONFIGS[name]
+    t0 = time.time()
+    inp = workload_inputs(w)
+    log(f"[bench] {name}: inputs drawn in {time.time() - t0:.1f}s")
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    es = 2 if w.dtype == "bf16" else 4
+    dev = torch.device("cuda", 0)
+    X = torch.from_numpy(inp.X).to(dt).to(dev)
+    logA = torch.from_numpy(inp.logA).to(dev)
+    B = torch.from_numpy(inp.B).to(dt).to(dev)
+    C = torch.from_numpy(inp.C).to(dt).to(dev)
+    init = None if inp.init is None else torch.from_numpy(inp.init).to(dev)
+    off = None if inp.seq_offsets is None else torch.from_numpy(inp.seq_offsets).to(dev)
+    nseq = w.nseq if w.varlen else w.batch
+    prob = ssd.problem_for(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_len,
+                           nseq, ssd.SSD_DTYPE_BF16 if w.dtype == "bf16" else ssd.SSD_DTYPE_F32)
+    wsb = ssd.ssd_workspace_bytes(prob)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    Y = torch.empty_like(X)
+    final = torch.empty((nseq, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    ptrs = [X.data_ptr(), logA.data_ptr(), B.data_ptr(), C.data_ptr(),
+            None if init is None else init.data_ptr(), None if off is None else off.data_ptr(),
+            Y.data_ptr(), final.data_ptr(), ws.data_ptr(), wsb, sp]
+
+    def step():
+        rc = ssd.ssd_forward(prob, *ptrs)
+        if rc != 0:
+            raise ssd.SsdError(rc)
+
+    def stage(k):
+        rc = ssd.ssd_forward_stage(k, prob, *ptrs)
+        if rc != 0:
+            raise ssd.SsdError(rc, f"ssd_forward_stage({k})")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # each launch alone, on the same stream, same events
+    stage_ms = {}
+    for k in (1, 2):
+        for _ in range(max(2, args.warmup // 2)):
+            stage(k)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            stage(k)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        stage_ms[k] = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] step {ms_step * 1e3:.1f} us; prep {stage_ms[1] * 1e3:.1f} us; "
+        f"walk {stage_ms[2] * 1e3:.1f} us")
+
+    lens = [w.seqlen] * w.batch if not w.varlen else list(np.diff(inp.seq_offsets))
+    tokens = w.batch * w.seqlen
+    fl = flops_pages(w, chunk_lengths(w, [int(v) for v in lens]))
+    abytes = algorithmic_bytes(w, es)
+    tok_s = tokens / (ms_step * 1e-3)
+    peak_mm = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+    achieved_gbs = abytes / (stage_ms[2] * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(COUNTERS_JSON):
+        try:
+            c = json.load(open(COUNTERS_JSON))
+            if c.get("kernel_source_hash") == kernel_source_hash() and c.get("workload") == name:
+                traffic = c.get("hbm_bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+
+    result = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded: X~N(0,1), B,C~N(0,1/N), logA=-U[.001,.1]*U[1,16])",
+        "config": dict(workload=name, **w.shape_dict()),
+        "tflops_pages": round(fl / (ms_step * 1e-3) / 1e12, 2),
+        "mfma_util_pages": round(fl / (ms_step * 1e-3) / 1e12 / peak_mm, 4),
+        "stage_us": {"prep": round(stage_ms[1] * 1e3, 2), "walk": round(stage_ms[2] * 1e3, 2)},
+        "roofline": {
+            "kernel": "ssd_walk_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": abytes,
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        x64 = [np.asarray(a, dtype=np.float64) for a in (inp.X, inp.logA, inp.B, inp.C)]
+        i64 = None if inp.init is None else inp.init.astype(np.float64)
+        oracle.recurrence(*[a[:, :64] for a in x64], None if i64 is None else i64, None)  # warm
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.recurrence(*x64, i64, inp.seq_offsets)
+            times.append(time.perf_counter() - t0)
+        t = statistics.median(times)
+        result["cpu_baseline"] = {
+            "value": round(tokens / t, 1),
+            "unit": "tokens/s",
+            "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"whole workload ({tokens} tokens, all {w.nheads} heads), float64 "
+                      f"recurrence, median of 3 runs ({t:.2f}s each)",
+        }
+        log(f"[bench] oracle {t:.2f}s on {oracle.threads()} threads")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -111,6 +111,20 @@ int ssd_forward(const ssd_problem* p, const void* X, const float* logA, const vo
                 const void* C, const float* init_state, const int32_t* seq_offsets, void* Y,
                 float* final_state, void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* One of the two launches that make up ssd_forward, with the same arguments and checks.
+ *   stage 1: chunk cumsum of logA and the C B^T tiles of every chunk, written to the
+ *            workspace (page section 6.1 and Listing 1 step 1 inputs);
+ *   stage 2: the chunk walk: outputs, chunk states and state passing (section 6.1 and
+ *            6.2), reading the workspace that a stage-1 call with the same problem and
+ *            inputs left there.
+ * ssd_forward is stage 1 followed by stage 2 on the same stream.  This entry point is for
+ * timing each launch on its own and for callers that place the two launches themselves.
+ * Returns SSD_ERR_INVALID_ARG for a stage other than 1 or 2. */
+int ssd_forward_stage(int stage, const ssd_problem* p, const void* X, const float* logA,
+                      const void* B, const void* C, const float* init_state,
+                      const int32_t* seq_offsets, void* Y, float* final_state, void* workspace,
+                      size_t workspace_bytes, void* hip_stream);
+
 /* Static English text for a status code (never NULL). */
 const char* ssd_status_string(int status);
 

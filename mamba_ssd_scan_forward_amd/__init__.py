@@ -22,7 +22,8 @@ import os
 __all__ = [
     "SSD_OK", "SSD_ERR_INVALID_ARG", "SSD_ERR_UNSUPPORTED", "SSD_ERR_WORKSPACE", "SSD_ERR_HIP",
     "SSD_DTYPE_F32", "SSD_DTYPE_BF16", "SsdProblem", "SsdError", "lib_path", "load_library",
-    "ssd_check_problem", "ssd_workspace_bytes", "ssd_forward", "ssd_status_string",
+    "ssd_check_problem", "ssd_workspace_bytes", "ssd_forward", "ssd_forward_stage",
+    "ssd_status_string",
     "ssd_abi_version", "forward", "problem_for",
 ]
 
@@ -76,6 +77,8 @@ def load_library():
     lib.ssd_workspace_bytes.restype = sz
     lib.ssd_forward.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ssd_forward.restype = ctypes.c_int
+    lib.ssd_forward_stage.argtypes = [ctypes.c_int, pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_forward_stage.restype = ctypes.c_int
     lib.ssd_status_string.argtypes = [ctypes.c_int]
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_abi_version.argtypes = []
@@ -109,6 +112,14 @@ def ssd_forward(problem: SsdProblem, X, logA, B, C, init_state, seq_offsets, Y, 
     return int(load_library().ssd_forward(ctypes.byref(problem), X, logA, B, C, init_state,
                                           seq_offsets, Y, final_state, workspace,
                                           int(workspace_bytes), hip_stream))
+
+
+def ssd_forward_stage(stage: int, problem: SsdProblem, X, logA, B, C, init_state, seq_offsets, Y,
+                      final_state, workspace, workspace_bytes: int, hip_stream) -> int:
+    """Direct call of ssd_forward_stage (stage 1: prep launch, stage 2: chunk walk)."""
+    return int(load_library().ssd_forward_stage(int(stage), ctypes.byref(problem), X, logA, B, C,
+                                                init_state, seq_offsets, Y, final_state,
+                                                workspace, int(workspace_bytes), hip_stream))
 
 
 def problem_for(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len, nseq, dtype) -> SsdProblem:

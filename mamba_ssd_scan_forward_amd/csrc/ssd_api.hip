@@ -15,13 +15,16 @@ constexpr int kLdsMax = 160 * 1024;   // LDS per workgroup on gfx950
 constexpr int kWalkThreads = 512;
 constexpr int kPrepThreads = 256;
 
+typedef void (*walk_fn_t)(ssd::WalkArgs);
+
 struct Plan {
     int dtype;
     int Q, Qp, nlb, ntile;
-    int PT, NP, ptiles, qb;
+    int PT, NP, ptiles, qb, cb_lds;
     int64_t nslots, nitems;
     size_t cs_off, cb_off, ws_bytes;
     int lds_bytes, xs_off, xts_off, bs_off, hs_off, cs_lds_off;
+    walk_fn_t walk;   // the walk kernel instance for this plan
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -44,16 +47,57 @@ int check_problem(const ssd_problem* p) {
     return SSD_OK;
 }
 
+// LDS of the walk kernel: X, X~ [Qp][PT+pad]; a region holding B rows [qb][NP+pad]
+// during the state phase and, when cb_lds, the off-diagonal C B^T tiles of the chunk
+// during the output phase; h [PT][NP+pad]; the chunk cumsum [Qp] floats.
 int lds_layout(Plan* pl, int es) {
     const int pad = 16 / es;
     const int XS = pl->PT + pad, BS = pl->NP + pad, HS = pl->NP + pad;
+    const int nlb = pl->Qp / 32;
+    int region = pl->qb * BS * es;
+    const int cb_bytes = nlb * (nlb - 1) / 2 * 1024 * es;
+    if (pl->cb_lds && cb_bytes > region) region = cb_bytes;
     pl->xs_off = 0;
     pl->xts_off = pl->xs_off + pl->Qp * XS * es;
     pl->bs_off = pl->xts_off + pl->Qp * XS * es;
-    pl->hs_off = pl->bs_off + pl->qb * BS * es;
+    pl->hs_off = pl->bs_off + region;
     pl->cs_lds_off = pl->hs_off + pl->PT * HS * es;
     pl->lds_bytes = pl->cs_lds_off + pl->Qp * 4;
     return pl->lds_bytes;
+}
+
+typedef void (*walk_fn)(ssd::WalkArgs);
+typedef void (*prep_fn)(ssd::PrepArgs);
+
+template <typename T, int PT, int NP, bool CBL>
+walk_fn walk_instance() { return ssd::ssd_walk_kernel<T, PT, NP, CBL>; }
+
+// float32: 32-wide P tiles, C B^T tiles read from global memory
+walk_fn pick_walk_f32(int NP) {
+    switch (NP) {
+        case 32: return walk_instance<float, 32, 32, false>();
+        case 64: return walk_instance<float, 32, 64, false>();
+        case 128: return walk_instance<float, 32, 128, false>();
+        case 256: return walk_instance<float, 32, 256, false>();
+    }
+    return nullptr;
+}
+
+template <int PT, bool CBL>
+walk_fn pick_walk_bf16_np(int NP) {
+    switch (NP) {
+        case 32: return walk_instance<__bf16, PT, 32, CBL>();
+        case 64: return walk_instance<__bf16, PT, 64, CBL>();
+        case 128: return walk_instance<__bf16, PT, 128, CBL>();
+        case 256: return walk_instance<__bf16, PT, 256, CBL>();
+    }
+    return nullptr;
+}
+
+walk_fn pick_walk_bf16(int PT, int NP, bool cbl) {
+    if (PT == 32) return cbl ? pick_walk_bf16_np<32, true>(NP) : pick_walk_bf16_np<32, false>(NP);
+    if (PT == 64) return cbl ? pick_walk_bf16_np<64, true>(NP) : pick_walk_bf16_np<64, false>(NP);
+    return nullptr;
 }
 
 // Workspace and launch plan.  `nseq_total` slots: batch mode has batch * ceil(T/Q)
@@ -69,7 +113,8 @@ int make_plan(const ssd_problem* p, Plan* pl) {
     pl->ntile = pl->nlb * (pl->nlb + 1) / 2;
     const int N = (int)p->dstate, P = (int)p->headdim;
     pl->NP = N <= 32 ? 32 : N <= 64 ? 64 : N <= 128 ? 128 : 256;
-    pl->PT = (p->dtype == SSD_DTYPE_BF16 && P > 32) ? 64 : 32;
+    // 64-wide P tiles when there are enough (sequence, head) items to fill the chip
+    pl->PT = (p->dtype == SSD_DTYPE_BF16 && P > 32 && p->nseq * p->nheads * ((P + 63) / 64) >= 512) ? 64 : 32;
     pl->ptiles = (P + pl->PT - 1) / pl->PT;
     const int64_t nc = (p->seqlen + pl->Q - 1) / pl->Q;
     // slots are sized for the larger of the two numberings, so one plan serves
@@ -84,9 +129,20 @@ int make_plan(const ssd_problem* p, Plan* pl) {
     pl->cb_off = align_up(pl->cs_off + cs_bytes, 256);
     const size_t cb_bytes = (size_t)pl->nslots * p->ngroups * pl->ntile * 1024 * es;
     pl->ws_bytes = align_up(pl->cb_off + cb_bytes, 256);
+    // stage the off-diagonal C B^T tiles in LDS when they fit next to a whole chunk of B
+    // (or the largest B stage that fits), else read them from global memory
+    pl->cb_lds = p->dtype == SSD_DTYPE_BF16 ? 1 : 0;
     pl->qb = pl->Qp;
     while (lds_layout(pl, es) > kLdsMax && pl->qb > 32) pl->qb -= 32;
+    if (pl->lds_bytes > kLdsMax) {
+        pl->cb_lds = 0;
+        pl->qb = pl->Qp;
+        while (lds_layout(pl, es) > kLdsMax && pl->qb > 32) pl->qb -= 32;
+    }
     if (pl->lds_bytes > kLdsMax) return SSD_ERR_UNSUPPORTED;
+    pl->walk = p->dtype == SSD_DTYPE_BF16 ? pick_walk_bf16(pl->PT, pl->NP, pl->cb_lds != 0)
+                                          : (pl->cb_lds ? nullptr : pick_walk_f32(pl->NP));
+    if (!pl->walk) return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
 }
 
@@ -96,32 +152,6 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
     if (!a || !b || na == 0 || nb == 0) return false;
     const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
     return a0 < b0 + nb && b0 < a0 + na;
-}
-
-typedef void (*walk_fn)(ssd::WalkArgs);
-typedef void (*prep_fn)(ssd::PrepArgs);
-
-template <typename T, int PT, int NP>
-walk_fn walk_instance() { return ssd::ssd_walk_kernel<T, PT, NP>; }
-
-template <typename T>
-walk_fn pick_walk(int PT, int NP) {
-    if (PT == 32) {
-        switch (NP) {
-            case 32: return walk_instance<T, 32, 32>();
-            case 64: return walk_instance<T, 32, 64>();
-            case 128: return walk_instance<T, 32, 128>();
-            case 256: return walk_instance<T, 32, 256>();
-        }
-    } else if (PT == 64) {
-        switch (NP) {
-            case 32: return walk_instance<T, 64, 32>();
-            case 64: return walk_instance<T, 64, 64>();
-            case 128: return walk_instance<T, 64, 128>();
-            case 256: return walk_instance<T, 64, 256>();
-        }
-    }
-    return nullptr;
 }
 
 // Raise the dynamic-LDS limit of a walk kernel to the full 160 KiB, once per kernel
@@ -169,7 +199,12 @@ size_t ssd_workspace_bytes(const ssd_problem* p) {
     return pl.ws_bytes;
 }
 
-int ssd_forward(const ssd_problem* p, const void* X, const float* logA, const void* B,
+}  // extern "C"
+
+namespace {
+
+// stages: bit 0 = prep launch, bit 1 = walk launch
+int run_forward(int stages, const ssd_problem* p, const void* X, const float* logA, const void* B,
                 const void* C, const float* init_state, const int32_t* seq_offsets, void* Y,
                 float* final_state, void* workspace, size_t workspace_bytes, void* hip_stream) {
     Plan pl;
@@ -203,11 +238,9 @@ int ssd_forward(const ssd_problem* p, const void* X, const float* logA, const vo
     if (final_state && overlap(Y, nx, final_state, ns)) return SSD_ERR_INVALID_ARG;
     if (workspace_bytes < pl.ws_bytes) return SSD_ERR_WORKSPACE;
 
-    walk_fn walk = p->dtype == SSD_DTYPE_BF16 ? pick_walk<__bf16>(pl.PT, pl.NP)
-                                              : pick_walk<float>(pl.PT, pl.NP);
+    walk_fn walk = pl.walk;
     prep_fn prep = p->dtype == SSD_DTYPE_BF16 ? ssd::ssd_prep_kernel<__bf16>
                                               : ssd::ssd_prep_kernel<float>;
-    if (!walk) return SSD_ERR_UNSUPPORTED;
     rc = ensure_lds_limit(reinterpret_cast<const void*>(walk));
     if (rc != SSD_OK) return rc;
 
@@ -234,11 +267,13 @@ int ssd_forward(const ssd_problem* p, const void* X, const float* logA, const vo
     pa.Qp = pl.Qp;
     pa.ntile = pl.ntile;
     pa.nseq = (int)p->nseq;
-    pa.hblocks = (int)((H + 3) / 4);
+    pa.hblocks = (int)((H + ssd::kPrepHeads - 1) / ssd::kPrepHeads);
     pa.cs_blocks = (int)(nslots * pa.hblocks);
-    const int64_t prep_blocks = nslots * pa.hblocks + nslots * G;
+    pa.cb_groups = (pl.ntile + 3) / 4;
+    const int64_t prep_blocks = nslots * pa.hblocks + nslots * G * pa.cb_groups;
     if (prep_blocks > INT32_MAX) return SSD_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(prep, dim3((unsigned)prep_blocks), dim3(kPrepThreads), 0, stream, pa);
+    if (stages & 1)
+        hipLaunchKernelGGL(prep, dim3((unsigned)prep_blocks), dim3(kPrepThreads), 0, stream, pa);
 
     ssd::WalkArgs wa;
     wa.X = X;
@@ -262,14 +297,36 @@ int ssd_forward(const ssd_problem* p, const void* X, const float* logA, const vo
     wa.ptiles = pl.ptiles;
     wa.nitems = (int)pl.nitems;
     wa.qb = pl.qb;
+    wa.cb_lds = pl.cb_lds;
     wa.xs_off = pl.xs_off;
     wa.xts_off = pl.xts_off;
     wa.bs_off = pl.bs_off;
     wa.hs_off = pl.hs_off;
     wa.cs_off = pl.cs_lds_off;
-    hipLaunchKernelGGL(walk, dim3((unsigned)pl.nitems), dim3(kWalkThreads), pl.lds_bytes, stream, wa);
+    if (stages & 2)
+        hipLaunchKernelGGL(walk, dim3((unsigned)pl.nitems), dim3(kWalkThreads), pl.lds_bytes, stream, wa);
     if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
     return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_forward(const ssd_problem* p, const void* X, const float* logA, const void* B,
+                const void* C, const float* init_state, const int32_t* seq_offsets, void* Y,
+                float* final_state, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    return run_forward(3, p, X, logA, B, C, init_state, seq_offsets, Y, final_state, workspace,
+                       workspace_bytes, hip_stream);
+}
+
+int ssd_forward_stage(int stage, const ssd_problem* p, const void* X, const float* logA,
+                      const void* B, const void* C, const float* init_state,
+                      const int32_t* seq_offsets, void* Y, float* final_state, void* workspace,
+                      size_t workspace_bytes, void* hip_stream) {
+    if (stage != 1 && stage != 2) return SSD_ERR_INVALID_ARG;
+    return run_forward(stage, p, X, logA, B, C, init_state, seq_offsets, Y, final_state, workspace,
+                       workspace_bytes, hip_stream);
 }
 
 }  // extern "C"

@@ -34,6 +34,19 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Buffer resources: 32-bit byte offsets against a base and a size; a load whose bytes
+// fall outside [0, size) returns zeros.  Predicated loads pass kOutOfRange.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kRsrcWord3 = 0x00020000;   // gfx9 raw buffer, no swizzle
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ float ldb_f32(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
 template <typename T> struct Elem;
 
 template <> struct Elem<__bf16> {
@@ -49,6 +62,12 @@ template <> struct Elem<__bf16> {
     // 8 contiguous elements from global memory (16-byte aligned).
     __device__ static __forceinline__ frag ldg8(const __bf16* p) {
         return __builtin_bit_cast(frag, *reinterpret_cast<const u32x4*>(p));
+    }
+    // 8 contiguous elements through a buffer resource (zeros out of range).  The whole
+    // vector is cast at once: casting single elements of the loaded vector has been
+    // seen to shrink the load.
+    __device__ static __forceinline__ frag ldb8(rsrc_t r, uint32_t off) {
+        return __builtin_bit_cast(frag, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
     }
     // 8 contiguous elements from LDS.
     __device__ static __forceinline__ frag lds8(const __bf16* p) {
@@ -80,6 +99,12 @@ template <> struct Elem<float> {
         f32x4 lo = v[0], hi = v[1];
         frag r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         return r;
+    }
+    __device__ static __forceinline__ frag ldb8(rsrc_t r, uint32_t off) {
+        const f32x4 lo = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+        const f32x4 hi = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 16), 0, 0));
+        frag v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return v;
     }
     __device__ static __forceinline__ frag lds8(const float* p) { return ldg8(p); }
     __device__ static __forceinline__ float to_f(float v) { return v; }

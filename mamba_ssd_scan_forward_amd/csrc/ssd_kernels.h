@@ -41,7 +41,10 @@ struct PrepArgs {
     float* cs;        // [nslots, H, Qp] float, log2 units
     void* cb;         // [nslots, G, ntile, 32, 32] elements of the input dtype
     int64_t T;
-    int H, N, G, Q, Qp, ntile, nseq, cs_blocks, hblocks;
+    int H, N, G, Q, Qp, ntile, nseq;
+    int cs_blocks;    // workgroups of the cumsum role: nslots * hblocks
+    int hblocks;      // 64-head blocks per chunk
+    int cb_groups;    // 4-tile groups per (chunk, group) in the C B^T role
 };
 
 struct WalkArgs {
@@ -56,6 +59,7 @@ struct WalkArgs {
     const void* cb;
     int64_t T;
     int H, P, N, G, Q, Qp, ntile, nseq, ptiles, nitems, qb;
+    int cb_lds;                                    // stage off-diagonal C B^T tiles in LDS
     int xs_off, xts_off, bs_off, hs_off, cs_off;   // LDS byte offsets
 };
 
@@ -106,10 +110,14 @@ __device__ __forceinline__ float wave_inclusive_sum(float x, int lane) {
     return x;
 }
 
+constexpr int kPrepHeads = 16;   // heads per cumsum workgroup (small LDS tile: the C B^T role
+                                 // shares the launch and its occupancy)
+
 template <typename T>
 __global__ void __launch_bounds__(256) ssd_prep_kernel(PrepArgs a) {
     using E = Elem<T>;
     typedef typename E::frag frag;
+    __shared__ float lt[256][kPrepHeads + 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lg = lane >> 5;
     int bid = blockIdx.x;
     const bool cs_role = bid < a.cs_blocks;
@@ -119,63 +127,92 @@ __global__ void __launch_bounds__(256) ssd_prep_kernel(PrepArgs a) {
         rest = bid % a.hblocks;
     } else {
         bid -= a.cs_blocks;
-        k = bid / a.G;
-        rest = bid % a.G;
+        k = bid / (a.G * a.cb_groups);
+        rest = bid % (a.G * a.cb_groups);
     }
     int64_t rowc;
     int len;
     if (!locate_chunk(k, a.seq_offsets, a.T, a.Q, a.nseq, &rowc, &len)) return;
 
     if (cs_role) {
-        // (a) one wavefront per head: 4 consecutive tokens per lane, then a lane scan.
-        const int h = rest * 4 + wave;
-        if (h >= a.H) return;
-        float v[4];
+        // (a) a Qp x 16 block of logA (tokens x heads) through LDS with coalesced loads,
+        //     then one wavefront per head: 4 consecutive tokens per lane and a lane scan.
+        const int h0 = rest * kPrepHeads;
+        const int nh = min(kPrepHeads, a.H - h0);
+        for (int base = 0; base < a.Qp * kPrepHeads; base += 16 * 256) {
+            float v[16];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 4 * lane + j;
-            v[j] = (r < len) ? a.logA[(rowc + r) * a.H + h] : 0.f;
+            for (int q = 0; q < 16; ++q) {
+                const int idx = base + tid + 256 * q;
+                const int r = idx / kPrepHeads, hh = idx % kPrepHeads;
+                v[q] = (r < len && hh < nh) ? a.logA[(rowc + r) * a.H + h0 + hh] : 0.f;
+            }
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int idx = base + tid + 256 * q;
+                if (idx < a.Qp * kPrepHeads) lt[idx / kPrepHeads][idx % kPrepHeads] = v[q];
+            }
         }
-        v[1] += v[0];
-        v[2] += v[1];
-        v[3] += v[2];
-        const float excl = wave_inclusive_sum(v[3], lane) - v[3];
-        if (4 * lane < a.Qp) {
-            f32x4 o = {(excl + v[0]) * kLog2e, (excl + v[1]) * kLog2e, (excl + v[2]) * kLog2e,
-                       (excl + v[3]) * kLog2e};
-            *reinterpret_cast<f32x4*>(a.cs + ((int64_t)k * a.H + h) * a.Qp + 4 * lane) = o;
+        __syncthreads();
+        for (int hh = wave; hh < nh; hh += 4) {
+            float v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = (4 * lane + j < a.Qp) ? lt[4 * lane + j][hh] : 0.f;
+            v[1] += v[0];
+            v[2] += v[1];
+            v[3] += v[2];
+            const float excl = wave_inclusive_sum(v[3], lane) - v[3];
+            if (4 * lane < a.Qp) {
+                f32x4 o = {(excl + v[0]) * kLog2e, (excl + v[1]) * kLog2e, (excl + v[2]) * kLog2e,
+                           (excl + v[3]) * kLog2e};
+                *reinterpret_cast<f32x4*>(a.cs + ((int64_t)k * a.H + h0 + hh) * a.Qp + 4 * lane) = o;
+            }
         }
         return;
     }
 
-    // (b) C B^T tiles (i, j), j <= i, of this chunk and group.  The tile is computed
-    // transposed, D[s][l] = sum_n B[s][n] C[l][n], so that each lane ends with one
-    // row l of C B^T and writes it as runs of 4 consecutive s.
-    const int g = rest;
+    // (b) C B^T tile (i, j), j <= i, one tile per wavefront.  The tile is computed
+    // transposed, D[s][l] = sum_n B[s][n] C[l][n], so that each lane ends with one row l
+    // of C B^T and writes it as runs of 4 consecutive s.  Tiles are stored in the order
+    // of the walk kernel's B-operand fragments: element (l, s) of a tile sits at
+    // ((s / 16) * 64 + ((s % 16) / 8) * 32 + l) * 8 + s % 8, so one fragment of one
+    // wavefront is 1 KB of contiguous memory.
+    const int g = rest / a.cb_groups;
+    const int t = (rest % a.cb_groups) * 4 + wave;
+    const int nlb = (len + 31) >> 5;
+    if (t >= nlb * (nlb + 1) / 2) return;
+    int i = 0;
+    while ((i + 1) * (i + 2) / 2 <= t) ++i;
+    const int j = t - i * (i + 1) / 2;
     const T* Bp = static_cast<const T*>(a.B);
     const T* Cp = static_cast<const T*>(a.C);
-    const int nlb = (len + 31) >> 5;
-    const int ntl = nlb * (nlb + 1) / 2;
-    for (int t = wave; t < ntl; t += 4) {
-        int i = 0;
-        while ((i + 1) * (i + 2) / 2 <= t) ++i;
-        const int j = t - i * (i + 1) / 2;
-        const bool svalid = 32 * j + lr < len, lvalid = 32 * i + lr < len;
-        const T* brow = Bp + ((rowc + 32 * j + lr) * a.G + g) * (int64_t)a.N + 8 * lg;
-        const T* crow = Cp + ((rowc + 32 * i + lr) * a.G + g) * (int64_t)a.N + 8 * lg;
-        f32x16 acc = {};
-        for (int ks = 0; ks < a.N / 16; ++ks) {
-            const frag av = svalid ? E::ldg8(brow + 16 * ks) : E::zero();
-            const frag bv = lvalid ? E::ldg8(crow + 16 * ks) : E::zero();
-            acc = E::mma(acc, av, bv);
-        }
-        T* out = static_cast<T*>(a.cb) + ((int64_t)(k * a.G + g) * a.ntile + t) * 1024 + lr * 32 + 4 * lg;
+    const bool svalid = 32 * j + lr < len, lvalid = 32 * i + lr < len;
+    const T* brow = Bp + ((rowc + 32 * j + lr) * a.G + g) * (int64_t)a.N + 8 * lg;
+    const T* crow = Cp + ((rowc + 32 * i + lr) * a.G + g) * (int64_t)a.N + 8 * lg;
+    f32x16 acc = {};
+    const int nks = a.N / 16;
+    for (int kb = 0; kb < nks; kb += 8) {
+        frag av[8], bv[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) E::st4(out + 8 * q, acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+        for (int q = 0; q < 8; ++q) {
+            const bool ok = kb + q < nks;
+            av[q] = (ok && svalid) ? E::ldg8(brow + 16 * (kb + q)) : E::zero();
+            bv[q] = (ok && lvalid) ? E::ldg8(crow + 16 * (kb + q)) : E::zero();
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (kb + q < nks) acc = E::mma(acc, av[q], bv[q]);
+    }
+    T* out = static_cast<T*>(a.cb) + ((int64_t)(k * a.G + g) * a.ntile + t) * 1024;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        // rows s = 8q + 4lg + 0..3 of this lane's column l = lr
+        T* o = out + (((q >> 1) * 64 + (q & 1) * 32 + lr) * 8 + 4 * lg);
+        E::st4(o, acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
     }
 }
 
-template <typename T, int PT, int NP>
+template <typename T, int PT, int NP, bool CBL>
 __global__ void __launch_bounds__(512) ssd_walk_kernel(WalkArgs a) {
     using E = Elem<T>;
     typedef typename E::frag frag;
@@ -184,10 +221,24 @@ __global__ void __launch_bounds__(512) ssd_walk_kernel(WalkArgs a) {
     constexpr int PSUB = PT / 32, NT = NP / 32;
     constexpr int NTILE_S = PSUB * NT;
     constexpr int TPW = (NTILE_S + 7) / 8;
+    // register prefetch of the next chunk: X rows (PT/8 fragments of 8 per row) and,
+    // when a whole chunk of B fits in LDS and in registers, B rows (NP/8 fragments)
+    constexpr int XSEG = PT / 8, BSEG = NP / 8;
+    constexpr int XPASS = (256 * XSEG + 511) / 512;
+    constexpr int BPASS = (256 * BSEG + 511) / 512;
+    // B of the next chunk is not held in registers across the output phase (registers
+    // are the limit there); it is loaded straight into LDS when the chunk is committed
+    constexpr bool BPRE = false;
+    constexpr int BPASS_R = 1;
+    constexpr int KC = NP / 16 < 4 ? NP / 16 : 4;   // C fragments issued per batch
+    // off-diagonal C B^T tiles of one chunk (at most 28 for 8 blocks), 128 fragments each
+    constexpr int CBPASS = (28 * 128 + 511) / 512;
+
     extern __shared__ __align__(16) unsigned char smem[];
     T* Xs = reinterpret_cast<T*>(smem + a.xs_off);
     T* Xts = reinterpret_cast<T*>(smem + a.xts_off);
     T* Bs = reinterpret_cast<T*>(smem + a.bs_off);
+    T* CBs = Bs;   // the off-diagonal C B^T tiles reuse the B region after the state phase
     T* hs = reinterpret_cast<T*>(smem + a.hs_off);
     float* css = reinterpret_cast<float*>(smem + a.cs_off);
 
@@ -200,6 +251,7 @@ __global__ void __launch_bounds__(512) ssd_walk_kernel(WalkArgs a) {
     const int g = h / (a.H / a.G);
     const int p_base = pt * PT;
     const int H = a.H, P = a.P, N = a.N, G = a.G, Q = a.Q;
+    constexpr bool cb_lds = CBL;
 
     int64_t row0;
     int len_seq, slot0;
@@ -214,6 +266,7 @@ __global__ void __launch_bounds__(512) ssd_walk_kernel(WalkArgs a) {
         for (int u = 0; u < s; ++u) slot0 += (a.seq_offsets[u + 1] - a.seq_offsets[u] + Q - 1) / Q;
     }
     const int nchunks = (len_seq + Q - 1) / Q;
+    const bool one_stage = a.qb >= a.Qp;
 
     const T* X = static_cast<const T*>(a.X);
     const T* Bg = static_cast<const T*>(a.B);
@@ -256,78 +309,264 @@ __global__ void __launch_bounds__(512) ssd_walk_kernel(WalkArgs a) {
                        hacc[k][4 * q + 2], hacc[k][4 * q + 3]);
         }
     };
-    write_state_lds();
 
-    const bool one_stage = a.qb >= a.Qp;
+    auto chunk_rows = [&](int c, int64_t* rowc, int* len) {
+        *rowc = row0 + (int64_t)c * Q;
+        *len = min(Q, len_seq - c * Q);
+        return ((*len + 31) >> 5) * 32;
+    };
+
+    // ---- staging of X, X~, B and the cumsum: global -> registers -> LDS
+    frag px[XPASS];
+    float pcs_r[XPASS], pcs_e[XPASS];
+    frag pb[BPASS_R];
+    float pcs;
+    constexpr uint32_t ES = sizeof(T);
+    auto x_rsrc = [&](int64_t rowc, int len) {
+        return make_rsrc(X + rowc * H * (int64_t)P, (uint32_t)len * H * P * ES);
+    };
+    auto bc_rsrc = [&](const T* base, int64_t rowc, int len) {
+        return make_rsrc(base + rowc * G * (int64_t)N, (uint32_t)len * G * N * ES);
+    };
+    auto prefetch_in = [&](int c) {
+        int64_t rowc;
+        int len;
+        const int rows = chunk_rows(c, &rowc, &len);
+        const rsrc_t xr = x_rsrc(rowc, len);
+        const rsrc_t csr = make_rsrc(a.cs + ((int64_t)(slot0 + c) * H + h) * a.Qp, rows * 4);
+#pragma unroll
+        for (int k = 0; k < XPASS; ++k) {
+            const int idx = tid + 512 * k;
+            const int r = idx / XSEG, c8 = (idx % XSEG) * 8;
+            const int p = p_base + c8;
+            px[k] = E::ldb8(xr, p < P ? (uint32_t)((r * H + h) * P + p) * ES : kOutOfRange);
+            pcs_r[k] = ldb_f32(csr, 4u * r);
+            pcs_e[k] = ldb_f32(csr, 4u * (r | 31));
+        }
+        if (BPRE && one_stage) {
+            const rsrc_t br = bc_rsrc(Bg, rowc, len);
+#pragma unroll
+            for (int k = 0; k < BPASS_R; ++k) {
+                const int idx = tid + 512 * k;
+                const int r = idx / BSEG, c8 = (idx % BSEG) * 8;
+                pb[k] = E::ldb8(br, c8 < N ? (uint32_t)((r * G + g) * N + c8) * ES : kOutOfRange);
+            }
+        }
+        pcs = ldb_f32(csr, 4u * tid);
+    };
+    // B rows [rb0, rb1) of chunk c straight into LDS, all loads of a batch issued first
+    auto load_b_rows = [&](int c, int rb0, int rb1) {
+        int64_t rowc;
+        int len;
+        chunk_rows(c, &rowc, &len);
+        const rsrc_t br = bc_rsrc(Bg, rowc, len);
+        constexpr int BB = 8;
+        for (int base = 0; base < (rb1 - rb0) * BSEG; base += BB * 512) {
+            frag v[BB];
+#pragma unroll
+            for (int k = 0; k < BB; ++k) {
+                const int idx = base + tid + 512 * k;
+                const int r = rb0 + idx / BSEG, c8 = (idx % BSEG) * 8;
+                v[k] = E::ldb8(br, (c8 < N && r < rb1) ? (uint32_t)((r * G + g) * N + c8) * ES : kOutOfRange);
+            }
+#pragma unroll
+            for (int k = 0; k < BB; ++k) {
+                const int idx = base + tid + 512 * k;
+                const int r = rb0 + idx / BSEG, c8 = (idx % BSEG) * 8;
+                if (r < rb1) *reinterpret_cast<frag*>(Bs + (r - rb0) * BS + c8) = v[k];
+            }
+        }
+    };
+    auto commit_in = [&](int c) {
+        int64_t rowc;
+        int len;
+        const int rows = chunk_rows(c, &rowc, &len);
+#pragma unroll
+        for (int k = 0; k < XPASS; ++k) {
+            const int idx = tid + 512 * k;
+            const int r = idx / XSEG, c8 = (idx % XSEG) * 8;
+            if (r < rows) {
+                const float f = fast_exp2(pcs_e[k] - pcs_r[k]);
+                frag vt;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) vt[q] = E::from_f(E::to_f(px[k][q]) * f);
+                *reinterpret_cast<frag*>(Xs + r * XS + c8) = px[k];
+                *reinterpret_cast<frag*>(Xts + r * XS + c8) = vt;
+            }
+        }
+        if (BPRE && one_stage) {
+#pragma unroll
+            for (int k = 0; k < BPASS_R; ++k) {
+                const int idx = tid + 512 * k;
+                const int r = idx / BSEG, c8 = (idx % BSEG) * 8;
+                if (r < rows) *reinterpret_cast<frag*>(Bs + r * BS + c8) = pb[k];
+            }
+        } else if (one_stage) {
+            load_b_rows(c, 0, rows);
+        }
+        if (tid < rows) css[tid] = pcs;
+    };
+
+    // ---- operands of the output phase, prefetched during the state phase
+    frag pcb[cb_lds ? CBPASS : 1];   // off-diagonal C B^T tiles of the chunk (staged to LDS)
+    frag pdg[4];            // diagonal C B^T fragments of this wave's first unit
+    frag pc1[KC];           // first C fragments of this wave's first tile
+    auto row_of_offdiag = [](int o) {   // o = i (i - 1) / 2 + j, j < i  ->  i
+        int i = 1;
+        while ((i + 1) * i / 2 <= o) ++i;
+        return i;
+    };
+    auto cb_rsrc = [&](int slot) {
+        return make_rsrc(static_cast<const T*>(a.cb) + (int64_t)(slot * G + g) * a.ntile * 1024,
+                         (uint32_t)a.ntile * 1024 * ES);
+    };
+    // byte offset of the C fragment (row l of the chunk, K-step ks) of this lane
+    auto c_off = [&](int l, int ks) {
+        return 16 * ks < N ? (uint32_t)((l * G + g) * N + 16 * ks + 8 * lg) * ES : kOutOfRange;
+    };
+    auto prefetch_out = [&](int c) {
+        int64_t rowc;
+        int len;
+        const int rows = chunk_rows(c, &rowc, &len);
+        const int nlb = rows >> 5;
+        const rsrc_t cbr = cb_rsrc(slot0 + c);
+        if constexpr (cb_lds) {
+            const int nto = nlb * (nlb - 1) / 2;
+#pragma unroll
+            for (int k = 0; k < CBPASS; ++k) {
+                const int e = tid + 512 * k;
+                const int o = e >> 7, f = e & 127;
+                pcb[k] = E::ldb8(cbr, o < nto ? (uint32_t)((o + row_of_offdiag(o)) * 1024 + f * 8) * ES : kOutOfRange);
+            }
+        }
+        const int npairs = (nlb + 1) >> 1;
+        if (wave < npairs * PSUB) {
+            const int pa = wave / PSUB;
+            const int i1 = pa, i2 = nlb - 1 - pa;
+            const bool two = i2 != i1;
+            const uint32_t d1 = (uint32_t)((i1 * (i1 + 1) / 2 + i1) * 1024 + lane * 8) * ES;
+            const uint32_t d2 = two ? (uint32_t)((i2 * (i2 + 1) / 2 + i2) * 1024 + lane * 8) * ES : kOutOfRange;
+            pdg[0] = E::ldb8(cbr, d1);
+            pdg[1] = E::ldb8(cbr, d1 + 512 * ES);
+            pdg[2] = E::ldb8(cbr, d2);
+            pdg[3] = E::ldb8(cbr, two ? d2 + 512 * ES : kOutOfRange);
+            const rsrc_t cr = bc_rsrc(Cg, rowc, len);
+#pragma unroll
+            for (int q = 0; q < KC; ++q) pc1[q] = E::ldb8(cr, c_off(32 * i1 + lr, q));
+        }
+    };
+
+    auto cb_frag_diag = [&](rsrc_t cbr, int i, int ks) {
+        return E::ldb8(cbr, (uint32_t)((i * (i + 1) / 2 + i) * 1024 + ks * 512 + lane * 8) * ES);
+    };
+
+    if (nchunks > 0) {
+        prefetch_in(0);
+        commit_in(0);
+    }
+    write_state_lds();
+    __syncthreads();
 
     for (int c = 0; c < nchunks; ++c) {
-        const int64_t rowc = row0 + (int64_t)c * Q;
-        const int len = min(Q, len_seq - c * Q);
-        const int nlb = (len + 31) >> 5;
-        const int rows = nlb * 32;
+        int64_t rowc;
+        int len;
+        const int rows = chunk_rows(c, &rowc, &len);
+        const int nlb = rows >> 5;
         const int slot = slot0 + c;
-        const float* csg = a.cs + ((int64_t)slot * H + h) * a.Qp;
+        prefetch_out(c);
 
-        // ---- phase 1: chunk cumsum, X and decay-scaled X~ into LDS (and B if it fits)
-        for (int i = tid; i < rows; i += 512) css[i] = csg[i];
-        for (int idx = tid; idx < rows * (PT / 8); idx += 512) {
-            const int r = idx / (PT / 8), c8 = (idx % (PT / 8)) * 8;
-            const int p = p_base + c8;
-            frag v = E::zero();
-            if (r < len && p < P) v = E::ldg8(X + ((rowc + r) * H + h) * (int64_t)P + p);
-            const float f = fast_exp2(csg[r | 31] - csg[r]);
-            frag vt;
+        // ---- state phase: h = 2^(cs_last) h + B^T (decay o X), telescoped block by
+        //      block: h = 2^(cs[e_j] - cs[e_{j-1}]) h + B_j^T X~_j   (right and center factors)
+        float prev[TPW];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) vt[q] = E::from_f(E::to_f(v[q]) * f);
-            *reinterpret_cast<frag*>(Xs + r * XS + c8) = v;
-            *reinterpret_cast<frag*>(Xts + r * XS + c8) = vt;
-        }
-        auto load_b_rows = [&](int rb0, int rb1) {
-            for (int idx = tid; idx < (rb1 - rb0) * (NP / 8); idx += 512) {
-                const int r = rb0 + idx / (NP / 8), c8 = (idx % (NP / 8)) * 8;
-                frag v = E::zero();
-                if (r < len && c8 < N) v = E::ldg8(Bg + ((rowc + r) * G + g) * (int64_t)N + c8);
-                *reinterpret_cast<frag*>(Bs + (r - rb0) * BS + c8) = v;
+        for (int k = 0; k < TPW; ++k) prev[k] = 0.f;
+        const int bpb = one_stage ? nlb : a.qb / 32;   // 32-row blocks per B stage
+        for (int jb0 = 0; jb0 < nlb; jb0 += bpb) {
+            const int jb1 = min(nlb, jb0 + bpb);
+            if (!one_stage) {
+                __syncthreads();
+                load_b_rows(c, 32 * jb0, 32 * jb1);
+                __syncthreads();
             }
-        };
-        if (one_stage) load_b_rows(0, rows);
-        __syncthreads();
-
-        // ---- phase 2: output tiles Y^T[p][l] for (32-row block i, 32-wide p sub-tile).
-        //      Wave units pair block a with block nlb-1-a to balance the causal work.
-        const T* cbase_g = static_cast<const T*>(a.cb) + (int64_t)(slot * G + g) * a.ntile * 1024;
-        auto out_tile = [&](int i, int ps) {
-            const int l0 = 32 * i, p0 = 32 * ps;
-            const bool lvalid = l0 + lr < len;
-            f32x16 acc = {};
-            // left factor: C_l . h  (A = h rows from LDS, B = C rows from global)
-            const T* crow = Cg + ((rowc + l0 + lr) * G + g) * (int64_t)N + 8 * lg;
-            for (int ks = 0; ks < N / 16; ++ks) {
-                const frag av = E::lds8(hs + (p0 + lr) * HS + 16 * ks + 8 * lg);
-                const frag bv = lvalid ? E::ldg8(crow + 16 * ks) : E::zero();
-                acc = E::mma(acc, av, bv);
-            }
-            // earlier blocks j < i through (C B^T)_{ij} and X~_j, decayed block to block
-            const T* cbase = cbase_g + (int64_t)(i * (i + 1) / 2) * 1024 + lr * 32 + 8 * lg;
-            float prev = 0.f;
-            for (int j = 0; j < i; ++j) {
-                const float e = css[32 * j + 31];
-                acc *= fast_exp2(e - prev);
-                prev = e;
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const frag av = lds_col<T>(Xts, XS, 32 * j + 16 * ks, p0, lane);
-                    const frag bv = E::ldg8(cbase + j * 1024 + 16 * ks);
-                    acc = E::mma(acc, av, bv);
+            for (int k = 0; k < TPW; ++k) {
+                const int t = wave + 8 * k;
+                if (t >= NTILE_S) continue;
+                const int n0 = 32 * (t / PSUB), p0 = 32 * (t % PSUB);
+                if (n0 >= N || p_base + p0 >= P) continue;
+                for (int j = jb0; j < jb1; ++j) {
+                    const frag a0 = lds_col<T>(Bs, BS, 32 * (j - jb0), n0, lane);
+                    const frag b0 = lds_col<T>(Xts, XS, 32 * j, p0, lane);
+                    const frag a1 = lds_col<T>(Bs, BS, 32 * (j - jb0) + 16, n0, lane);
+                    const frag b1 = lds_col<T>(Xts, XS, 32 * j + 16, p0, lane);
+                    const float e = css[32 * j + 31];
+                    hacc[k] *= fast_exp2(e - prev[k]);
+                    prev[k] = e;
+                    hacc[k] = E::mma(hacc[k], a0, b0);
+                    hacc[k] = E::mma(hacc[k], a1, b1);
                 }
             }
+        }
+        __syncthreads();
+        if constexpr (cb_lds) {
+            const int nto = nlb * (nlb - 1) / 2;
+#pragma unroll
+            for (int k = 0; k < CBPASS; ++k) {
+                const int e = tid + 512 * k;
+                if ((e >> 7) < nto) *reinterpret_cast<frag*>(CBs + e * 8) = pcb[k];
+            }
+        }
+        // the next chunk's inputs travel while the outputs of this one are computed
+        if (c + 1 < nchunks) prefetch_in(c + 1);
+        if constexpr (cb_lds) __syncthreads();
+
+        // ---- output phase: tiles Y^T[p][l] for (32-row block i, 32-wide p sub-tile).
+        //      A wave takes blocks i1 = pa and i2 = nlb-1-pa of one p sub-tile, so the
+        //      causal work is balanced and the X~ fragments are shared by both tiles.
+        const rsrc_t cbr = cb_rsrc(slot);
+        const rsrc_t cr = bc_rsrc(Cg, rowc, len);
+        auto cb_frag = [&](int i, int j, int ks) -> frag {
+            if constexpr (cb_lds) return E::lds8(CBs + (i * (i - 1) / 2 + j) * 1024 + ks * 512 + lane * 8);
+            return E::ldb8(cbr, (uint32_t)((i * (i + 1) / 2 + j) * 1024 + ks * 512 + lane * 8) * ES);
+        };
+        // one output tile: block i, p sub-tile p0; the first unit of a wave takes its
+        // diagonal and first C fragments from the prefetch registers
+        auto out_tile = [&](int i, int p0, bool pre, frag da, frag db) {
+            const bool lvalid = 32 * i + lr < len;
+            f32x16 acc = {};
+            // left factor: acc = h C_l^T over n, C fragments issued KC at a time
+#pragma unroll
+            for (int kb = 0; kb < NP / 16; kb += KC) {
+                frag cf[KC];
+#pragma unroll
+                for (int q = 0; q < KC; ++q) cf[q] = (pre && kb == 0) ? pc1[q] : E::ldb8(cr, c_off(32 * i + lr, kb + q));
+#pragma unroll
+                for (int q = 0; q < KC; ++q) {
+                    if (16 * (kb + q) >= N) continue;
+                    const frag av = E::lds8(hs + (p0 + lr) * HS + 16 * (kb + q) + 8 * lg);
+                    acc = E::mma(acc, av, cf[q]);
+                }
+            }
+            // earlier blocks j through (C B^T)_{ij} and X~_j, decayed block to block
+            float prevf = 0.f;
+            for (int j = 0; j < i; ++j) {
+                const frag x0 = lds_col<T>(Xts, XS, 32 * j, p0, lane);
+                const frag x1 = lds_col<T>(Xts, XS, 32 * j + 16, p0, lane);
+                const frag u0 = cb_frag(i, j, 0), u1 = cb_frag(i, j, 1);
+                const float e = css[32 * j + 31];
+                acc *= fast_exp2(e - prevf);
+                prevf = e;
+                acc = E::mma(acc, x0, u0);
+                acc = E::mma(acc, x1, u1);
+            }
+            // row scale and diagonal tile: exact mask 2^(cs[l] - cs[s]), s <= l, on unscaled X
+            const int l0 = 32 * i;
             const float csl = css[l0 + lr];
-            acc *= fast_exp2(csl - prev);
-            // diagonal tile: exact mask 2^(cs[l] - cs[s]), s <= l, on unscaled X
+            acc *= fast_exp2(csl - prevf);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const frag av = lds_col<T>(Xs, XS, l0 + 16 * ks, p0, lane);
-                const frag raw = E::ldg8(cbase + i * 1024 + 16 * ks);
+                const frag raw = ks == 0 ? da : db;
                 frag m;
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
@@ -348,46 +587,22 @@ __global__ void __launch_bounds__(512) ssd_walk_kernel(WalkArgs a) {
         };
         const int npairs = (nlb + 1) >> 1;
         for (int u = wave; u < npairs * PSUB; u += 8) {
+            const bool first = u == wave;
             const int ps = u % PSUB, pa = u / PSUB;
-            if (p_base + 32 * ps >= P) continue;
-            out_tile(pa, ps);
-            if (nlb - 1 - pa != pa) out_tile(nlb - 1 - pa, ps);
-        }
-
-        // ---- phase 3: chunk state, h = 2^(cs_last) h + B^T (decay o X), telescoped
-        //      block by block: h = 2^(cs[e_j] - cs[e_{j-1}]) h + B_j^T X~_j.
-        float prev[TPW];
-#pragma unroll
-        for (int k = 0; k < TPW; ++k) prev[k] = 0.f;
-        const int bpb = one_stage ? nlb : a.qb / 32;   // 32-row blocks per B stage
-        for (int jb0 = 0; jb0 < nlb; jb0 += bpb) {
-            const int jb1 = min(nlb, jb0 + bpb);
-            if (!one_stage) {
-                __syncthreads();
-                load_b_rows(32 * jb0, 32 * jb1);
-                __syncthreads();
-            }
-#pragma unroll
-            for (int k = 0; k < TPW; ++k) {
-                const int t = wave + 8 * k;
-                if (t >= NTILE_S) continue;
-                const int n0 = 32 * (t / PSUB), p0 = 32 * (t % PSUB);
-                if (n0 >= N || p_base + p0 >= P) continue;
-                for (int j = jb0; j < jb1; ++j) {
-                    const float e = css[32 * j + 31];
-                    hacc[k] *= fast_exp2(e - prev[k]);
-                    prev[k] = e;
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
-                        const frag av = lds_col<T>(Bs, BS, 32 * (j - jb0) + 16 * ks, n0, lane);
-                        const frag bv = lds_col<T>(Xts, XS, 32 * j + 16 * ks, p0, lane);
-                        hacc[k] = E::mma(hacc[k], av, bv);
-                    }
-                }
+            const int p0 = 32 * ps;
+            if (p_base + p0 >= P) continue;
+            const int i1 = pa, i2 = nlb - 1 - pa;
+            if (first) out_tile(i1, p0, true, pdg[0], pdg[1]);
+            else out_tile(i1, p0, false, cb_frag_diag(cbr, i1, 0), cb_frag_diag(cbr, i1, 1));
+            if (i2 != i1) {
+                if (first) out_tile(i2, p0, false, pdg[2], pdg[3]);
+                else out_tile(i2, p0, false, cb_frag_diag(cbr, i2, 0), cb_frag_diag(cbr, i2, 1));
             }
         }
         __syncthreads();
         write_state_lds();
+        if (c + 1 < nchunks) commit_in(c + 1);
+        __syncthreads();
     }
 
     if (a.final_state) {

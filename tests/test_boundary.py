@@ -24,7 +24,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["ssd_abi_version", "ssd_check_problem", "ssd_forward",
-                                           "ssd_status_string", "ssd_workspace_bytes"])
+                                           "ssd_forward_stage", "ssd_status_string",
+                                           "ssd_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -133,3 +134,21 @@ def test_binding_refuses_host_tensors():
     X = torch.zeros(1, 4, 1, 16)
     with pytest.raises(ValueError):
         ssd.forward(X, torch.zeros(1, 4, 1), torch.zeros(1, 4, 1, 16), torch.zeros(1, 4, 1, 16), 16)
+
+
+@pytest.mark.parametrize("stage", [0, 3, -1])
+def test_forward_stage_rejects_unknown_stage(stage):
+    p = prob()
+    a = ADDR
+    assert ssd.ssd_forward_stage(stage, p, a["X"], a["logA"], a["B"], a["C"], a["init"], None,
+                                 a["Y"], a["final"], a["ws"], ssd.ssd_workspace_bytes(p),
+                                 None) == ssd.SSD_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("stage", [1, 2])
+def test_forward_stage_validates_like_forward(stage):
+    p = prob()
+    a = ADDR
+    assert ssd.ssd_forward_stage(stage, p, a["X"] + 4, a["logA"], a["B"], a["C"], a["init"], None,
+                                 a["Y"], a["final"], a["ws"], ssd.ssd_workspace_bytes(p),
+                                 None) == ssd.SSD_ERR_INVALID_ARG
