@@ -8,6 +8,7 @@
 
 #include "ssd.h"
 #include "ssd_kernels.h"
+#include "ssd_walk_split.h"
 
 namespace {
 
@@ -24,6 +25,7 @@ struct Plan {
     int64_t nslots, nitems;
     size_t cs_off, cb_off, ws_bytes;
     int lds_bytes, xs_off, xts_off, bs_off, hs_off, cs_lds_off;
+    int split;        // the split-role walker (bf16, 256-row chunks, d_state 64 / 128)
     walk_fn_t walk;   // the walk kernel instance for this plan
 };
 
@@ -143,6 +145,23 @@ int make_plan(const ssd_problem* p, Plan* pl) {
     pl->walk = p->dtype == SSD_DTYPE_BF16 ? pick_walk_bf16(pl->PT, pl->NP, pl->cb_lds != 0)
                                           : (pl->cb_lds ? nullptr : pick_walk_f32(pl->NP));
     if (!pl->walk) return SSD_ERR_UNSUPPORTED;
+    // the common layer shapes take the split-role walker: 64-wide P tiles, whole chunks
+    pl->split = 0;
+    if (p->dtype == SSD_DTYPE_BF16 && pl->Q == 256 && (N == 64 || N == 128) && P % 64 == 0) {
+        pl->split = 1;
+        pl->PT = 64;
+        pl->ptiles = P / 64;
+        pl->nitems = p->nseq * p->nheads * pl->ptiles;
+        pl->qb = pl->Qp;
+        pl->cb_lds = 0;
+        if (N == 64) {
+            pl->walk = ssd::ssd_walk_split_kernel<64>;
+            pl->lds_bytes = ssd::SplitLds<64>::bytes;
+        } else {
+            pl->walk = ssd::ssd_walk_split_kernel<128>;
+            pl->lds_bytes = ssd::SplitLds<128>::bytes;
+        }
+    }
     return SSD_OK;
 }
 

@@ -43,6 +43,13 @@ constexpr int kRsrcWord3 = 0x00020000;   // gfx9 raw buffer, no swizzle
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
 }
+// A value the optimizer must treat as unknown at this point: offsets derived from it are
+// recomputed where they are used instead of being hoisted out of a loop and held in
+// (or spilled from) registers for its whole length.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
 __device__ __forceinline__ float ldb_f32(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }
@@ -68,6 +75,11 @@ template <> struct Elem<__bf16> {
     // seen to shrink the load.
     __device__ static __forceinline__ frag ldb8(rsrc_t r, uint32_t off) {
         return __builtin_bit_cast(frag, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+    }
+    // the same with a uniform byte offset in a scalar register; only for loads that are
+    // known to be in range (the scalar offset takes no part in the range check)
+    __device__ static __forceinline__ frag ldb8(rsrc_t r, uint32_t voff, uint32_t soff) {
+        return __builtin_bit_cast(frag, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
     }
     // 8 contiguous elements from LDS.
     __device__ static __forceinline__ frag lds8(const __bf16* p) {
@@ -144,6 +156,62 @@ lds_col<float>(const float* M, int stride, int r0, int c0, int lane) {
     for (int q = 0; q < 8; ++q) r[q] = p[q * stride];
     return r;
 }
+
+// Row-major LDS matrices of W columns.  bf16: rows are not padded; the 16-byte units
+// of a row are XOR-swizzled by the row index so that the four rows read together by
+// a transposing load fall in different banks.  f32: rows padded by 16 bytes.
+template <typename T, int W> struct LdsMat;
+
+template <int W> struct LdsMat<__bf16, W> {
+    static constexpr int stride = W;
+    static constexpr int rows_bytes(int rows) { return rows * W * 2; }
+    __device__ static __forceinline__ int swz(int r) {
+        return W >= 64 ? 2 * (r & 3) : 2 * ((r >> 1) & 1);
+    }
+    // element (r, c) with c % 4 == 0: start of a 4- or 8-element piece inside a unit
+    __device__ static __forceinline__ int idx(int r, int c) {
+        return r * W + ((((c >> 3) ^ swz(r)) << 3) | (c & 7));
+    }
+};
+
+template <int W> struct LdsMat<float, W> {
+    static constexpr int stride = W + 4;
+    static constexpr int rows_bytes(int rows) { return rows * (W + 4) * 4; }
+    __device__ static __forceinline__ int idx(int r, int c) { return r * (W + 4) + c; }
+};
+
+// Column fragment of an LDS matrix M (layout LdsMat<T, W>): the lane receives
+// M[r0 + 8*lg + q][c0 + lr], q = 0..7.  This is the operand shape of both "A = M^T"
+// (rows of M along K) and "B = M" (rows of M along K).
+// bf16 uses two ds_read_b64_tr_b16: inside each group of 16 lanes, lane i reads 4
+// consecutive elements of row (i / 4) at column 4 * (i % 4) of a 4 x 16 block and the
+// hardware hands lane j the j-th column of that block.
+template <typename T, int W> struct LdsCol;
+
+template <int W> struct LdsCol<__bf16, W> {
+    __device__ static __forceinline__ bf16x8 get(const __bf16* M, int r0, int c0, int lane) {
+        typedef LdsMat<__bf16, W> L;
+        const int row = r0 + 8 * (lane >> 5) + ((lane & 15) >> 2);
+        const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        const __bf16* p0 = M + L::idx(row, col);
+        const __bf16* p1 = M + L::idx(row + 4, col);
+        bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SSD_LDS bf16x4*)(SSD_LDS __bf16*)p0);
+        bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SSD_LDS bf16x4*)(SSD_LDS __bf16*)p1);
+        bf16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return r;
+    }
+};
+
+template <int W> struct LdsCol<float, W> {
+    __device__ static __forceinline__ f32x8 get(const float* M, int r0, int c0, int lane) {
+        typedef LdsMat<float, W> L;
+        const float* p = M + L::idx(r0 + 8 * (lane >> 5), c0 + (lane & 31));
+        f32x8 r;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) r[q] = p[q * L::stride];
+        return r;
+    }
+};
 
 // Element 16*ks + 8*lg + q of a 32-wide row, as a (row, column) index inside a
 // 32 x 32 tile: the K position of fragment element q at K-step ks.

@@ -154,6 +154,32 @@ def test_bitwise_repeatable():
     np.testing.assert_array_equal(F1, F2)
 
 
+# The common layer shapes (bf16, 256-row chunks, d_state 64 or 128, head dimension a
+# multiple of 64) run on their own walker; these cases reach its edges.
+@pytest.mark.parametrize("case", ["varlen", "strong_decay", "headdim128", "one_chunk_n64", "a_one"])
+def test_layer_shape_walker_edges(case):
+    if case == "varlen":
+        lens = [5, 0, 300, 1, 256, 257, 600, 33]
+        inp = make_inputs(1, sum(lens), 4, 64, 128, 2, "bf16", seed=1000, init_state=True,
+                          seq_lengths=lens)
+        Y, F = check(inp, 256, case)
+        np.testing.assert_array_equal(F[1], inp.init[1].astype(np.float64))
+    elif case == "strong_decay":
+        inp = make_inputs(1, 512, 2, 64, 128, 1, "bf16", seed=1001)
+        inp.logA[:] = -1e4
+        check(inp, 256, case)
+    elif case == "headdim128":
+        inp = make_inputs(2, 520, 3, 128, 64, 1, "bf16", seed=1002, init_state=True)
+        check(inp, 256, case)
+    elif case == "one_chunk_n64":
+        inp = make_inputs(3, 256, 2, 64, 64, 2, "bf16", seed=1003)
+        check(inp, 256, case)
+    else:
+        inp = make_inputs(1, 700, 2, 64, 128, 1, "bf16", seed=1004, init_state=True)
+        inp.logA[:] = 0.0
+        check(inp, 256, case)
+
+
 SAMPLE_HEADS = {"cfg1_mamba2_2.7b_bf16": [0, 41, 79], "cfg2a_state64_bf16": [0, 31],
                 "cfg2b_state256_bf16": [5, 30], "cfg3_long16k_bf16": [0, 47, 79],
                 "cfg4_varlen32k_bf16": [0, 13, 79]}
