@@ -23,7 +23,7 @@ struct Plan {
     int Q, Qp, nlb, ntile;
     int PT, NP, ptiles, qb, cb_lds;
     int64_t nslots, nitems;
-    size_t cs_off, cb_off, ws_bytes;
+    size_t cs_off, cb_off, bt_off, ct_off, ws_bytes;
     int lds_bytes, xs_off, xts_off, bs_off, hs_off, cs_lds_off;
     int split;        // the split-role walker (bf16, 256-row chunks, d_state 64 / 128)
     walk_fn_t walk;   // the walk kernel instance for this plan
@@ -130,7 +130,13 @@ int make_plan(const ssd_problem* p, Plan* pl) {
     const size_t cs_bytes = (size_t)pl->nslots * p->nheads * pl->Qp * sizeof(float);
     pl->cb_off = align_up(pl->cs_off + cs_bytes, 256);
     const size_t cb_bytes = (size_t)pl->nslots * p->ngroups * pl->ntile * 1024 * es;
-    pl->ws_bytes = align_up(pl->cb_off + cb_bytes, 256);
+    pl->bt_off = align_up(pl->cb_off + cb_bytes, 256);
+    // the common layer shapes take the split-role walker (64-wide P tiles, whole
+    // chunks), which also needs B^T of every chunk in fragment order
+    pl->split = p->dtype == SSD_DTYPE_BF16 && pl->Q == 256 && (N == 64 || N == 128) && P % 64 == 0;
+    const size_t bt_bytes = pl->split ? (size_t)pl->nslots * p->ngroups * ssd::split_bt_bytes(N) : 0;
+    pl->ct_off = align_up(pl->bt_off + bt_bytes, 256);
+    pl->ws_bytes = align_up(pl->ct_off + bt_bytes, 256);   // C fragments: as many bytes as B^T
     // stage the off-diagonal C B^T tiles in LDS when they fit next to a whole chunk of B
     // (or the largest B stage that fits), else read them from global memory
     pl->cb_lds = p->dtype == SSD_DTYPE_BF16 ? 1 : 0;
@@ -145,10 +151,7 @@ int make_plan(const ssd_problem* p, Plan* pl) {
     pl->walk = p->dtype == SSD_DTYPE_BF16 ? pick_walk_bf16(pl->PT, pl->NP, pl->cb_lds != 0)
                                           : (pl->cb_lds ? nullptr : pick_walk_f32(pl->NP));
     if (!pl->walk) return SSD_ERR_UNSUPPORTED;
-    // the common layer shapes take the split-role walker: 64-wide P tiles, whole chunks
-    pl->split = 0;
-    if (p->dtype == SSD_DTYPE_BF16 && pl->Q == 256 && (N == 64 || N == 128) && P % 64 == 0) {
-        pl->split = 1;
+    if (pl->split) {
         pl->PT = 64;
         pl->ptiles = P / 64;
         pl->nitems = p->nseq * p->nheads * pl->ptiles;
@@ -289,7 +292,10 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
     pa.hblocks = (int)((H + ssd::kPrepHeads - 1) / ssd::kPrepHeads);
     pa.cs_blocks = (int)(nslots * pa.hblocks);
     pa.cb_groups = (pl.ntile + 3) / 4;
-    const int64_t prep_blocks = nslots * pa.hblocks + nslots * G * pa.cb_groups;
+    pa.cb_blocks = (int)(nslots * G * pa.cb_groups);
+    pa.bt = pl.split ? ws + pl.bt_off : nullptr;
+    pa.ct = pl.split ? ws + pl.ct_off : nullptr;
+    const int64_t prep_blocks = nslots * pa.hblocks + nslots * G * pa.cb_groups + (pl.split ? nslots * G * 8 : 0);
     if (prep_blocks > INT32_MAX) return SSD_ERR_UNSUPPORTED;
     if (stages & 1)
         hipLaunchKernelGGL(prep, dim3((unsigned)prep_blocks), dim3(kPrepThreads), 0, stream, pa);
@@ -304,6 +310,8 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
     wa.final_state = final_state;
     wa.cs = cs;
     wa.cb = cb;
+    wa.bt = ws + pl.bt_off;
+    wa.ct = ws + pl.ct_off;
     wa.T = T;
     wa.H = (int)H;
     wa.P = (int)P;
