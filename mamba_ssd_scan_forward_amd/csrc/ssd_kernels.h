@@ -253,6 +253,12 @@ __global__ void __launch_bounds__(256) ssd_prep_kernel(PrepArgs a) {
             if (kb + q < nks) acc = E::mma(acc, av[q], bv[q]);
     }
     T* out = static_cast<T*>(a.cb) + ((int64_t)(k * a.G + g) * a.ntile + t) * 1024;
+    if (i == j) {
+        // diagonal tiles carry the causal mask: (C B^T)_{ls} = 0 for s > l
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            if (acc_row(e, lane) > lr) acc[e] = 0.f;
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         // rows s = 8q + 4lg + 0..3 of this lane's column l = lr

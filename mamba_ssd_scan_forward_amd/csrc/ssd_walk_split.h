@@ -45,18 +45,18 @@
 
 namespace ssd {
 
-// LDS of the split walker: raw X [2][256][64] (swizzled), X~ [256][64] (swizzled),
-// h [64][NP + 8], the cumsum [2][256] and, per output wave, its two 32 x 64 Y tiles
-// [2][32][72] on their way to global memory.
+// LDS of the split walker: X~ [2][256][64] (swizzled), h [64][NP + 8], the cumsum
+// [2][256], per output wave its two 32 x 64 Y tiles [2][32][72] on their way to global
+// memory, and per state wave a private copy of the next chunk's cumsum [256].
 template <int NP> struct SplitLds {
-    static constexpr int xs = 0;                        // two buffers
-    static constexpr int xts = xs + 2 * 256 * 64 * 2;
-    static constexpr int hs = xts + 256 * 64 * 2;
+    static constexpr int xts = 0;                       // two buffers
+    static constexpr int hs = xts + 2 * 256 * 64 * 2;
     static constexpr int hstride = NP + 8;
     static constexpr int cs = hs + 64 * hstride * 2;    // two buffers
     static constexpr int ystride = 72;                  // Y rows padded by 16 bytes
     static constexpr int ys = cs + 2 * 256 * 4;         // [2 blocks][4 output waves]
-    static constexpr int bytes = ys + 2 * 4 * 32 * ystride * 2;
+    static constexpr int csp = ys + 2 * 4 * 32 * ystride * 2;   // [4 state waves][256]
+    static constexpr int bytes = csp + 4 * 256 * 4;
 };
 
 // Bytes of B^T fragments per (chunk slot, group) in the workspace.
@@ -75,7 +75,6 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
     constexpr int HS = L::hstride;
 
     extern __shared__ __align__(16) unsigned char smem[];
-    __bf16* Xts = reinterpret_cast<__bf16*>(smem + L::xts);
     __bf16* hs = reinterpret_cast<__bf16*>(smem + L::hs);
 
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
@@ -111,7 +110,7 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
     __bf16* Y = static_cast<__bf16*>(a.Y);
     const int64_t state_base = ((int64_t)s * H + h) * P * (int64_t)N;
 
-    auto xs_buf = [&](int c) { return reinterpret_cast<__bf16*>(smem + L::xs + (c & 1) * 256 * 64 * 2); };
+    auto xts_buf = [&](int c) { return reinterpret_cast<__bf16*>(smem + L::xts + (c & 1) * 256 * 64 * 2); };
     auto cs_buf = [&](int c) { return reinterpret_cast<float*>(smem + L::cs + (c & 1) * 256 * 4); };
     auto chunk_at = [&](int c, int64_t* rowc, int* len) {
         *rowc = row0 + (int64_t)c * 256;
@@ -149,29 +148,38 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) px[k] = E::ldb8(xr, xb + k * xstep);
         };
-        // the cumsum of chunk c (1 KB) straight to its LDS buffer: one load instruction of
-        // wave 0, complete at the next barrier.  It is issued after the wave's last LDS
-        // read of the current chunk (the compiler orders later LDS reads behind it).
+        // the cumsum of chunk c (1 KB) straight to LDS: wave 0 fills the shared buffer,
+        // every state wave its private copy.  Issued after the wave's last LDS read of the
+        // current chunk; the wave then waits for all its outstanding memory operations
+        // (the older ones are long complete), so the private copy can be read at once and
+        // the shared one is complete before the next barrier.
+        float* csp = reinterpret_cast<float*>(smem + L::csp) + sw * 256;
         auto dma_cs = [&](int c) {
-            if (sw == 0) {
-                const rsrc_t csr = make_rsrc(a.cs + ((int64_t)(slot0 + c) * H + h) * 256, 256 * 4);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(csr, (SSD_LDS void*)cs_buf(c), 16, opaque(16u * lane), 0, 0, 0);
+            const rsrc_t csr = make_rsrc(a.cs + ((int64_t)(slot0 + c) * H + h) * 256, 256 * 4);
+            const uint32_t lb = opaque(16u * lane);
+            if (sw == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(csr, (SSD_LDS void*)cs_buf(c), 16, lb, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(csr, (SSD_LDS void*)csp, 16, lb, 0, 0, 0);
+            __builtin_amdgcn_s_waitcnt(0);
+        };
+        // X~ = X scaled by its decay to the end of its 32-row block, from the private copy
+        // of the cumsum; done before B_mid, while the output waves still read this chunk
+        frag pxt[8];
+        auto scale_x = [&]() {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int r = (ts >> 3) + 32 * k;
+                const float f = fast_exp2(csp[32 * k + 31] - csp[r]);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) pxt[k][q] = E::from_f(E::to_f(px[k][q]) * f);
             }
         };
-        // raw X and X~ of chunk c into LDS (raw X: buffer c & 1); the cumsum of the chunk
-        // is in its LDS buffer already
+        // X~ of chunk c into its LDS buffer (c & 1)
         auto commit_x = [&](int c) {
-            __bf16* Xs = xs_buf(c);
-            const float* css = cs_buf(c);
+            __bf16* Xt = xts_buf(c);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const int r = (ts >> 3) + 32 * k, c8 = (ts & 7) * 8;
-                const float f = fast_exp2(css[32 * k + 31] - css[r]);
-                frag vt;
-#pragma unroll
-                for (int q = 0; q < 8; ++q) vt[q] = E::from_f(E::to_f(px[k][q]) * f);
-                *reinterpret_cast<frag*>(Xs + XL::idx(r, c8)) = px[k];
-                *reinterpret_cast<frag*>(Xts + XL::idx(r, c8)) = vt;
+                *reinterpret_cast<frag*>(Xt + XL::idx(r, c8)) = pxt[k];
             }
         };
         // Y tile (block slot u) of output wave sw for chunk c: 8 whole rows per store
@@ -189,14 +197,25 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
                     *reinterpret_cast<frag*>(Y + ((rowc + 32 * i + r) * H + h) * (int64_t)P + p_base + 8 * (lane & 7)) = v;
             }
         };
+        // h as bf16, packed before B_mid and written after it
+        u32x2 hpk[TPS][4];
+        auto pack_h = [&]() {
+#pragma unroll
+            for (int u = 0; u < TPS; ++u)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const bf16x4 v = {(__bf16)hacc[u][4 * q], (__bf16)hacc[u][4 * q + 1],
+                                      (__bf16)hacc[u][4 * q + 2], (__bf16)hacc[u][4 * q + 3]};
+                    hpk[u][q] = __builtin_bit_cast(u32x2, v);
+                }
+        };
         auto write_h = [&]() {
 #pragma unroll
             for (int u = 0; u < TPS; ++u) {
                 const int n0 = tile_n0(u), p = tile_p0(u) + lr;
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    E::st4(hs + p * HS + n0 + 8 * q + 4 * lg, hacc[u][4 * q], hacc[u][4 * q + 1],
-                           hacc[u][4 * q + 2], hacc[u][4 * q + 3]);
+                    *reinterpret_cast<u32x2*>(hs + p * HS + n0 + 8 * q + 4 * lg) = hpk[u][q];
             }
         };
         // h = 2^(cs_last) h + B^T (decay o X), telescoped over the 8 blocks.  With one
@@ -206,6 +225,7 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
         constexpr bool DUAL = TPS == 1;
         auto state_chunk = [&](int c) {
             const float* css = cs_buf(c);
+            const __bf16* Xts = xts_buf(c);
             f32x16 hodd = {};
             float ref0 = 0.f, ref1 = 0.f;
 #pragma unroll
@@ -259,7 +279,11 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
             dma_cs(0);
         }
         __syncthreads();   // the cumsum of chunk 0 has landed
-        if (nchunks > 0) commit_x(0);
+        if (nchunks > 0) {
+            scale_x();
+            commit_x(0);
+        }
+        pack_h();
         write_h();
         __syncthreads();
         for (int c = 0; c < nchunks; ++c) {
@@ -270,7 +294,9 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
             if (more) {
                 dma_cs(c + 1);
                 load_bt(c + 1);
+                scale_x();
             }
+            pack_h();
             __syncthreads();   // B_mid: X~ and h of chunk c are no longer read
             store_y(c, 1);
             write_h();
@@ -302,7 +328,6 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
                             // reloaded for the next chunk once its block has taken it
         frag pcb[14];       // off-diagonal C B^T: tile t < i2 is (i2, t), else (i1, 6 - t)
         frag pdg[2][2];     // diagonal C B^T (block, K-step)
-        frag mk[2];         // decay-masked diagonal tile of the current block (K-step)
         f32x16 acc[2];      // Y^T tiles of the current block (p sub-tile)
 
         // C rows of block u of chunk c, from the fragment-ordered copy (1 KB per fragment)
@@ -338,6 +363,7 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
         // cs[e_{i-1}] (0 for the first block)
         auto left_and_chain = [&](int c, int u) -> float {
             const float* css = cs_buf(c);
+            const __bf16* Xts = xts_buf(c);
             const int i = u == 0 ? i1 : i2;
             acc[0] = f32x16{};
             acc[1] = f32x16{};
@@ -389,43 +415,70 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
         };
         // the exact decay mask of a diagonal tile, 2^(cs[l] - cs[s]) (C B^T)_{ls} for s <= l
         // (one fragment serves both p sub-tiles)
-        auto build_mask = [&](int c, int u) {
-            const float* css = cs_buf(c);
-            const int l0 = 32 * (u == 0 ? i1 : i2);
-            const float csl = css[l0 + lr];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const f32x4 c0 = *reinterpret_cast<const f32x4*>(css + l0 + 16 * ks + 8 * lg);
-                const f32x4 c1 = *reinterpret_cast<const f32x4*>(css + l0 + 16 * ks + 8 * lg + 4);
-                const float cv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const int sl = 16 * ks + 8 * lg + q;
-                    const float w = (sl <= lr) ? E::to_f(pdg[u][ks][q]) * fast_exp2(csl - cv[q]) : 0.f;
-                    mk[ks][q] = E::from_f(w);
-                }
-            }
-            // the next chunk's diagonal tile of this block travels while this one is used
-            if (c + 1 < nchunks) load_dg(c + 1, u);
-        };
-        // row scale 2^(cs[l] - cs[e_{i-1}]), the diagonal tile on unscaled X, and the
-        // tile to this wave's LDS area (block slot u) for the state waves to store
+        // The diagonal block.  When the block's decay span R = cs[first row] - cs[e_i] is
+        // at most 100 (log2 units; Mamba-2 parameters give at most about 74) it is one
+        // more step of the chain, on X~ and the causally masked tile (masked once by the
+        // prep kernel): acc = 2^(cs[e_i] - cs[e_{i-1}]) acc + (C B^T)_ii X~_i, then the row
+        // scale 2^(cs[l] - cs[e_i]) <= 2^R.  Otherwise (very strong decay, where X~ would
+        // lose rows to underflow) the exact mask 2^(cs[l] - cs[s]) (C B^T)_{ls} is applied
+        // to unscaled X read from global memory.  The tile then goes to this wave's LDS
+        // area (block slot u) for the state waves to store.
         auto diag = [&](int c, int u, float prev) {
             const float* css = cs_buf(c);
-            const __bf16* Xs = xs_buf(c);
             const int l0 = 32 * (u == 0 ? i1 : i2);
+            const float e = css[l0 + 31];
+            const float csl = css[l0 + lr];
+            const bool moderate = __builtin_amdgcn_readfirstlane((int)(css[l0] - e <= 100.f)) != 0;
+            // acc = f2 (f1 acc + X_blk^T D): the branches only choose X_blk, D, f1 and f2
+            const __bf16* xsrc;
+            frag dg[2];
+            float f1, f2;
+            if (moderate) {
+                xsrc = xts_buf(c) + l0 * 64;   // row l0 of X~ (the swizzle depends on row & 3 only)
+                dg[0] = pdg[u][0];
+                dg[1] = pdg[u][1];
+                f1 = fast_exp2(e - prev);
+                f2 = fast_exp2(csl - e);
+            } else {
+                // unscaled X of the block from global memory, staged in this wave's Y area
+                // (the transposing reads need it in LDS), and the exact mask
+                int64_t rowc;
+                int len;
+                chunk_at(c, &rowc, &len);
+                __bf16* xb = reinterpret_cast<__bf16*>(smem + L::ys) + (u * 4 + ok_) * 32 * L::ystride;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int r = 8 * k + (lane >> 3), c8 = (lane & 7) * 8;
+                    const frag v = l0 + r < len ? E::ldg8(X + ((rowc + l0 + r) * H + h) * (int64_t)P + p_base + c8) : E::zero();
+                    *reinterpret_cast<frag*>(xb + XL::idx(r, c8)) = v;
+                }
+                xsrc = xb;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const int sl = 16 * ks + 8 * lg + q;
+                        const float w = (sl <= lr) ? E::to_f(pdg[u][ks][q]) * fast_exp2(csl - css[l0 + sl]) : 0.f;
+                        dg[ks][q] = E::from_f(w);
+                    }
+                f1 = fast_exp2(csl - prev);
+                f2 = 1.f;
+            }
             frag xv[2][2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int v = 0; v < 2; ++v) xv[ks][v] = XC::get(Xs, l0 + 16 * ks, 32 * v, lane);
-            const float fr = fast_exp2(css[l0 + lr] - prev);
-            acc[0] *= fr;
-            acc[1] *= fr;
+                for (int v = 0; v < 2; ++v) xv[ks][v] = XC::get(xsrc, 16 * ks, 32 * v, lane);
+            acc[0] *= f1;
+            acc[1] *= f1;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int v = 0; v < 2; ++v) acc[v] = E::mma(acc[v], xv[ks][v], mk[ks]);
+                for (int v = 0; v < 2; ++v) acc[v] = E::mma(acc[v], xv[ks][v], dg[ks]);
+            acc[0] *= f2;
+            acc[1] *= f2;
+            // the next chunk's diagonal tile of this block travels while this one is used
+            if (c + 1 < nchunks) load_dg(c + 1, u);
             __bf16* ys = reinterpret_cast<__bf16*>(smem + L::ys) + (u * 4 + ok_) * 32 * L::ystride;
 #pragma unroll
             for (int v = 0; v < 2; ++v)
@@ -446,13 +499,11 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
         __syncthreads();
         for (int c = 0; c < nchunks; ++c) {
             const bool more = c + 1 < nchunks;
-            build_mask(c, 1);
             const float prev2 = left_and_chain(c, 1);
             diag(c, 1, prev2);
             const float prev1 = left_and_chain(c, 0);
             if (more) load_cb(c + 1);
             __syncthreads();   // B_mid: X~ and h of chunk c are no longer read
-            build_mask(c, 0);
             diag(c, 0, prev1);
             __syncthreads();   // B_end
         }

@@ -156,7 +156,7 @@ def test_bitwise_repeatable():
 
 # The common layer shapes (bf16, 256-row chunks, d_state 64 or 128, head dimension a
 # multiple of 64) run on their own walker; these cases reach its edges.
-@pytest.mark.parametrize("case", ["varlen", "strong_decay", "headdim128", "one_chunk_n64", "a_one"])
+@pytest.mark.parametrize("case", ["varlen", "strong_decay", "mixed_decay", "headdim128", "one_chunk_n64", "a_one"])
 def test_layer_shape_walker_edges(case):
     if case == "varlen":
         lens = [5, 0, 300, 1, 256, 257, 600, 33]
@@ -167,6 +167,15 @@ def test_layer_shape_walker_edges(case):
     elif case == "strong_decay":
         inp = make_inputs(1, 512, 2, 64, 128, 1, "bf16", seed=1001)
         inp.logA[:] = -1e4
+        check(inp, 256, case)
+    elif case == "mixed_decay":
+        # ordinary decay with a few 32-row blocks whose decay span is huge (rows of
+        # logA = -30 or -70), next to blocks where it is not, in every chunk
+        inp = make_inputs(2, 700, 3, 64, 128, 1, "bf16", seed=1005, init_state=True)
+        for t0 in (40, 300, 620):
+            inp.logA[:, t0:t0 + 4, :] = -30.0
+        inp.logA[:, 170, 1] = -70.0
+        inp.logA[1, 455, :] = -70.0
         check(inp, 256, case)
     elif case == "headdim128":
         inp = make_inputs(2, 520, 3, 128, 64, 1, "bf16", seed=1002, init_state=True)
