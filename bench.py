@@ -47,6 +47,13 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def walk_kernel_name(w):
+    """The walk kernel that the library's planner picks for this workload."""
+    if w.dtype == "bf16" and w.chunk_len == 256 and w.dstate in (64, 128) and w.headdim % 64 == 0:
+        return f"ssd_walk_split_kernel<{w.dstate}>"
+    return "ssd_walk_kernel"
+
+
 def algorithmic_bytes(w, es):
     """Minimum HBM traffic of one forward: read X, B, C, logA (+ init), write Y, final."""
     tokens = w.batch * w.seqlen
@@ -93,6 +100,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"])
     args = ap.parse_args()
 
@@ -174,6 +182,37 @@ def main():
     log(f"[bench] step {ms_step * 1e3:.1f} us; prep {stage_ms[1] * 1e3:.1f} us; "
         f"walk {stage_ms[2] * 1e3:.1f} us")
 
+    # the recurrent decode step (one token per sequence, state updated in place) at the
+    # same sequences, heads and sizes; HBM-bound on the float32 state
+    dec = None
+    if not args.no_decode:
+        g = torch.Generator(device="cpu").manual_seed(5)
+        H_, P_, N_, G_ = w.nheads, w.headdim, w.dstate, w.ngroups
+        xd = torch.randn(nseq, H_, P_, generator=g).to(dt).to(dev)
+        ld = (-torch.rand(nseq, H_, generator=g) * 0.5).to(dev)
+        Bd = (torch.randn(nseq, G_, N_, generator=g) / N_ ** 0.5).to(dt).to(dev)
+        Cd = (torch.randn(nseq, G_, N_, generator=g) / N_ ** 0.5).to(dt).to(dev)
+        Sd = torch.zeros(nseq, H_, P_, N_, dtype=torch.float32, device=dev)
+        yd = torch.empty_like(xd)
+        dprob = ssd.problem_for(nseq, 1, H_, P_, N_, G_, w.chunk_len, nseq, prob.dtype)
+        dptr = [xd.data_ptr(), ld.data_ptr(), Bd.data_ptr(), Cd.data_ptr(), Sd.data_ptr(), yd.data_ptr(), sp]
+        for _ in range(10):
+            assert ssd.ssd_decode_step(dprob, *dptr) == 0
+        torch.cuda.synchronize()
+        nd = 200
+        e0.record(stream)
+        for _ in range(nd):
+            ssd.ssd_decode_step(dprob, *dptr)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / nd
+        dbytes = 2 * nseq * H_ * P_ * N_ * 4 + 2 * nseq * H_ * P_ * es + 2 * nseq * G_ * N_ * es + nseq * H_ * 4
+        dec = {"kernel": "ssd_decode_kernel", "us_per_step": round(us, 2),
+               "tokens_per_s": round(nseq / (us * 1e-6), 1),
+               "bytes_per_step": dbytes, "achieved_gbs": round(dbytes / (us * 1e-6) / 1e9, 1),
+               "frac_hbm": round(dbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"[bench] decode step {us:.2f} us, {dec['achieved_gbs']} GB/s")
+
     lens = [w.seqlen] * w.batch if not w.varlen else list(np.diff(inp.seq_offsets))
     tokens = w.batch * w.seqlen
     fl = flops_pages(w, chunk_lengths(w, [int(v) for v in lens]))
@@ -209,7 +248,7 @@ def main():
         "mfma_util_pages": round(fl / (ms_step * 1e-3) / 1e12 / peak_mm, 4),
         "stage_us": {"prep": round(stage_ms[1] * 1e3, 2), "walk": round(stage_ms[2] * 1e3, 2)},
         "roofline": {
-            "kernel": "ssd_walk_kernel",
+            "kernel": walk_kernel_name(w),
             "bound": "hbm",
             "achieved": round(achieved_gbs, 1),
             "peak": HBM_PEAK_GBS,
@@ -219,6 +258,9 @@ def main():
             "algorithmic_bytes": abytes,
         },
     }
+
+    if dec is not None:
+        result["decode"] = dec
 
     if not args.no_cpu_baseline:
         import oracle

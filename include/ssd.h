@@ -125,6 +125,23 @@ int ssd_forward_stage(int stage, const ssd_problem* p, const void* X, const floa
                       const int32_t* seq_offsets, void* Y, float* final_state, void* workspace,
                       size_t workspace_bytes, void* hip_stream);
 
+/* One recurrent (decode) step for every sequence and head: the recurrence above for a
+ * single token, continuing from a state a forward pass (final_state) or an earlier step
+ * left (page section 2.4; the recurrent mode of section 3: constant memory and work per
+ * token).  For each sequence s and head h with group g = h / (H/G):
+ *     a = exp(logA[s, h]);  state[s, h] <- a state[s, h] + x[s, h] B[s, g]^T;
+ *     y[s, h] = state[s, h] C[s, g]                 (after the update)
+ * Problem: p->seqlen must be 1 and p->nseq == p->batch (one row per sequence);
+ * headdim and dstate as for ssd_forward; chunk_len is not used.  Arguments (device):
+ *   x      [b, H, P]     dtype          logA [b, H] float32
+ *   B, C   [b, G, N]     dtype
+ *   state  [b, H, P, N]  float32        read and overwritten in place
+ *   y      [b, H, P]     dtype (out)    rounded to dtype (round to nearest even)
+ * y and state must not overlap the inputs or each other.  No workspace.
+ * Returns SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED or SSD_ERR_HIP. */
+int ssd_decode_step(const ssd_problem* p, const void* x, const float* logA, const void* B,
+                    const void* C, float* state, void* y, void* hip_stream);
+
 /* Static English text for a status code (never NULL). */
 const char* ssd_status_string(int status);
 

@@ -5,6 +5,7 @@ marshals arguments: every step of the computation runs in the library's HIP kern
 the caller's current HIP stream.  PyTorch supplies device memory and the stream.
 
     Y, final_state = forward(X, logA, B, C, chunk_len, init_state=None, seq_offsets=None)
+    y = decode_step(x, logA, B, C, state)      # one recurrent step, state updated in place
 
 Shapes (row-major): X [b, T, H, P] (float32 or bfloat16); logA [b, T, H] float32;
 B, C [b, T, G, N] (same dtype as X); init_state [nseq, H, P, N] float32 or None;
@@ -23,8 +24,8 @@ __all__ = [
     "SSD_OK", "SSD_ERR_INVALID_ARG", "SSD_ERR_UNSUPPORTED", "SSD_ERR_WORKSPACE", "SSD_ERR_HIP",
     "SSD_DTYPE_F32", "SSD_DTYPE_BF16", "SsdProblem", "SsdError", "lib_path", "load_library",
     "ssd_check_problem", "ssd_workspace_bytes", "ssd_forward", "ssd_forward_stage",
-    "ssd_status_string",
-    "ssd_abi_version", "forward", "problem_for",
+    "ssd_decode_step", "ssd_status_string",
+    "ssd_abi_version", "forward", "decode_step", "problem_for",
 ]
 
 SSD_OK = 0
@@ -79,6 +80,8 @@ def load_library():
     lib.ssd_forward.restype = ctypes.c_int
     lib.ssd_forward_stage.argtypes = [ctypes.c_int, pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ssd_forward_stage.restype = ctypes.c_int
+    lib.ssd_decode_step.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ssd_decode_step.restype = ctypes.c_int
     lib.ssd_status_string.argtypes = [ctypes.c_int]
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_abi_version.argtypes = []
@@ -120,6 +123,12 @@ def ssd_forward_stage(stage: int, problem: SsdProblem, X, logA, B, C, init_state
     return int(load_library().ssd_forward_stage(int(stage), ctypes.byref(problem), X, logA, B, C,
                                                 init_state, seq_offsets, Y, final_state,
                                                 workspace, int(workspace_bytes), hip_stream))
+
+
+def ssd_decode_step(problem: SsdProblem, x, logA, B, C, state, y, hip_stream) -> int:
+    """Direct call of ssd_decode_step (device addresses as integers); returns the status."""
+    return int(load_library().ssd_decode_step(ctypes.byref(problem), x, logA, B, C, state, y,
+                                              hip_stream))
 
 
 def problem_for(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len, nseq, dtype) -> SsdProblem:
@@ -177,3 +186,38 @@ def forward(X, logA, B, C, chunk_len: int, init_state=None, seq_offsets=None,
     if rc != SSD_OK:
         raise SsdError(rc)
     return Y, final
+
+
+def decode_step(x, logA, B, C, state, y=None):
+    """One recurrent step on the current HIP stream: for every sequence s and head h,
+    state[s, h] <- exp(logA[s, h]) state[s, h] + x[s, h] B[s, g]^T and
+    y[s, h] = state[s, h] C[s, g].  x [b, H, P], logA [b, H] float32, B/C [b, G, N],
+    state [b, H, P, N] float32 (updated in place).  Returns y [b, H, P] (x's dtype)."""
+    import torch
+
+    if x.dtype == torch.bfloat16:
+        dt = SSD_DTYPE_BF16
+    elif x.dtype == torch.float32:
+        dt = SSD_DTYPE_F32
+    else:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    if x.dim() != 3 or logA.dim() != 2 or B.dim() != 3 or C.dim() != 3 or state.dim() != 4:
+        raise ValueError("expected x [b,H,P], logA [b,H], B/C [b,G,N], state [b,H,P,N]")
+    b, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    if (tuple(logA.shape) != (b, H) or tuple(B.shape) != (b, G, N) or tuple(C.shape) != (b, G, N)
+            or tuple(state.shape) != (b, H, P, N)):
+        raise ValueError("shape mismatch between x, logA, B, C and state")
+    if B.dtype != x.dtype or C.dtype != x.dtype or logA.dtype != torch.float32 or state.dtype != torch.float32:
+        raise TypeError("B and C must share x's dtype; logA and state must be float32")
+    if not state.is_contiguous():
+        raise ValueError("state must be contiguous (it is updated in place)")
+    x, logA, B, C = x.contiguous(), logA.contiguous(), B.contiguous(), C.contiguous()
+    if y is None:
+        y = torch.empty_like(x)
+    prob = problem_for(b, 1, H, P, N, G, 16, b, dt)
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    rc = ssd_decode_step(prob, _ptr(x), _ptr(logA), _ptr(B), _ptr(C), _ptr(state), _ptr(y), stream)
+    if rc != SSD_OK:
+        raise SsdError(rc, "ssd_decode_step")
+    return y

@@ -347,6 +347,51 @@ int ssd_forward(const ssd_problem* p, const void* X, const float* logA, const vo
                        workspace_bytes, hip_stream);
 }
 
+int ssd_decode_step(const ssd_problem* p, const void* x, const float* logA, const void* B,
+                    const void* C, float* state, void* y, void* hip_stream) {
+    if (!p) return SSD_ERR_INVALID_ARG;
+    if (p->batch < 1 || p->seqlen != 1 || p->nheads < 1 || p->headdim < 1 || p->dstate < 1 ||
+        p->ngroups < 1 || p->nseq != p->batch || p->reserved != 0)
+        return SSD_ERR_INVALID_ARG;
+    if (p->nheads % p->ngroups != 0) return SSD_ERR_INVALID_ARG;
+    if (p->dtype != SSD_DTYPE_F32 && p->dtype != SSD_DTYPE_BF16) return SSD_ERR_UNSUPPORTED;
+    if (p->headdim % 16 != 0 || p->headdim > 256 || p->dstate % 16 != 0 || p->dstate > 256)
+        return SSD_ERR_UNSUPPORTED;
+    if (p->batch * p->nheads > INT32_MAX) return SSD_ERR_UNSUPPORTED;
+    if (!x || !logA || !B || !C || !state || !y) return SSD_ERR_INVALID_ARG;
+    const void* ptrs[] = {x, logA, B, C, state, y};
+    for (const void* q : ptrs)
+        if (!aligned16(q)) return SSD_ERR_INVALID_ARG;
+    const size_t es = p->dtype == SSD_DTYPE_BF16 ? 2 : 4;
+    const int64_t b = p->batch, H = p->nheads, P = p->headdim, N = p->dstate, G = p->ngroups;
+    const size_t nx = (size_t)(b * H * P) * es, na = (size_t)(b * H) * 4, nbc = (size_t)(b * G * N) * es;
+    const size_t ns = (size_t)(b * H * P * N) * 4;
+    // y and the state are written: neither may overlap an input or the other
+    const void* ins[] = {x, logA, B, C};
+    const size_t nin[] = {nx, na, nbc, nbc};
+    for (int i = 0; i < 4; ++i)
+        if (overlap(y, nx, ins[i], nin[i]) || overlap(state, ns, ins[i], nin[i])) return SSD_ERR_INVALID_ARG;
+    if (overlap(y, nx, state, ns)) return SSD_ERR_INVALID_ARG;
+    ssd::DecodeArgs da;
+    da.x = x;
+    da.logA = logA;
+    da.B = B;
+    da.C = C;
+    da.state = state;
+    da.y = y;
+    da.H = (int)H;
+    da.P = (int)P;
+    da.N = (int)N;
+    da.G = (int)G;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (p->dtype == SSD_DTYPE_BF16)
+        hipLaunchKernelGGL(ssd::ssd_decode_kernel<__bf16>, dim3((unsigned)(b * H)), dim3(256), 0, stream, da);
+    else
+        hipLaunchKernelGGL(ssd::ssd_decode_kernel<float>, dim3((unsigned)(b * H)), dim3(256), 0, stream, da);
+    if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
 int ssd_forward_stage(int stage, const ssd_problem* p, const void* X, const float* logA,
                       const void* B, const void* C, const float* init_state,
                       const int32_t* seq_offsets, void* Y, float* final_state, void* workspace,

@@ -70,6 +70,16 @@ struct WalkArgs {
     int xs_off, xts_off, bs_off, hs_off, cs_off;   // LDS byte offsets
 };
 
+struct DecodeArgs {
+    const void* x;       // [b, H, P]   input dtype
+    const float* logA;   // [b, H]
+    const void* B;       // [b, G, N]   input dtype
+    const void* C;       // [b, G, N]   input dtype
+    float* state;        // [b, H, P, N] float32, updated in place
+    void* y;             // [b, H, P]   input dtype
+    int H, P, N, G;
+};
+
 // Consecutive workgroup ids are dispatched round-robin over the 8 XCDs.  Give each
 // XCD a contiguous range of work items, so the heads of one sequence (which share
 // B, C and C B^T) meet in the same L2.
@@ -264,6 +274,49 @@ __global__ void __launch_bounds__(256) ssd_prep_kernel(PrepArgs a) {
         // rows s = 8q + 4lg + 0..3 of this lane's column l = lr
         T* o = out + (((q >> 1) * 64 + (q & 1) * 32 + lr) * 8 + 4 * lg);
         E::st4(o, acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+    }
+}
+
+// One recurrent step of every (sequence, head): h <- a h + x B^T, y = h C (page "Transformers
+// are SSMs" paper summary, section 2.4 with A_t = a_t I; the recurrent mode of section 3,
+// one token at a time from a state the forward pass returned).  One 256-thread workgroup
+// per (sequence, head) streams the P x N state once: each thread owns 4 consecutive
+// state entries of a row per pass, the N/4 threads of a row reduce y[p] with lane
+// shuffles.  The state goes from HBM to registers and back, nothing is staged.
+template <typename T>
+__global__ void __launch_bounds__(256) ssd_decode_kernel(DecodeArgs a) {
+    using E = Elem<T>;
+    const int bh = blockIdx.x;
+    const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
+    const int tid = threadIdx.x;
+    const int tpr = a.N / 4;                 // threads per state row (4 .. 64)
+    const int rpp = 256 / tpr;               // rows per pass
+    const int j = tid % tpr, rsub = tid / tpr;
+    const T* Bv = static_cast<const T*>(a.B) + ((int64_t)b * a.G + g) * a.N + 4 * j;
+    const T* Cv = static_cast<const T*>(a.C) + ((int64_t)b * a.G + g) * a.N + 4 * j;
+    const float b0 = E::to_f(Bv[0]), b1 = E::to_f(Bv[1]), b2 = E::to_f(Bv[2]), b3 = E::to_f(Bv[3]);
+    const float c0 = E::to_f(Cv[0]), c1 = E::to_f(Cv[1]), c2 = E::to_f(Cv[2]), c3 = E::to_f(Cv[3]);
+    const float da = fast_exp2(a.logA[(int64_t)b * a.H + h] * kLog2e);
+    const T* xv = static_cast<const T*>(a.x) + ((int64_t)b * a.H + h) * a.P;
+    T* yv = static_cast<T*>(a.y) + ((int64_t)b * a.H + h) * a.P;
+    float* st = a.state + ((int64_t)b * a.H + h) * a.P * (int64_t)a.N;
+    for (int p0 = 0; p0 < a.P; p0 += rpp) {
+        const int p = p0 + rsub;
+        float part = 0.f;
+        if (p < a.P) {
+            f32x4* s4 = reinterpret_cast<f32x4*>(st + (int64_t)p * a.N + 4 * j);
+            const float xp = E::to_f(xv[p]);
+            f32x4 v = *s4;
+            v[0] = da * v[0] + xp * b0;
+            v[1] = da * v[1] + xp * b1;
+            v[2] = da * v[2] + xp * b2;
+            v[3] = da * v[3] + xp * b3;
+            *s4 = v;
+            part = v[0] * c0 + v[1] * c1 + v[2] * c2 + v[3] * c3;
+        }
+        // sum over the tpr threads of the row (consecutive lanes of one wavefront)
+        for (int d = tpr >> 1; d > 0; d >>= 1) part += __shfl_xor(part, d, 64);
+        if (p < a.P && j == 0) yv[p] = E::from_f(part);
     }
 }
 

@@ -16,6 +16,8 @@ What is computed (page: "Transformers are SSMs" paper summary):
 * ``chunked`` -- the block decomposition of section 6 (6.1 diagonal blocks,
   6.2 right / center / left factors of the low-rank blocks), for any chunk
   length, ragged last chunk included.
+* ``decode_step`` -- one step of the recurrence for a single token per sequence
+  (the recurrent mode of section 3), continuing from a given state.
 
 Readings of the pages that these functions take:
 A is the log decay (logA <= 0, a_t = exp(logA_t), -inf allowed, giving a = 0);
@@ -241,3 +243,23 @@ def chunked(X, logA, B, C, chunk_len: int, init=None, seq_offsets=None):
                 y_off = decay_in[k][:, None] * (cc @ entry[k].T)
                 Y[c0:c1, h] = y_diag[k] + y_off
     return Y.reshape(b, T, H, P), final
+
+
+def decode_step(state, x, logA, B, C):
+    """One token of the recurrence for every sequence and head, from ``state``
+    (section 2.4 with A_t = a_t I; the recurrent mode of section 3):
+    S <- a S + x B^T, y = S C with a = exp(logA), S of head h using group h // (H // G).
+    Shapes: state [b, H, P, N]; x [b, H, P]; logA [b, H]; B, C [b, G, N].
+    Returns (y [b, H, P], new state [b, H, P, N]), float64; ``state`` is not modified."""
+    S = _f64(state).copy()
+    x, logA, B, C = _f64(x), _f64(logA), _f64(B), _f64(C)
+    b, H, P, N = S.shape
+    G = B.shape[1]
+    hpg = H // G
+    y = np.empty((b, H, P))
+    for s in range(b):
+        for h in range(H):
+            g = h // hpg
+            S[s, h] = np.exp(logA[s, h]) * S[s, h] + np.outer(x[s, h], B[s, g])
+            y[s, h] = S[s, h] @ C[s, g]
+    return y, S

@@ -23,8 +23,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["ssd_abi_version", "ssd_check_problem", "ssd_forward",
-                                           "ssd_forward_stage", "ssd_status_string",
+    assert declared_functions() == sorted(["ssd_abi_version", "ssd_check_problem", "ssd_decode_step",
+                                           "ssd_forward", "ssd_forward_stage", "ssd_status_string",
                                            "ssd_workspace_bytes"])
 
 
@@ -152,3 +152,44 @@ def test_forward_stage_validates_like_forward(stage):
     assert ssd.ssd_forward_stage(stage, p, a["X"] + 4, a["logA"], a["B"], a["C"], a["init"], None,
                                  a["Y"], a["final"], a["ws"], ssd.ssd_workspace_bytes(p),
                                  None) == ssd.SSD_ERR_INVALID_ARG
+
+
+# ssd_decode_step: the same fake-address discipline (validation fails before any launch).
+DADDR = dict(x=1 * GB, logA=2 * GB, B=3 * GB, C=4 * GB, state=5 * GB, y=6 * GB)
+
+
+def dprob(**kw):
+    d = dict(batch=3, seqlen=1, nheads=4, headdim=64, dstate=128, ngroups=2, chunk_len=16,
+             nseq=3, dtype=ssd.SSD_DTYPE_BF16)
+    d.update(kw)
+    return ssd.problem_for(**d)
+
+
+def dcall(p, **over):
+    a = dict(DADDR)
+    a.update(over)
+    return ssd.ssd_decode_step(p, a["x"], a["logA"], a["B"], a["C"], a["state"], a["y"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(seqlen=2), ssd.SSD_ERR_INVALID_ARG),
+    (dict(nseq=2), ssd.SSD_ERR_INVALID_ARG),
+    (dict(nheads=3), ssd.SSD_ERR_INVALID_ARG),
+    (dict(batch=0, nseq=0), ssd.SSD_ERR_INVALID_ARG),
+    (dict(dtype=5), ssd.SSD_ERR_UNSUPPORTED),
+    (dict(headdim=40), ssd.SSD_ERR_UNSUPPORTED),
+    (dict(dstate=512), ssd.SSD_ERR_UNSUPPORTED),
+])
+def test_decode_rejects_invalid_problem(kw, code):
+    assert dcall(dprob(**kw)) == code
+
+
+@pytest.mark.parametrize("name", list(DADDR))
+def test_decode_rejects_null_and_misaligned_pointers(name):
+    assert dcall(dprob(), **{name: None}) == ssd.SSD_ERR_INVALID_ARG
+    assert dcall(dprob(), **{name: DADDR[name] + 8}) == ssd.SSD_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("out,inp", [("y", "x"), ("state", "B"), ("state", "y")])
+def test_decode_rejects_aliased_outputs(out, inp):
+    assert dcall(dprob(), **{out: DADDR[inp]}) == ssd.SSD_ERR_INVALID_ARG

@@ -278,3 +278,46 @@ def test_inputs_reproducible_and_head_subset():
     np.testing.assert_array_equal(a.init[:, [1, 4]], b.init)
     np.testing.assert_array_equal(bf16_round(a.X), a.X)
     assert np.all(a.logA < 0) and np.all(np.exp(a.logA) > 0.19)
+
+
+# --------------------------------------------------------------------------- decode step
+
+def test_decode_step_worked_p2_n3():
+    """The hand-worked P=2, N=3 head, stepped one token at a time from a zero state."""
+    g = {r[0]: [float(v) for v in r[1:]] for r in _golden_lines("ssd_p2_n3_worked.txt")}
+    S = np.zeros((1, 1, 2, 3))
+    for t in range(2):
+        y, S = oracle.decode_step(S, np.array(g[f"x{t}"]).reshape(1, 1, 2),
+                                  np.log(np.array([[g["a"][t]]])),
+                                  np.array(g[f"B{t}"]).reshape(1, 1, 3), np.array(g[f"C{t}"]).reshape(1, 1, 3))
+        np.testing.assert_allclose(y.reshape(-1), g[f"y{t}"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(S.reshape(-1), g["final"], rtol=0, atol=1e-14)
+
+
+def test_decode_step_closed_forms():
+    """a = 1: S' = S + x B^T; a = 0 (logA = -inf): S' = x B^T, y = (B . C) x."""
+    rng = np.random.default_rng(7)
+    S0 = rng.standard_normal((2, 3, 4, 5))
+    x = rng.standard_normal((2, 3, 4))
+    B = rng.standard_normal((2, 1, 5))
+    C = rng.standard_normal((2, 1, 5))
+    y, S = oracle.decode_step(S0, x, np.zeros((2, 3)), B, C)
+    want = S0 + x[..., None] * B[:, :, None, :]
+    np.testing.assert_allclose(S, want, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(y, np.einsum("bhpn,bn->bhp", want, C[:, 0]), rtol=1e-13, atol=1e-13)
+    y, S = oracle.decode_step(S0, x, np.full((2, 3), -np.inf), B, C)
+    np.testing.assert_allclose(S, x[..., None] * B[:, :, None, :], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(y, np.sum(B * C, axis=-1)[:, :, None] * x, rtol=1e-13, atol=1e-13)
+
+
+def test_decode_steps_continue_the_forward_pass():
+    """Forward over T tokens, then k decode steps == forward over T + k tokens (the
+    recurrent mode resumes exactly where the forward pass's final state stops)."""
+    X, logA, B, C, I = rand_problem(31, b=2, T=20, H=4, P=6, N=5, G=2)
+    T0 = 14
+    Y_all, F_all = oracle.recurrence(X, logA, B, C, I)
+    _, S = oracle.recurrence(X[:, :T0], logA[:, :T0], B[:, :T0], C[:, :T0], I)
+    for t in range(T0, 20):
+        y, S = oracle.decode_step(S, X[:, t], logA[:, t], B[:, t], C[:, t])
+        np.testing.assert_allclose(y, Y_all[:, t], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S, F_all, rtol=1e-12, atol=1e-12)
