@@ -15,6 +15,7 @@ namespace {
 constexpr int kLdsMax = 160 * 1024;   // LDS per workgroup on gfx950
 constexpr int kWalkThreads = 512;
 constexpr int kPrepThreads = 256;
+constexpr int kComputeUnits = 256;     // MI355X: 8 XCDs x 32 CUs
 
 typedef void (*walk_fn_t)(ssd::WalkArgs);
 
@@ -26,7 +27,10 @@ struct Plan {
     size_t cs_off, cb_off, bt_off, ct_off, ws_bytes;
     int lds_bytes, xs_off, xts_off, bs_off, hs_off, cs_lds_off;
     int split;        // the split-role walker (bf16, 256-row chunks, d_state 64 / 128)
+    int nseg;         // segments per sequence of a batch without seq_offsets
+    size_t seg_off, segd_off;
     walk_fn_t walk;   // the walk kernel instance for this plan
+    walk_fn_t summary;   // the segment-summary instance (nseg > 1)
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -108,6 +112,7 @@ int make_plan(const ssd_problem* p, Plan* pl) {
     const int rc = check_problem(p);
     if (rc != SSD_OK) return rc;
     pl->dtype = p->dtype;
+    pl->summary = nullptr;
     const int es = p->dtype == SSD_DTYPE_BF16 ? 2 : 4;
     pl->Q = (int)p->chunk_len;
     pl->Qp = (pl->Q + 31) / 32 * 32;
@@ -136,7 +141,20 @@ int make_plan(const ssd_problem* p, Plan* pl) {
     pl->split = p->dtype == SSD_DTYPE_BF16 && pl->Q == 256 && (N == 64 || N == 128) && P % 64 == 0;
     const size_t bt_bytes = pl->split ? (size_t)pl->nslots * p->ngroups * ssd::split_bt_bytes(N) : 0;
     pl->ct_off = align_up(pl->bt_off + bt_bytes, 256);
-    pl->ws_bytes = align_up(pl->ct_off + bt_bytes, 256);   // C fragments: as many bytes as B^T
+    pl->seg_off = align_up(pl->ct_off + bt_bytes, 256);   // C fragments: as many bytes as B^T
+    // Segmented walk: when the (sequence, head, P tile) items of a batch cannot fill the
+    // 256 compute units of the part, each sequence is walked as nseg segments of at
+    // least 4 chunks, after a pass that sums up every segment but the last.
+    pl->nseg = 1;
+    if (pl->split) {
+        const int64_t items = p->nseq * p->nheads * (P / 64);
+        int64_t k = kComputeUnits / items;
+        if (k > nc / 4) k = nc / 4;
+        if (k > 1) pl->nseg = (int)k;
+    }
+    const size_t seg_bytes = (size_t)p->nseq * (pl->nseg - 1) * p->nheads * P * N * sizeof(float);
+    pl->segd_off = align_up(pl->seg_off + seg_bytes, 256);
+    pl->ws_bytes = align_up(pl->segd_off + (size_t)p->nseq * (pl->nseg - 1) * p->nheads * sizeof(float), 256);
     // stage the off-diagonal C B^T tiles in LDS when they fit next to a whole chunk of B
     // (or the largest B stage that fits), else read them from global memory
     pl->cb_lds = p->dtype == SSD_DTYPE_BF16 ? 1 : 0;
@@ -158,10 +176,12 @@ int make_plan(const ssd_problem* p, Plan* pl) {
         pl->qb = pl->Qp;
         pl->cb_lds = 0;
         if (N == 64) {
-            pl->walk = ssd::ssd_walk_split_kernel<64>;
+            pl->walk = ssd::ssd_walk_split_kernel<64, false>;
+            pl->summary = ssd::ssd_walk_split_kernel<64, true>;
             pl->lds_bytes = ssd::SplitLds<64>::bytes;
         } else {
-            pl->walk = ssd::ssd_walk_split_kernel<128>;
+            pl->walk = ssd::ssd_walk_split_kernel<128, false>;
+            pl->summary = ssd::ssd_walk_split_kernel<128, true>;
             pl->lds_bytes = ssd::SplitLds<128>::bytes;
         }
     }
@@ -265,6 +285,12 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
                                               : ssd::ssd_prep_kernel<float>;
     rc = ensure_lds_limit(reinterpret_cast<const void*>(walk));
     if (rc != SSD_OK) return rc;
+    // packed sequences are walked whole
+    const int nseg = seq_offsets ? 1 : pl.nseg;
+    if (nseg > 1) {
+        rc = ensure_lds_limit(reinterpret_cast<const void*>(pl.summary));
+        if (rc != SSD_OK) return rc;
+    }
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     unsigned char* ws = static_cast<unsigned char*>(workspace);
@@ -330,8 +356,16 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
     wa.bs_off = pl.bs_off;
     wa.hs_off = pl.hs_off;
     wa.cs_off = pl.cs_lds_off;
+    wa.nseg = nseg;
+    wa.seg_state = reinterpret_cast<float*>(ws + pl.seg_off);
+    wa.seg_decay = reinterpret_cast<float*>(ws + pl.segd_off);
+    if ((stages & 2) && nseg > 1) {
+        wa.nitems = (int)(pl.nitems * (nseg - 1));
+        hipLaunchKernelGGL(pl.summary, dim3((unsigned)wa.nitems), dim3(kWalkThreads / 2), pl.lds_bytes, stream, wa);
+    }
+    wa.nitems = (int)(pl.nitems * nseg);
     if (stages & 2)
-        hipLaunchKernelGGL(walk, dim3((unsigned)pl.nitems), dim3(kWalkThreads), pl.lds_bytes, stream, wa);
+        hipLaunchKernelGGL(walk, dim3((unsigned)wa.nitems), dim3(kWalkThreads), pl.lds_bytes, stream, wa);
     if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
     return SSD_OK;
 }

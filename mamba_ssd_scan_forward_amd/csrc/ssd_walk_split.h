@@ -17,16 +17,15 @@
 //   reloaded for the next chunk as soon as it has been consumed.  Only per-head data
 //   is staged in LDS: X, X~ and the cumsum of the chunk, and h at its start.
 //
-//   The state waves also stage the next chunk (X, X~, cumsum) and h_{c+1}.  Raw X
-//   and the cumsum are double-buffered, X~ and h are not, which gives two barriers
-//   per chunk:
+//   The state waves also stage the next chunk (X~ and the cumsum) and h_{c+1}.  X~
+//   and the cumsum are double-buffered, h is not, which gives two barriers per chunk:
 //     state waves : state(c)                          | B_mid | store Y of block i2,
-//                                                      |       | write h, X~, X, cs of c+1
+//                                                      |       | write h, X~ of c+1
 //     output waves: block i2 whole, block i1 up to its | B_mid | block i1's diagonal
 //                   chain                              |       |
-//     then B_end, after which the state waves store Y of block i1.  (X~ and h of chunk
-//   c are last read before B_mid; raw X and the cumsum of chunk c may be read after it:
-//   the state waves write the other buffer.)  Output tiles go through LDS, where the
+//     then B_end, after which the state waves store Y of block i1.  (h of chunk c is
+//   last read before B_mid; X~ and the cumsum of chunk c may be read after it: the
+//   state waves write the other buffer.)  Output tiles go through LDS, where the
 //   state waves, which have time to spare, pick them up and write whole 128-byte rows
 //   of Y (a lane of an output wave holds 16 of a row's values in 4-value pieces).
 //
@@ -62,7 +61,18 @@ template <int NP> struct SplitLds {
 // Bytes of B^T fragments per (chunk slot, group) in the workspace.
 __host__ __device__ constexpr int split_bt_bytes(int N) { return N * 512; }
 
-template <int NP>
+// A long sequence may be walked as nseg segments of consecutive chunks, one workgroup
+// per (sequence, segment, head, P tile), so that few sequences still fill the chip.
+// This is the chunk recurrence h_{c+1} = a_c h_c + S_c taken two levels deep, as in a
+// scan over an associative operator on pairs (a, S):
+//   SUMMARY = true : for every segment k but the last, the state waves alone walk its
+//                    chunks from a zero state and store that state and the segment's
+//                    total log2 decay (256 threads per workgroup);
+//   SUMMARY = false: segment k starts from E_k, with E_0 the initial state (or zero) and
+//                    E_{k+1} = 2^(decay_k) E_k + state_k, folded in the prologue, and
+//                    walks its chunks in full.  Only the last segment writes the final
+//                    state.
+template <int NP, bool SUMMARY>
 __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
     typedef Elem<__bf16> E;
     typedef bf16x8 frag;
@@ -82,9 +92,13 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int item = xcd_remap(blockIdx.x, gridDim.x);
     if (item >= a.nitems) return;
+    // item = ((s * nseg' + segment) * H + h) * ptiles + pt, nseg' = nseg - 1 for the
+    // summaries: the heads of one segment sit next to each other (one XCD, one L2)
     const int pt = item % a.ptiles;
-    const int sh = item / a.ptiles;
-    const int h = sh % a.H, s = sh / a.H;
+    const int sk = item / a.ptiles / a.H;
+    const int h = item / a.ptiles % a.H;
+    const int nsk = SUMMARY ? a.nseg - 1 : a.nseg;
+    const int s = sk / nsk, seg = sk % nsk;
     const int g = h / (a.H / a.G);
     const int p_base = pt * 64;
     const int H = a.H, P = a.P, N = a.N, G = a.G;
@@ -100,6 +114,15 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
         len_seq = a.seq_offsets[s + 1] - a.seq_offsets[s];
         slot0 = 0;
         for (int u = 0; u < s; ++u) slot0 += (a.seq_offsets[u + 1] - a.seq_offsets[u] + 255) / 256;
+    }
+    if (a.nseg > 1) {
+        // segments of a batch without seq_offsets: chunks [c0, c1) of sequence s; every
+        // segment but the last holds whole chunks only
+        const int nc = (len_seq + 255) / 256;
+        const int c0 = (int)((int64_t)seg * nc / a.nseg), c1 = (int)((int64_t)(seg + 1) * nc / a.nseg);
+        row0 += (int64_t)c0 * 256;
+        slot0 += c0;
+        len_seq = min(len_seq, c1 * 256) - c0 * 256;
     }
     const int nchunks = (len_seq + 255) / 256;
 
@@ -259,20 +282,71 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
             }
         };
 
+        // the state tiles of this wave from / to a [P][N] float32 state at `base`
+        auto add_state = [&](const float* base, float f) {
 #pragma unroll
-        for (int u = 0; u < TPS; ++u) {
-            hacc[u] = f32x16{};
-            if (!a.init) continue;
-            const int n0 = tile_n0(u), p = p_base + tile_p0(u) + lr;
+            for (int u = 0; u < TPS; ++u) {
+                const int n0 = tile_n0(u), p = p_base + tile_p0(u) + lr;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x4 v = *reinterpret_cast<const f32x4*>(a.init + state_base + (int64_t)p * N + n0 + 8 * q + 4 * lg);
-                hacc[u][4 * q] = v[0];
-                hacc[u][4 * q + 1] = v[1];
-                hacc[u][4 * q + 2] = v[2];
-                hacc[u][4 * q + 3] = v[3];
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(base + (int64_t)p * N + n0 + 8 * q + 4 * lg);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) hacc[u][4 * q + e] = hacc[u][4 * q + e] * f + v[e];
+                }
             }
+        };
+        auto put_state = [&](float* base) {
+#pragma unroll
+            for (int u = 0; u < TPS; ++u) {
+                const int n0 = tile_n0(u), p = p_base + tile_p0(u) + lr;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 v = {hacc[u][4 * q], hacc[u][4 * q + 1], hacc[u][4 * q + 2], hacc[u][4 * q + 3]};
+                    *reinterpret_cast<f32x4*>(base + (int64_t)p * N + n0 + 8 * q + 4 * lg) = v;
+                }
+            }
+        };
+        const int64_t pn = (int64_t)P * N;
+        auto summary_at = [&](int k) { return ((int64_t)s * (a.nseg - 1) + k) * H + h; };
+#pragma unroll
+        for (int u = 0; u < TPS; ++u) hacc[u] = f32x16{};
+
+        if constexpr (SUMMARY) {
+            // ---------------------------------------------- segment summary (state only)
+            // one barrier per chunk: X~ is double-buffered and written right after it
+            // has been scaled, and nothing else is shared
+            float dsum = 0.f;
+            if (nchunks > 0) {
+                load_bt(0);
+                prefetch_x(0);
+                dma_cs(0);
+                scale_x();
+                commit_x(0);
+            }
+            __syncthreads();
+            for (int c = 0; c < nchunks; ++c) {
+                const bool more = c + 1 < nchunks;
+                if (more) prefetch_x(c + 1);
+                state_chunk(c);
+                dsum += cs_buf(c)[255];
+                if (more) {
+                    dma_cs(c + 1);
+                    load_bt(c + 1);
+                    scale_x();
+                    commit_x(c + 1);
+                }
+                __syncthreads();
+            }
+            put_state(a.seg_state + summary_at(seg) * pn);
+            if (sw == 0 && pt == 0 && lane == 0) a.seg_decay[summary_at(seg)] = dsum;
+            return;
         }
+
+        // the entry state of this segment
+        if (a.init) add_state(a.init + state_base, 0.f);
+        for (int k = 0; k < seg; ++k)
+            add_state(a.seg_state + summary_at(k) * pn, fast_exp2(a.seg_decay[summary_at(k)]));
+
         if (nchunks > 0) {
             load_bt(0);
             prefetch_x(0);
@@ -304,18 +378,8 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
             __syncthreads();   // B_end
         }
         if (nchunks > 0) store_y(nchunks - 1, 0);
-        if (a.final_state) {
-#pragma unroll
-            for (int u = 0; u < TPS; ++u) {
-                const int n0 = tile_n0(u), p = p_base + tile_p0(u) + lr;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x4 v = {hacc[u][4 * q], hacc[u][4 * q + 1], hacc[u][4 * q + 2], hacc[u][4 * q + 3]};
-                    *reinterpret_cast<f32x4*>(a.final_state + state_base + (int64_t)p * N + n0 + 8 * q + 4 * lg) = v;
-                }
-            }
-        }
-    } else {
+        if (a.final_state && seg == a.nseg - 1) put_state(a.final_state + state_base);
+    } else if constexpr (!SUMMARY) {
         // ========================================================== output waves
         // The two blocks are done one after the other, the later one (longer chain)
         // first; only the second block's diagonal and store come after B_mid.  The code

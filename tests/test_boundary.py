@@ -193,3 +193,4 @@ def test_decode_rejects_null_and_misaligned_pointers(name):
 @pytest.mark.parametrize("out,inp", [("y", "x"), ("state", "B"), ("state", "y")])
 def test_decode_rejects_aliased_outputs(out, inp):
     assert dcall(dprob(), **{out: DADDR[inp]}) == ssd.SSD_ERR_INVALID_ARG
+

@@ -189,6 +189,40 @@ def test_layer_shape_walker_edges(case):
         check(inp, 256, case)
 
 
+# Few long sequences: each is walked as several segments of chunks (a first pass sums
+# up every segment but the last; each segment then starts from the combined state).
+# The plan picks the segment count from the number of (sequence, head, P tile) items and
+# chunks: 2 here for 8 items and 9 chunks, 3 for 4 items and 12 chunks.
+@pytest.mark.parametrize("case", ["two_segments", "three_segments_mixed", "a_one", "strong_decay"])
+def test_segmented_walk(case):
+    if case == "two_segments":
+        inp = make_inputs(2, 2100, 4, 64, 128, 2, "bf16", seed=1200, init_state=True)
+    elif case == "three_segments_mixed":
+        inp = make_inputs(1, 3000, 2, 128, 64, 1, "bf16", seed=1201, init_state=True)
+        for t0 in (100, 1030, 2300):
+            inp.logA[:, t0:t0 + 3, :] = -30.0
+        inp.logA[0, 1800, 1] = -70.0
+    elif case == "a_one":
+        inp = make_inputs(1, 2048, 2, 64, 128, 1, "bf16", seed=1202, init_state=True)
+        inp.logA[:] = 0.0
+    else:
+        inp = make_inputs(1, 2048, 2, 64, 64, 1, "bf16", seed=1203, init_state=True)
+        inp.logA[:] = -1e4
+    check(inp, 256, "segmented " + case)
+
+
+def test_segmented_walk_matches_whole_walk():
+    """The same sequence as a batch of one (segmented) and as one packed sequence
+    (walked whole): both within the bar of each other."""
+    import copy
+    inp = make_inputs(1, 2600, 4, 64, 128, 1, "bf16", seed=1210, init_state=True)
+    Y1, F1 = run_gpu(inp, 256)
+    packed = copy.deepcopy(inp)
+    packed.seq_offsets = np.array([0, 2600], dtype=np.int32)
+    Y2, F2 = run_gpu(packed, 256)
+    assert rel_err(Y1, Y2) <= 2e-2 and rel_err(F1, F2) <= 2e-2
+
+
 SAMPLE_HEADS = {"cfg1_mamba2_2.7b_bf16": [0, 41, 79], "cfg2a_state64_bf16": [0, 31],
                 "cfg2b_state256_bf16": [5, 30], "cfg3_long16k_bf16": [0, 47, 79],
                 "cfg4_varlen32k_bf16": [0, 13, 79]}
