@@ -28,6 +28,8 @@ struct Plan {
     int lds_bytes, xs_off, xts_off, bs_off, hs_off, cs_lds_off;
     int split;        // the split-role walker (bf16, 256-row chunks, d_state 64 / 128)
     int nseg;         // segments per sequence of a batch without seq_offsets
+    int nsplit;       // summary parts per segment
+    int summary_lds;
     size_t seg_off, segd_off;
     walk_fn_t walk;   // the walk kernel instance for this plan
     walk_fn_t summary;   // the segment-summary instance (nseg > 1)
@@ -144,17 +146,24 @@ int make_plan(const ssd_problem* p, Plan* pl) {
     pl->seg_off = align_up(pl->ct_off + bt_bytes, 256);   // C fragments: as many bytes as B^T
     // Segmented walk: when the (sequence, head, P tile) items of a batch cannot fill the
     // 256 compute units of the part, each sequence is walked as nseg segments of at
-    // least 4 chunks, after a pass that sums up every segment but the last.
+    // least 4 chunks, after a pass that sums up every segment but the last, in parts
+    // of at least 2 chunks, about two summary workgroups per compute unit.
     pl->nseg = 1;
+    pl->nsplit = 1;
     if (pl->split) {
         const int64_t items = p->nseq * p->nheads * (P / 64);
         int64_t k = kComputeUnits / items;
         if (k > nc / 4) k = nc / 4;
-        if (k > 1) pl->nseg = (int)k;
+        if (k > 1) {
+            pl->nseg = (int)k;
+            int64_t m = 2 * kComputeUnits / (items * (k - 1));
+            if (m > nc / k / 2) m = nc / k / 2;
+            pl->nsplit = m > 1 ? (int)m : 1;
+        }
     }
-    const size_t seg_bytes = (size_t)p->nseq * (pl->nseg - 1) * p->nheads * P * N * sizeof(float);
-    pl->segd_off = align_up(pl->seg_off + seg_bytes, 256);
-    pl->ws_bytes = align_up(pl->segd_off + (size_t)p->nseq * (pl->nseg - 1) * p->nheads * sizeof(float), 256);
+    const size_t nparts = (size_t)p->nseq * (pl->nseg - 1) * pl->nsplit * p->nheads;
+    pl->segd_off = align_up(pl->seg_off + nparts * P * N * sizeof(float), 256);
+    pl->ws_bytes = align_up(pl->segd_off + nparts * sizeof(float), 256);
     // stage the off-diagonal C B^T tiles in LDS when they fit next to a whole chunk of B
     // (or the largest B stage that fits), else read them from global memory
     pl->cb_lds = p->dtype == SSD_DTYPE_BF16 ? 1 : 0;
@@ -179,10 +188,12 @@ int make_plan(const ssd_problem* p, Plan* pl) {
             pl->walk = ssd::ssd_walk_split_kernel<64, false>;
             pl->summary = ssd::ssd_walk_split_kernel<64, true>;
             pl->lds_bytes = ssd::SplitLds<64>::bytes;
+            pl->summary_lds = ssd::SummaryLds<64>::bytes;
         } else {
             pl->walk = ssd::ssd_walk_split_kernel<128, false>;
             pl->summary = ssd::ssd_walk_split_kernel<128, true>;
             pl->lds_bytes = ssd::SplitLds<128>::bytes;
+            pl->summary_lds = ssd::SummaryLds<128>::bytes;
         }
     }
     return SSD_OK;
@@ -357,11 +368,12 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
     wa.hs_off = pl.hs_off;
     wa.cs_off = pl.cs_lds_off;
     wa.nseg = nseg;
+    wa.nsplit = pl.nsplit;
     wa.seg_state = reinterpret_cast<float*>(ws + pl.seg_off);
     wa.seg_decay = reinterpret_cast<float*>(ws + pl.segd_off);
     if ((stages & 2) && nseg > 1) {
-        wa.nitems = (int)(pl.nitems * (nseg - 1));
-        hipLaunchKernelGGL(pl.summary, dim3((unsigned)wa.nitems), dim3(kWalkThreads / 2), pl.lds_bytes, stream, wa);
+        wa.nitems = (int)(pl.nitems * (nseg - 1) * pl.nsplit);
+        hipLaunchKernelGGL(pl.summary, dim3((unsigned)wa.nitems), dim3(kWalkThreads / 2), pl.summary_lds, stream, wa);
     }
     wa.nitems = (int)(pl.nitems * nseg);
     if (stages & 2)

@@ -64,9 +64,10 @@ struct WalkArgs {
     const void* cb;
     const void* bt;   // B^T fragments (split-role walker only)
     const void* ct;   // C fragments (split-role walker only)
-    float* seg_state;   // segmented walk: [nseq][nseg - 1][H][P][N] float32 states
-    float* seg_decay;   // and [nseq][nseg - 1][H] total log2 decays of the segments
+    float* seg_state;   // segmented walk: [nseq][nseg - 1][nsplit][H][P][N] float32
+    float* seg_decay;   // states of the summed-up parts and their total log2 decays
     int nseg;           // segments per sequence (1 unless the split walker segments)
+    int nsplit;         // summary parts per segment
     int64_t T;
     int H, P, N, G, Q, Qp, ntile, nseq, ptiles, nitems, qb;
     int cb_lds;                                    // stage off-diagonal C B^T tiles in LDS

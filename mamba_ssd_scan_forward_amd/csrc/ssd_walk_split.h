@@ -58,6 +58,16 @@ template <int NP> struct SplitLds {
     static constexpr int bytes = csp + 4 * 256 * 4;
 };
 
+// LDS of the segment summaries (state waves only): X~ [2][256][64], the cumsum [2][256]
+// and the private copies [4][256]; small enough for two workgroups per compute unit.
+template <int NP> struct SummaryLds {
+    static constexpr int xts = 0;
+    static constexpr int cs = xts + 2 * 256 * 64 * 2;
+    static constexpr int csp = cs + 2 * 256 * 4;
+    static constexpr int bytes = csp + 4 * 256 * 4;
+    static constexpr int hs = 0, hstride = NP + 8, ys = 0, ystride = 72;   // not used
+};
+
 // Bytes of B^T fragments per (chunk slot, group) in the workspace.
 __host__ __device__ constexpr int split_bt_bytes(int N) { return N * 512; }
 
@@ -65,18 +75,19 @@ __host__ __device__ constexpr int split_bt_bytes(int N) { return N * 512; }
 // per (sequence, segment, head, P tile), so that few sequences still fill the chip.
 // This is the chunk recurrence h_{c+1} = a_c h_c + S_c taken two levels deep, as in a
 // scan over an associative operator on pairs (a, S):
-//   SUMMARY = true : for every segment k but the last, the state waves alone walk its
-//                    chunks from a zero state and store that state and the segment's
-//                    total log2 decay (256 threads per workgroup);
-//   SUMMARY = false: segment k starts from E_k, with E_0 the initial state (or zero) and
-//                    E_{k+1} = 2^(decay_k) E_k + state_k, folded in the prologue, and
-//                    walks its chunks in full.  Only the last segment writes the final
-//                    state.
+//   SUMMARY = true : every segment but the last is cut into nsplit parts; for each part
+//                    the state waves alone walk its chunks from a zero state and store
+//                    that state and the part's total log2 decay (256 threads per
+//                    workgroup, two workgroups per compute unit);
+//   SUMMARY = false: segment k starts from E_k: the initial state (or zero) folded with
+//                    the parts of segments 0 .. k-1 in order, E <- 2^(decay) E + state,
+//                    in the prologue; it then walks its chunks in full.  Only the last
+//                    segment writes the final state.
 template <int NP, bool SUMMARY>
 __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
     typedef Elem<__bf16> E;
     typedef bf16x8 frag;
-    typedef SplitLds<NP> L;
+    typedef std::conditional_t<SUMMARY, SummaryLds<NP>, SplitLds<NP>> L;
     typedef LdsMat<__bf16, 64> XL;
     typedef LdsCol<__bf16, 64> XC;
     constexpr int NT = NP / 32;        // 32-wide n tiles
@@ -92,13 +103,17 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int item = xcd_remap(blockIdx.x, gridDim.x);
     if (item >= a.nitems) return;
-    // item = ((s * nseg' + segment) * H + h) * ptiles + pt, nseg' = nseg - 1 for the
-    // summaries: the heads of one segment sit next to each other (one XCD, one L2)
+    // item = ((s * nseg + segment) * H + h) * ptiles + pt for the walk and
+    // (((s * (nseg - 1) + segment) * nsplit + part) * H + h) * ptiles + pt for the
+    // summaries: the heads of one stretch of chunks sit next to each other (one XCD,
+    // one L2)
     const int pt = item % a.ptiles;
     const int sk = item / a.ptiles / a.H;
     const int h = item / a.ptiles % a.H;
+    const int part = SUMMARY ? sk % a.nsplit : 0;
+    const int skk = SUMMARY ? sk / a.nsplit : sk;
     const int nsk = SUMMARY ? a.nseg - 1 : a.nseg;
-    const int s = sk / nsk, seg = sk % nsk;
+    const int s = skk / nsk, seg = skk % nsk;
     const int g = h / (a.H / a.G);
     const int p_base = pt * 64;
     const int H = a.H, P = a.P, N = a.N, G = a.G;
@@ -119,7 +134,12 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
         // segments of a batch without seq_offsets: chunks [c0, c1) of sequence s; every
         // segment but the last holds whole chunks only
         const int nc = (len_seq + 255) / 256;
-        const int c0 = (int)((int64_t)seg * nc / a.nseg), c1 = (int)((int64_t)(seg + 1) * nc / a.nseg);
+        int c0 = (int)((int64_t)seg * nc / a.nseg), c1 = (int)((int64_t)(seg + 1) * nc / a.nseg);
+        if (SUMMARY) {
+            const int l = c1 - c0;
+            c1 = c0 + (part + 1) * l / a.nsplit;
+            c0 = c0 + part * l / a.nsplit;
+        }
         row0 += (int64_t)c0 * 256;
         slot0 += c0;
         len_seq = min(len_seq, c1 * 256) - c0 * 256;
@@ -154,13 +174,14 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
         frag pbt[16];                         // B^T fragments of the chunk: (block j, K-step)
         frag px[8];
 
-        auto load_bt = [&](int c) {
+        auto load_bt_to = [&](frag (&dst)[16], int c) {
             const rsrc_t r = make_rsrc(BTg + (int64_t)((slot0 + c) * G + g) * (split_bt_bytes(N) / 2),
                                        (uint32_t)split_bt_bytes(N));
             const uint32_t lb = opaque(16u * lane);
 #pragma unroll
-            for (int f = 0; f < 16; ++f) pbt[f] = E::ldb8(r, lb, (uint32_t)((my_nt * 16 + f) * 1024));
+            for (int f = 0; f < 16; ++f) dst[f] = E::ldb8(r, lb, (uint32_t)((my_nt * 16 + f) * 1024));
         };
+        auto load_bt = [&](int c) { load_bt_to(pbt, c); };
         auto prefetch_x = [&](int c) {
             int64_t rowc;
             int len;
@@ -171,27 +192,29 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) px[k] = E::ldb8(xr, xb + k * xstep);
         };
-        // the cumsum of chunk c (1 KB) straight to LDS: wave 0 fills the shared buffer,
-        // every state wave its private copy.  Issued after the wave's last LDS read of the
-        // current chunk; the wave then waits for all its outstanding memory operations
-        // (the older ones are long complete), so the private copy can be read at once and
-        // the shared one is complete before the next barrier.
-        float* csp = reinterpret_cast<float*>(smem + L::csp) + sw * 256;
-        auto dma_cs = [&](int c) {
-            const rsrc_t csr = make_rsrc(a.cs + ((int64_t)(slot0 + c) * H + h) * 256, 256 * 4);
-            const uint32_t lb = opaque(16u * lane);
-            if (sw == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(csr, (SSD_LDS void*)cs_buf(c), 16, lb, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(csr, (SSD_LDS void*)csp, 16, lb, 0, 0, 0);
-            __builtin_amdgcn_s_waitcnt(0);
+        // The cumsum of a chunk (1 KB, four values per lane) is loaded into registers
+        // together with X and written to LDS once the wave no longer reads the buffer:
+        // wave 0 fills the shared buffer (c & 1) and reads it itself, waves 1-3 fill and
+        // read private copies.  (The destination is a select, not a branch, so that
+        // every wave issues the same memory operations and the compiler's wait counts
+        // stay exact.)
+        float* const csp = reinterpret_cast<float*>(smem + L::csp) + sw * 256;
+        auto cs_own = [&](int c) { return sw == 0 ? cs_buf(c) : csp; };
+        f32x4 csv;
+        auto load_cs = [&](int src) {
+            const rsrc_t csr = make_rsrc(a.cs + ((int64_t)(slot0 + src) * H + h) * 256, 256 * 4);
+            csv = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(csr, (int)opaque(16u * lane), 0, 0));
         };
+        auto put_cs = [&](int c) { *reinterpret_cast<f32x4*>(cs_own(c) + 4 * lane) = csv; };
         // X~ = X scaled by its decay to the end of its 32-row block, from the private copy
         // of the cumsum; done before B_mid, while the output waves still read this chunk
         frag pxt[8];
-        auto scale_x = [&]() {
+        auto scale_x = [&](int c) {
+            const float* csx = cs_own(c);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const int r = (ts >> 3) + 32 * k;
-                const float f = fast_exp2(csp[32 * k + 31] - csp[r]);
+                const float f = fast_exp2(csx[32 * k + 31] - csx[r]);
 #pragma unroll
                 for (int q = 0; q < 8; ++q) pxt[k][q] = E::from_f(E::to_f(px[k][q]) * f);
             }
@@ -246,7 +269,7 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
         // overlaps the other's MFMAs), merged at the end; two tiles interleave by
         // themselves.
         constexpr bool DUAL = TPS == 1;
-        auto state_chunk = [&](int c) {
+        auto state_chunk_with = [&](int c, const frag (&bt)[16]) {
             const float* css = cs_buf(c);
             const __bf16* Xts = xts_buf(c);
             f32x16 hodd = {};
@@ -263,16 +286,16 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
                     const float f = fast_exp2(e - ref1);
                     ref1 = e;
                     hodd *= f;
-                    hodd = E::mma(hodd, pbt[2 * j], bv[0][0]);
-                    hodd = E::mma(hodd, pbt[2 * j + 1], bv[0][1]);
+                    hodd = E::mma(hodd, bt[2 * j], bv[0][0]);
+                    hodd = E::mma(hodd, bt[2 * j + 1], bv[0][1]);
                 } else {
                     const float f = fast_exp2(e - ref0);
                     ref0 = e;
 #pragma unroll
                     for (int u = 0; u < TPS; ++u) {
                         hacc[u] *= f;
-                        hacc[u] = E::mma(hacc[u], pbt[2 * j], bv[u][0]);
-                        hacc[u] = E::mma(hacc[u], pbt[2 * j + 1], bv[u][1]);
+                        hacc[u] = E::mma(hacc[u], bt[2 * j], bv[u][0]);
+                        hacc[u] = E::mma(hacc[u], bt[2 * j + 1], bv[u][1]);
                     }
                 }
             }
@@ -281,6 +304,7 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
                 hacc[0] = hacc[0] * fast_exp2(ref1 - ref0) + hodd;
             }
         };
+        auto state_chunk = [&](int c) { state_chunk_with(c, pbt); };
 
         // the state tiles of this wave from / to a [P][N] float32 state at `base`
         auto add_state = [&](const float* base, float f) {
@@ -307,77 +331,96 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
             }
         };
         const int64_t pn = (int64_t)P * N;
-        auto summary_at = [&](int k) { return ((int64_t)s * (a.nseg - 1) + k) * H + h; };
+        auto summary_at = [&](int k, int j) { return (((int64_t)s * (a.nseg - 1) + k) * a.nsplit + j) * H + h; };
 #pragma unroll
         for (int u = 0; u < TPS; ++u) hacc[u] = f32x16{};
 
         if constexpr (SUMMARY) {
             // ---------------------------------------------- segment summary (state only)
-            // one barrier per chunk: X~ is double-buffered and written right after it
-            // has been scaled, and nothing else is shared
+            // One barrier per chunk: X~ is double-buffered and written right after it
+            // has been scaled, and nothing else is shared.  The next chunk's cumsum, X
+            // and B^T (into the other buffer) are issued in that order before this
+            // chunk's products; the wave then waits for all but the 16 B^T loads.
+            // Every step issues the same loads (the last chunk's step reloads that chunk
+            // into buffers nobody reads again; a step past the end only loads), so the
+            // compiler's wait counts need not allow for skipped loads.
             float dsum = 0.f;
+            frag pbt2[16];
             if (nchunks > 0) {
+                load_cs(0);
                 load_bt(0);
                 prefetch_x(0);
-                dma_cs(0);
-                scale_x();
+                put_cs(0);
+                scale_x(0);
                 commit_x(0);
             }
             __syncthreads();
-            for (int c = 0; c < nchunks; ++c) {
-                const bool more = c + 1 < nchunks;
-                if (more) prefetch_x(c + 1);
-                state_chunk(c);
-                dsum += cs_buf(c)[255];
-                if (more) {
-                    dma_cs(c + 1);
-                    load_bt(c + 1);
-                    scale_x();
-                    commit_x(c + 1);
+            auto summary_step = [&](int c, const frag (&cur)[16], frag (&nxt)[16]) {
+                const int cn = min(c + 1, nchunks - 1);
+                load_cs(cn);
+                prefetch_x(cn);
+                load_bt_to(nxt, cn);
+                __builtin_amdgcn_sched_barrier(0);
+                if (c < nchunks) {
+                    state_chunk_with(c, cur);
+                    dsum += cs_buf(c)[255];
                 }
+                put_cs(c + 1);
+                scale_x(c + 1);
+                commit_x(c + 1);
                 __syncthreads();
+            };
+            for (int c = 0; c < nchunks; c += 2) {
+                summary_step(c, pbt, pbt2);
+                summary_step(c + 1, pbt2, pbt);
             }
-            put_state(a.seg_state + summary_at(seg) * pn);
-            if (sw == 0 && pt == 0 && lane == 0) a.seg_decay[summary_at(seg)] = dsum;
+            put_state(a.seg_state + summary_at(seg, part) * pn);
+            if (sw == 0 && pt == 0 && lane == 0) a.seg_decay[summary_at(seg, part)] = dsum;
             return;
         }
 
         // the entry state of this segment
         if (a.init) add_state(a.init + state_base, 0.f);
         for (int k = 0; k < seg; ++k)
-            add_state(a.seg_state + summary_at(k) * pn, fast_exp2(a.seg_decay[summary_at(k)]));
+            for (int j = 0; j < a.nsplit; ++j)
+                add_state(a.seg_state + summary_at(k, j) * pn, fast_exp2(a.seg_decay[summary_at(k, j)]));
 
         if (nchunks > 0) {
+            load_cs(0);
             load_bt(0);
             prefetch_x(0);
-            dma_cs(0);
+            put_cs(0);
         }
-        __syncthreads();   // the cumsum of chunk 0 has landed
+        __syncthreads();   // the cumsum of chunk 0 is in LDS
         if (nchunks > 0) {
-            scale_x();
+            scale_x(0);
             commit_x(0);
         }
         pack_h();
         write_h();
         __syncthreads();
+        // The loop issues the same loads and stores in every iteration: the last one
+        // reloads its own chunk into buffers that nobody reads again (a skipped load
+        // would make the compiler wait for every newer one before the next use).
         for (int c = 0; c < nchunks; ++c) {
-            const bool more = c + 1 < nchunks;
-            if (c > 0) store_y(c - 1, 0);
-            if (more) prefetch_x(c + 1);
+            const int cn = min(c + 1, nchunks - 1);
+            load_cs(cn);
+            prefetch_x(cn);
+            // keep the prefetch ahead of the products (the scheduler would sink it to
+            // shorten the live ranges, and then wait for it right after them)
+            __builtin_amdgcn_sched_barrier(0);
             state_chunk(c);
-            if (more) {
-                dma_cs(c + 1);
-                load_bt(c + 1);
-                scale_x();
-            }
+            load_bt(cn);
+            put_cs(c + 1);
+            scale_x(c + 1);
             pack_h();
-            __syncthreads();   // B_mid: X~ and h of chunk c are no longer read
+            __syncthreads();   // B_mid: h of chunk c is no longer read
             store_y(c, 1);
             write_h();
-            if (more) commit_x(c + 1);
+            commit_x(c + 1);
             __syncthreads();   // B_end
+            store_y(c, 0);
         }
-        if (nchunks > 0) store_y(nchunks - 1, 0);
         if (a.final_state && seg == a.nseg - 1) put_state(a.final_state + state_base);
     } else if constexpr (!SUMMARY) {
         // ========================================================== output waves
@@ -445,7 +488,7 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
 #pragma unroll
                 for (int v = 0; v < 2; ++v) acc[v] = E::mma(acc[v], hv[ks & 1][v], pc[u][ks]);
             }
-            if (c + 1 < nchunks) load_c(c + 1, u);
+            load_c(min(c + 1, nchunks - 1), u);
             float prev = 0.f;
             frag xf[2][2][2];   // (buffer, p sub-tile, K-step)
             if (i > 0) {
@@ -512,7 +555,9 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
                 __bf16* xb = reinterpret_cast<__bf16*>(smem + L::ys) + (u * 4 + ok_) * 32 * L::ystride;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    const int r = 8 * k + (lane >> 3), c8 = (lane & 7) * 8;
+                    // (opaque: the row indexes of this cold path are not worth registers
+                    // held across the loop)
+                    const int r = 8 * k + (int)opaque((uint32_t)lane >> 3), c8 = (lane & 7) * 8;
                     const frag v = l0 + r < len ? E::ldg8(X + ((rowc + l0 + r) * H + h) * (int64_t)P + p_base + c8) : E::zero();
                     *reinterpret_cast<frag*>(xb + XL::idx(r, c8)) = v;
                 }
@@ -542,7 +587,7 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
             acc[0] *= f2;
             acc[1] *= f2;
             // the next chunk's diagonal tile of this block travels while this one is used
-            if (c + 1 < nchunks) load_dg(c + 1, u);
+            load_dg(min(c + 1, nchunks - 1), u);
             __bf16* ys = reinterpret_cast<__bf16*>(smem + L::ys) + (u * 4 + ok_) * 32 * L::ystride;
 #pragma unroll
             for (int v = 0; v < 2; ++v)
@@ -562,11 +607,10 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
         __syncthreads();
         __syncthreads();
         for (int c = 0; c < nchunks; ++c) {
-            const bool more = c + 1 < nchunks;
             const float prev2 = left_and_chain(c, 1);
             diag(c, 1, prev2);
             const float prev1 = left_and_chain(c, 0);
-            if (more) load_cb(c + 1);
+            load_cb(min(c + 1, nchunks - 1));
             __syncthreads();   // B_mid: X~ and h of chunk c are no longer read
             diag(c, 0, prev1);
             __syncthreads();   // B_end
