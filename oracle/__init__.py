@@ -18,6 +18,10 @@ What is computed (page: "Transformers are SSMs" paper summary):
   length, ragged last chunk included.
 * ``decode_step`` -- one step of the recurrence for a single token per sequence
   (the recurrent mode of section 3), continuing from a given state.
+* ``backward`` -- the reverse-mode derivative of ``recurrence`` (the adjoint
+  recurrence, walked backwards over the tokens; the pages state only its cost,
+  section 6's training FLOPs), run by ``ssd_oracle.c``.  Pinned by central
+  finite differences of ``recurrence``.
 
 Readings of the pages that these functions take:
 A is the log decay (logA <= 0, a_t = exp(logA_t), -inf allowed, giving a = 0);
@@ -60,6 +64,10 @@ def _load():
                                               ctypes.POINTER(ctypes.c_int64), i64, d, d,
                                               ctypes.c_int]
         lib.ssd_oracle_recurrence.restype = ctypes.c_int
+        lib.ssd_oracle_backward.argtypes = [i64, i64, i64, i64, i64, i64, d, d, d, d, d,
+                                            ctypes.POINTER(ctypes.c_int64), i64, d, d,
+                                            d, d, d, d, d, ctypes.c_int]
+        lib.ssd_oracle_backward.restype = ctypes.c_int
         lib.ssd_oracle_threads.argtypes = []
         lib.ssd_oracle_threads.restype = ctypes.c_int
         _lib = lib
@@ -263,3 +271,42 @@ def decode_step(state, x, logA, B, C):
             S[s, h] = np.exp(logA[s, h]) * S[s, h] + np.outer(x[s, h], B[s, g])
             y[s, h] = S[s, h] @ C[s, g]
     return y, S
+
+
+def backward(X, logA, B, C, init=None, seq_offsets=None, dY=None, dfinal=None, nthreads: int = 0):
+    """Gradients of L = <dY, Y> + <dfinal, final> with respect to X, logA, B, C and init,
+    where (Y, final) = recurrence(X, logA, B, C, init, seq_offsets).  float64.
+    Returns (dX [b,T,H,P], dlogA [b,T,H], dB, dC [b,T,G,N], dinit [nseq,H,P,N] or None)."""
+    X, logA, B, C = _f64(X), _f64(logA), _f64(B), _f64(C)
+    b, T, H, P, N, G = _shapes(X, logA, B, C)
+    nseq = b if seq_offsets is None else int(np.asarray(seq_offsets).size - 1)
+    dY = _f64(dY)
+    assert dY.shape == X.shape, dY.shape
+    dp = ctypes.POINTER(ctypes.c_double)
+    init_p = dfinal_p = None
+    if init is not None:
+        init = _f64(init)
+        assert init.shape == (nseq, H, P, N), init.shape
+        init_p = init.ctypes.data_as(dp)
+    if dfinal is not None:
+        dfinal = _f64(dfinal)
+        assert dfinal.shape == (nseq, H, P, N), dfinal.shape
+        dfinal_p = dfinal.ctypes.data_as(dp)
+    off_p = None
+    if seq_offsets is not None:
+        off = np.ascontiguousarray(np.asarray(seq_offsets, dtype=np.int64).reshape(-1))
+        off_p = off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    dX = np.zeros_like(X)
+    dlogA = np.zeros_like(logA)
+    dB = np.zeros_like(B)
+    dC = np.zeros_like(C)
+    dinit = np.zeros((nseq, H, P, N)) if init is not None else None
+    rc = _load().ssd_oracle_backward(b, T, H, P, N, G, X.ctypes.data_as(dp), logA.ctypes.data_as(dp),
+                                     B.ctypes.data_as(dp), C.ctypes.data_as(dp), init_p, off_p, nseq,
+                                     dY.ctypes.data_as(dp), dfinal_p, dX.ctypes.data_as(dp),
+                                     dlogA.ctypes.data_as(dp), dB.ctypes.data_as(dp),
+                                     dC.ctypes.data_as(dp),
+                                     None if dinit is None else dinit.ctypes.data_as(dp), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"ssd_oracle_backward failed with code {rc}")
+    return dX, dlogA, dB, dC, dinit

@@ -321,3 +321,87 @@ def test_decode_steps_continue_the_forward_pass():
         y, S = oracle.decode_step(S, X[:, t], logA[:, t], B[:, t], C[:, t])
         np.testing.assert_allclose(y, Y_all[:, t], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(S, F_all, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- backward
+# The adjoint recurrence is pinned by central finite differences of the forward
+# oracle: L = <dY, Y> + <dF, final>, every entry of every input of tiny problems.
+
+def _fd_loss(X, logA, B, C, I, off, dY, dF):
+    Y, F = oracle.recurrence(X, logA, B, C, I, off)
+    return float(np.sum(dY * Y) + (0.0 if dF is None else np.sum(dF * F)))
+
+
+def _fd_grad(arr, f, eps=1e-6):
+    g = np.zeros_like(arr)
+    it = np.nditer(arr, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        v = arr[i]
+        arr[i] = v + eps
+        lp = f()
+        arr[i] = v - eps
+        lm = f()
+        arr[i] = v
+        g[i] = (lp - lm) / (2 * eps)
+    return g
+
+
+@pytest.mark.parametrize("case", ["batch_init_dfinal", "packed_groups_empty", "no_init_no_dfinal"])
+def test_backward_matches_finite_differences(case):
+    rng = np.random.default_rng(77)
+    off = None
+    if case == "batch_init_dfinal":
+        X, logA, B, C, I = rand_problem(70, b=2, T=5, H=2, P=3, N=2, G=1)
+        use_df = True
+    elif case == "packed_groups_empty":
+        lens = [3, 0, 4, 1]
+        off = np.cumsum([0] + lens)
+        X, logA, B, C, I = rand_problem(71, b=1, T=8, H=4, P=2, N=3, G=2, nseq=4)
+        use_df = True
+    else:
+        X, logA, B, C, I = rand_problem(72, b=1, T=6, H=2, P=2, N=2, G=2, init=False)
+        use_df = False
+    nseq = X.shape[0] if off is None else len(off) - 1
+    dY = rng.standard_normal(X.shape)
+    dF = rng.standard_normal((nseq,) + X.shape[2:] + (B.shape[3],)) if use_df else None
+    dX, dlogA, dB, dC, dI = oracle.backward(X, logA, B, C, I, off, dY, dF)
+    f = lambda: _fd_loss(X, logA, B, C, I, off, dY, dF)
+    for name, arr, got in [("X", X, dX), ("logA", logA, dlogA), ("B", B, dB), ("C", C, dC)] + \
+            ([("init", I, dI)] if I is not None else []):
+        want = _fd_grad(arr, f)
+        np.testing.assert_allclose(got, want, rtol=1e-6, atol=1e-8, err_msg=name)
+    if I is None:
+        assert dI is None
+
+
+def test_backward_empty_sequence_passes_dfinal_to_dinit():
+    X, logA, B, C, I = rand_problem(73, b=1, T=4, H=2, P=2, N=2, G=1, nseq=3)
+    off = np.array([0, 4, 4, 4])
+    rng = np.random.default_rng(5)
+    dY = rng.standard_normal(X.shape)
+    dF = rng.standard_normal(I.shape)
+    _, _, _, _, dI = oracle.backward(X, logA, B, C, I, off, dY, dF)
+    np.testing.assert_array_equal(dI[1:], dF[1:])
+
+
+def test_backward_long_sequence_crosses_checkpoints():
+    """A sequence of 150 tokens (three stretches between stored states), a few
+    directional finite differences."""
+    X, logA, B, C, I = rand_problem(74, b=1, T=150, H=2, P=3, N=4, G=1)
+    rng = np.random.default_rng(6)
+    dY = rng.standard_normal(X.shape)
+    dF = rng.standard_normal(I.shape)
+    grads = oracle.backward(X, logA, B, C, I, None, dY, dF)
+    for k, arr in enumerate([X, logA, B, C, I]):
+        v = rng.standard_normal(arr.shape)
+        eps = 1e-6
+        orig = arr.copy()
+        arr += eps * v
+        lp = _fd_loss(X, logA, B, C, I, None, dY, dF)
+        arr[...] = orig - eps * v
+        lm = _fd_loss(X, logA, B, C, I, None, dY, dF)
+        arr[...] = orig
+        want = (lp - lm) / (2 * eps)
+        got = float(np.sum(grads[k] * v))
+        assert abs(got - want) <= 1e-6 * max(1.0, abs(want)), (k, got, want)
