@@ -142,6 +142,39 @@ int ssd_forward_stage(int stage, const ssd_problem* p, const void* X, const floa
 int ssd_decode_step(const ssd_problem* p, const void* x, const float* logA, const void* B,
                     const void* C, float* state, void* y, void* hip_stream);
 
+/* Bytes of device scratch that ssd_backward needs for problem p (0 if p is invalid). */
+size_t ssd_backward_workspace_bytes(const ssd_problem* p);
+
+/* Gradients of the forward pass: for L = <dY, Y> + <dfinal, final_state>, the
+ * derivatives of L with respect to X, logA, B, C and init_state.  The pages give only
+ * the cost of training (section 6); the derivative is that of the recurrence of
+ * section 2.4, the adjoint state G walked backwards over the tokens:
+ *     G_t = a_{t+1} G_{t+1} + dy_t C_t^T        (G after the last token: dfinal)
+ *     dx_t = G_t B_t,  dB_t = sum_h G_t^T x_t,  dC_t = sum_h S_t^T dy_t,
+ *     dlogA_t = a_t <G_t, S_{t-1}>,  dinit = a_0 G_0       (sums over the group's heads)
+ * computed as three forward passes on re-arranged operands (time reversed for dX, dinit
+ * and dB) and small re-arranging and summing kernels.  The problem and the first six
+ * arguments are those of the ssd_forward call being differentiated; further (device):
+ *   Y            [b, T, H, P]     dtype          that call's output
+ *   final_state  [nseq, H, P, N]  float32        its final state; required when dfinal
+ *                                                is given, else may be NULL
+ *   dY           [b, T, H, P]     dtype          gradient of the output
+ *   dfinal       [nseq, H, P, N]  float32        gradient of the final state, or NULL (zero)
+ *   dX           [b, T, H, P]     dtype (out)
+ *   dlogA        [b, T, H]        float32 (out)
+ *   dB, dC       [b, T, G, N]     dtype (out)
+ *   dinit        [nseq, H, P, N]  float32 (out)  or NULL to skip (defined with or
+ *                                                without init_state)
+ *   workspace    >= ssd_backward_workspace_bytes(p) bytes, 256-byte aligned
+ * The outputs must not overlap any input, the workspace or each other.  Supported
+ * problems: those of ssd_forward whose transposed problem (head dimension and state
+ * size swapped) is supported too.  Returns SSD_OK or an ssd_status error code. */
+int ssd_backward(const ssd_problem* p, const void* X, const float* logA, const void* B, const void* C,
+                 const float* init_state, const int32_t* seq_offsets, const void* Y,
+                 const float* final_state, const void* dY, const float* dfinal, void* dX, float* dlogA,
+                 void* dB, void* dC, float* dinit, void* workspace, size_t workspace_bytes,
+                 void* hip_stream);
+
 /* Static English text for a status code (never NULL). */
 const char* ssd_status_string(int status);
 

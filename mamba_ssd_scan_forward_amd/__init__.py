@@ -24,8 +24,8 @@ __all__ = [
     "SSD_OK", "SSD_ERR_INVALID_ARG", "SSD_ERR_UNSUPPORTED", "SSD_ERR_WORKSPACE", "SSD_ERR_HIP",
     "SSD_DTYPE_F32", "SSD_DTYPE_BF16", "SsdProblem", "SsdError", "lib_path", "load_library",
     "ssd_check_problem", "ssd_workspace_bytes", "ssd_forward", "ssd_forward_stage",
-    "ssd_decode_step", "ssd_status_string",
-    "ssd_abi_version", "forward", "decode_step", "problem_for",
+    "ssd_decode_step", "ssd_backward_workspace_bytes", "ssd_backward", "ssd_status_string",
+    "ssd_abi_version", "forward", "decode_step", "backward", "problem_for",
 ]
 
 SSD_OK = 0
@@ -82,6 +82,10 @@ def load_library():
     lib.ssd_forward_stage.restype = ctypes.c_int
     lib.ssd_decode_step.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_decode_step.restype = ctypes.c_int
+    lib.ssd_backward_workspace_bytes.argtypes = [pp]
+    lib.ssd_backward_workspace_bytes.restype = sz
+    lib.ssd_backward.argtypes = [pp] + [vp] * 16 + [sz, vp]
+    lib.ssd_backward.restype = ctypes.c_int
     lib.ssd_status_string.argtypes = [ctypes.c_int]
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_abi_version.argtypes = []
@@ -129,6 +133,18 @@ def ssd_decode_step(problem: SsdProblem, x, logA, B, C, state, y, hip_stream) ->
     """Direct call of ssd_decode_step (device addresses as integers); returns the status."""
     return int(load_library().ssd_decode_step(ctypes.byref(problem), x, logA, B, C, state, y,
                                               hip_stream))
+
+
+def ssd_backward_workspace_bytes(problem: SsdProblem) -> int:
+    return int(load_library().ssd_backward_workspace_bytes(ctypes.byref(problem)))
+
+
+def ssd_backward(problem: SsdProblem, X, logA, B, C, init_state, seq_offsets, Y, final_state, dY,
+                 dfinal, dX, dlogA, dB, dC, dinit, workspace, workspace_bytes: int, hip_stream) -> int:
+    """Direct call of ssd_backward (device addresses as integers or None); returns the status."""
+    return int(load_library().ssd_backward(ctypes.byref(problem), X, logA, B, C, init_state, seq_offsets,
+                                           Y, final_state, dY, dfinal, dX, dlogA, dB, dC, dinit,
+                                           workspace, int(workspace_bytes), hip_stream))
 
 
 def problem_for(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len, nseq, dtype) -> SsdProblem:
@@ -221,3 +237,53 @@ def decode_step(x, logA, B, C, state, y=None):
     if rc != SSD_OK:
         raise SsdError(rc, "ssd_decode_step")
     return y
+
+
+def backward(X, logA, B, C, chunk_len: int, Y, dY, init_state=None, seq_offsets=None,
+             final_state=None, dfinal=None, need_dinit: bool = True, workspace=None):
+    """Gradients of <dY, Y> + <dfinal, final_state> for the forward pass
+    ``(Y, final_state) = forward(X, logA, B, C, chunk_len, init_state, seq_offsets)``, on the
+    current HIP stream.  Returns (dX, dlogA, dB, dC, dinit or None)."""
+    import torch
+
+    if X.dtype == torch.bfloat16:
+        dt = SSD_DTYPE_BF16
+    elif X.dtype == torch.float32:
+        dt = SSD_DTYPE_F32
+    else:
+        raise TypeError(f"unsupported dtype {X.dtype}")
+    if not X.is_cuda:
+        raise ValueError("backward() needs device tensors")
+    b, T, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    if tuple(Y.shape) != tuple(X.shape) or tuple(dY.shape) != tuple(X.shape):
+        raise ValueError("Y and dY must have X's shape")
+    if Y.dtype != X.dtype or dY.dtype != X.dtype:
+        raise TypeError("Y and dY must share X's dtype")
+    nseq = b if seq_offsets is None else seq_offsets.numel() - 1
+    if dfinal is not None and final_state is None:
+        raise ValueError("dfinal needs the forward pass's final_state")
+    for name, t in (("init_state", init_state), ("final_state", final_state), ("dfinal", dfinal)):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (nseq, H, P, N)):
+            raise ValueError(f"{name} must be float32 [nseq, H, P, N]")
+    X, logA, B, C, Y, dY = (t.contiguous() for t in (X, logA, B, C, Y, dY))
+    init_state, final_state, dfinal, seq_offsets = (None if t is None else t.contiguous()
+                                                    for t in (init_state, final_state, dfinal, seq_offsets))
+    prob = problem_for(b, T, H, P, N, G, int(chunk_len), nseq, dt)
+    wsb = ssd_backward_workspace_bytes(prob)
+    if wsb == 0:
+        raise SsdError(ssd_check_problem(prob) or SSD_ERR_UNSUPPORTED, "ssd_backward_workspace_bytes")
+    if workspace is None or workspace.numel() < wsb:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=X.device)
+    dX = torch.empty_like(X)
+    dlogA = torch.empty_like(logA)
+    dB = torch.empty_like(B)
+    dC = torch.empty_like(C)
+    dinit = torch.empty((nseq, H, P, N), dtype=torch.float32, device=X.device) if need_dinit else None
+    stream = torch.cuda.current_stream(X.device).cuda_stream
+    rc = ssd_backward(prob, _ptr(X), _ptr(logA), _ptr(B), _ptr(C), _ptr(init_state), _ptr(seq_offsets),
+                      _ptr(Y), _ptr(final_state), _ptr(dY), _ptr(dfinal), _ptr(dX), _ptr(dlogA), _ptr(dB),
+                      _ptr(dC), _ptr(dinit), _ptr(workspace), wsb, stream)
+    if rc != SSD_OK:
+        raise SsdError(rc, "ssd_backward")
+    return dX, dlogA, dB, dC, dinit

@@ -1,0 +1,210 @@
+// ssd_backward.h -- the small HBM-bound kernels of the SSD layer's backward pass.
+//
+// The pages give only the cost of training (page "Transformers are SSMs" paper
+// summary, section 6: training FLOPs of order T N^2); the derivative itself follows
+// from the recurrence of section 2.4.  With G the adjoint of the P x N state, walked
+// backwards from the final state's gradient dF,
+//     G_t = a_{t+1} G_{t+1} + dy_t C_t^T,   dx_t = G_t B_t,   dB_t = sum_h G_t^T x_t,
+//     dC_t = sum_h S_t^T dy_t,              dlogA_t = a_t <G_t, S_{t-1}>,
+//     dinit = a_0 G_0.
+// Each of G's contractions is an SSD forward pass of its own, so the backward runs the
+// forward kernels three times on re-arranged operands:
+//   dX, dinit: time reversed within every sequence, X' = dY, B' = C, C' = B, the
+//              decays shifted by one token (logA'_0 = 0, logA'_j = logA_{len-j}), the
+//              initial state dF: Y' is dX reversed, the final state is G_0;
+//   dB:        time reversed, X' = C (each head its group's row), B' = dY, C' = X,
+//              initial state dF^T: Y' reversed is dB per head;
+//   dC:        forward time, X' = B per head, B' = X, C' = dY, initial state init^T:
+//              Y' is dC per head;
+// then per-group sums over heads.  The decay gradient uses the identity
+//     dL/dcs_k = dy_k . y_k - x_k . dx_k  (+ <dF, final> at a sequence's last token)
+// for the inclusive cumsum cs of logA, and dlogA_t = sum_{k >= t} dL/dcs_k.
+// The kernels below do the re-arranging, the sums and that reverse cumsum.
+#pragma once
+
+#include "ssd_kernels.h"
+
+namespace ssd {
+
+// Token rows of a [rows, ...] tensor: fixed-length sequences of T rows, or packed ones
+// delimited by seq_offsets.  src(r) is r itself, or its mirror within its sequence.
+struct RowMap {
+    const int32_t* off;
+    int64_t T;
+    int nseq;
+    int reverse;
+
+    __device__ __forceinline__ void range(int64_t r, int64_t* r0, int64_t* r1) const {
+        if (!off) {
+            const int64_t s = r / T;
+            *r0 = s * T;
+            *r1 = *r0 + T;
+            return;
+        }
+        // the last sequence that starts at or before r (empty ones are skipped over)
+        int lo = 0, hi = nseq - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (off[mid] <= r) lo = mid;
+            else hi = mid - 1;
+        }
+        *r0 = off[lo];
+        *r1 = off[lo + 1];
+    }
+    __device__ __forceinline__ int64_t src(int64_t r) const {
+        if (!reverse) return r;
+        int64_t r0, r1;
+        range(r, &r0, &r1);
+        return r0 + r1 - 1 - r;
+    }
+};
+
+__device__ __forceinline__ void seq_rows(int s, int64_t T, const int32_t* off, int64_t* r0, int64_t* r1) {
+    if (off) {
+        *r0 = off[s];
+        *r1 = off[s + 1];
+    } else {
+        *r0 = (int64_t)s * T;
+        *r1 = *r0 + T;
+    }
+}
+
+// out[r][k][:] = in[src(r)][k / (K / Kin)][:], rows of K segments of `seg` 16-byte vectors
+// (a reversed copy when K == Kin, a per-head expansion of per-group rows otherwise)
+__global__ void __launch_bounds__(256) ssd_bwd_remap_kernel(const uint4* in, uint4* out, int64_t rows, int K,
+                                                            int Kin, int seg, RowMap m) {
+    const int64_t total = rows * K * seg;
+    const int per = K / Kin;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+        const int v = (int)(i % seg);
+        const int64_t rk = i / seg;
+        const int k = (int)(rk % K);
+        const int64_t r = rk / K;
+        out[i] = in[(m.src(r) * Kin + k / per) * seg + v];
+    }
+}
+
+// the decays of the reversed sequences: out[r0 + j][h] = j == 0 ? 0 : logA[r1 - j][h]
+__global__ void __launch_bounds__(256) ssd_bwd_logA_kernel(const float* logA, float* out, int64_t rows, int H,
+                                                           RowMap m) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < rows * H; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = i / H;
+        const int h = (int)(i % H);
+        int64_t r0, r1;
+        m.range(r, &r0, &r1);
+        const int64_t j = r - r0;
+        out[i] = j == 0 ? 0.f : logA[(r1 - j) * H + h];
+    }
+}
+
+// [S][P][N] -> [S][N][P], float32
+__global__ void __launch_bounds__(256) ssd_bwd_transpose_kernel(const float* in, float* out, int64_t S, int P, int N) {
+    const int64_t pn = (int64_t)P * N;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < S * pn; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t s = i / pn;
+        const int rem = (int)(i % pn);
+        const int n = rem / P, p = rem % P;
+        out[i] = in[s * pn + (int64_t)p * N + n];
+    }
+}
+
+// out[r][g][:] = sum over the heads h of group g of in[src(r)][h][:] (float32 sums,
+// stored in the element type), 8 values per thread
+template <typename T>
+__global__ void __launch_bounds__(256) ssd_bwd_group_sum_kernel(const T* in, T* out, int64_t rows, int H, int G,
+                                                                int N, RowMap m) {
+    using E = Elem<T>;
+    typedef typename E::frag frag;
+    const int nv = N / 8, hpg = H / G;
+    const int64_t total = rows * G * nv;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+        const int v = (int)(i % nv);
+        const int64_t rg = i / nv;
+        const int g = (int)(rg % G);
+        const int64_t r = rg / G;
+        const int64_t src = m.src(r);
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
+            const frag x = E::ldg8(in + (src * H + h) * (int64_t)N + 8 * v);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[q] += E::to_f(x[q]);
+        }
+        frag o;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) o[q] = E::from_f(acc[q]);
+        *reinterpret_cast<frag*>(out + (r * G + g) * (int64_t)N + 8 * v) = o;
+    }
+}
+
+// rr[r][h] = dy . y - x . dx over the head's P values.  Each thread takes one 16-byte
+// vector of the flat [rows * H * P] arrays (coalesced), and the partial sums of one
+// (row, head) meet in LDS: a block of 256 vectors spans at most 256 / (P / 8) + 1 of them.
+template <typename T>
+__global__ void __launch_bounds__(256) ssd_bwd_dot_kernel(const T* dY, const T* Y, const T* X, const T* dX,
+                                                          float* rr, int64_t rows, int H, int P) {
+    using E = Elem<T>;
+    typedef typename E::frag frag;
+    __shared__ float part[257];
+    const int vpi = P / 8;                             // vectors per (row, head)
+    const int64_t nvec = rows * H * vpi;
+    for (int64_t base = (int64_t)blockIdx.x * 256; base < nvec; base += (int64_t)gridDim.x * 256) {
+        const int64_t item0 = base / vpi;
+        const int64_t item_end = min(nvec, base + 256) - 1;
+        const int nitem = (int)(item_end / vpi - item0) + 1;
+        for (int i = threadIdx.x; i < nitem; i += 256) part[i] = 0.f;
+        __syncthreads();
+        const int64_t v = base + threadIdx.x;
+        if (v < nvec) {
+            const int64_t e = v * 8;
+            const frag a = E::ldg8(dY + e), b = E::ldg8(Y + e), x = E::ldg8(X + e), d = E::ldg8(dX + e);
+            float acc = 0.f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc += E::to_f(a[q]) * E::to_f(b[q]) - E::to_f(x[q]) * E::to_f(d[q]);
+            atomicAdd(&part[v / vpi - item0], acc);
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < nitem; i += 256) rr[item0 + i] = part[i];
+        __syncthreads();
+    }
+}
+
+// dlogA[t][h] = sum over the tokens k >= t of its sequence of rr[k][h], plus <dF, final>
+// of (sequence, head) when dF is given: one wavefront per (sequence, head), 64 tokens
+// per step from the end, a lane scan and a carry.
+__global__ void __launch_bounds__(64) ssd_bwd_dlogA_kernel(const float* rr, const float* dF, const float* F,
+                                                           float* dlogA, int64_t T, const int32_t* off, int H,
+                                                           int PN) {
+    const int sh = blockIdx.x, lane = threadIdx.x;
+    const int s = sh / H, h = sh % H;
+    float carry = 0.f;
+    if (dF) {
+        float acc = 0.f;
+        for (int i = lane; i < PN; i += 64) acc += dF[(int64_t)sh * PN + i] * F[(int64_t)sh * PN + i];
+        carry = __shfl(wave_inclusive_sum(acc, lane), 63, 64);
+    }
+    int64_t r0, r1;
+    seq_rows(s, T, off, &r0, &r1);
+    for (int64_t top = r1; top > r0; top -= 64) {
+        const int64_t t = top - 1 - lane;
+        const float v = t >= r0 ? rr[t * H + h] : 0.f;
+        const float sum = wave_inclusive_sum(v, lane);
+        if (t >= r0) dlogA[t * H + h] = carry + sum;
+        carry += __shfl(sum, 63, 64);
+    }
+}
+
+// dinit = a_0 G_0 in place (G_0 as the reversed pass left it; an empty sequence keeps
+// dF, which that pass passed through)
+__global__ void __launch_bounds__(256) ssd_bwd_dinit_kernel(float* dinit, const float* logA, int64_t T,
+                                                            const int32_t* off, int nseq, int H, int PN) {
+    const int64_t total = (int64_t)nseq * H * PN;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t sh = i / PN;
+        const int s = (int)(sh / H), h = (int)(sh % H);
+        int64_t r0, r1;
+        seq_rows(s, T, off, &r0, &r1);
+        if (r1 > r0) dinit[i] *= fast_exp2(logA[r0 * H + h] * kLog2e);
+    }
+}
+
+}  // namespace ssd

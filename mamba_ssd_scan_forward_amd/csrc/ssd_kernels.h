@@ -44,8 +44,7 @@ struct PrepArgs {
     int H, N, G, Q, Qp, ntile, nseq;
     int cs_blocks;    // workgroups of the cumsum role: nslots * hblocks
     int hblocks;      // 64-head blocks per chunk
-    int cb_groups;    // 4-tile groups per (chunk, group) in the C B^T role
-    int cb_blocks;    // workgroups of the C B^T role: nslots * G * cb_groups
+    int cb_blocks;    // workgroups of the C B^T role: nslots * G
     void* bt;         // optional: B^T of every 256-row chunk in MFMA A-operand fragment
                       // order, [nslots, G, N/32, 8, 2, 64 lanes, 8], and
     void* ct;         // C in MFMA B-operand fragment order, [nslots, G, 8, N/16, 64 lanes,
@@ -134,11 +133,19 @@ __device__ __forceinline__ float wave_inclusive_sum(float x, int lane) {
 constexpr int kPrepHeads = 16;   // heads per cumsum workgroup (small LDS tile: the C B^T role
                                  // shares the launch and its occupancy)
 
+// The C B^T role stages the chunk's B and C rows in LDS in slabs of kCbSlab<T> columns
+// (rows padded by 16 bytes): 40 KB for either element type.
+template <typename T> constexpr int kCbSlab = sizeof(T) == 2 ? 32 : 16;
+template <typename T> constexpr int kCbStride = kCbSlab<T> + 16 / (int)sizeof(T);
+template <typename T> constexpr int kPrepLds = 2 * 256 * kCbStride<T> * (int)sizeof(T);
+
 template <typename T>
-__global__ void __launch_bounds__(256) ssd_prep_kernel(PrepArgs a) {
+__global__ void __launch_bounds__(256, 2) ssd_prep_kernel(PrepArgs a) {
     using E = Elem<T>;
     typedef typename E::frag frag;
-    __shared__ float lt[256][kPrepHeads + 1];
+    static_assert(kPrepLds<T> >= 256 * (kPrepHeads + 1) * 4, "cumsum tile must fit");
+    __shared__ __align__(16) unsigned char smem[kPrepLds<T>];
+    float (*lt)[kPrepHeads + 1] = reinterpret_cast<float (*)[kPrepHeads + 1]>(smem);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lg = lane >> 5;
     int bid = blockIdx.x;
     const bool cs_role = bid < a.cs_blocks;
@@ -153,8 +160,8 @@ __global__ void __launch_bounds__(256) ssd_prep_kernel(PrepArgs a) {
         rest = bid % (a.G * 8);
     } else {
         bid -= a.cs_blocks;
-        k = bid / (a.G * a.cb_groups);
-        rest = bid % (a.G * a.cb_groups);
+        k = bid / a.G;
+        rest = bid % a.G;
     }
     int64_t rowc;
     int len;
@@ -234,50 +241,78 @@ __global__ void __launch_bounds__(256) ssd_prep_kernel(PrepArgs a) {
         return;
     }
 
-    // (b) C B^T tile (i, j), j <= i, one tile per wavefront.  The tile is computed
-    // transposed, D[s][l] = sum_n B[s][n] C[l][n], so that each lane ends with one row l
-    // of C B^T and writes it as runs of 4 consecutive s.  Tiles are stored in the order
-    // of the walk kernel's B-operand fragments: element (l, s) of a tile sits at
-    // ((s / 16) * 64 + ((s % 16) / 8) * 32 + l) * 8 + s % 8, so one fragment of one
+    // (b) C B^T of one (chunk slot, group): all ntile lower tiles (i, j), j <= i, of the
+    // chunk.  B and C rows of the chunk go through LDS in slabs of columns (rows past the
+    // chunk's end as zeros), and wavefront w accumulates tiles w, w + 4, ... over the
+    // slabs, so every row is read from memory once per (chunk, group).  Each tile is
+    // computed transposed, D[s][l] = sum_n B[s][n] C[l][n], so that each lane ends with
+    // one row l of C B^T and writes it as runs of 4 consecutive s.  Tiles are stored in
+    // the order of the walk kernels' B-operand fragments: element (l, s) of a tile sits
+    // at ((s / 16) * 64 + ((s % 16) / 8) * 32 + l) * 8 + s % 8, so one fragment of one
     // wavefront is 1 KB of contiguous memory.
-    const int g = rest / a.cb_groups;
-    const int t = (rest % a.cb_groups) * 4 + wave;
-    const int nlb = (len + 31) >> 5;
-    if (t >= nlb * (nlb + 1) / 2) return;
-    int i = 0;
-    while ((i + 1) * (i + 2) / 2 <= t) ++i;
-    const int j = t - i * (i + 1) / 2;
-    const T* Bp = static_cast<const T*>(a.B);
-    const T* Cp = static_cast<const T*>(a.C);
-    const bool svalid = 32 * j + lr < len, lvalid = 32 * i + lr < len;
-    const T* brow = Bp + ((rowc + 32 * j + lr) * a.G + g) * (int64_t)a.N + 8 * lg;
-    const T* crow = Cp + ((rowc + 32 * i + lr) * a.G + g) * (int64_t)a.N + 8 * lg;
-    f32x16 acc = {};
-    const int nks = a.N / 16;
-    for (int kb = 0; kb < nks; kb += 8) {
-        frag av[8], bv[8];
+    constexpr int SW = kCbSlab<T>, SS = kCbStride<T>;
+    constexpr int MAXT = 9;   // ceil(36 / 4): tiles per wavefront for 256-row chunks
+    const int g = rest;
+    T* Bs = reinterpret_cast<T*>(smem);
+    T* Cs = Bs + 256 * SS;
+    const char* Bp = static_cast<const char*>(a.B);
+    const char* Cp = static_cast<const char*>(a.C);
+    int ti[MAXT], tj[MAXT];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const bool ok = kb + q < nks;
-            av[q] = (ok && svalid) ? E::ldg8(brow + 16 * (kb + q)) : E::zero();
-            bv[q] = (ok && lvalid) ? E::ldg8(crow + 16 * (kb + q)) : E::zero();
+    for (int u = 0; u < MAXT; ++u) {
+        const int t = wave + 4 * u;
+        int i = 0;
+        while ((i + 1) * (i + 2) / 2 <= t) ++i;
+        ti[u] = i;
+        tj[u] = t - i * (i + 1) / 2;
+    }
+    f32x16 acc[MAXT];
+#pragma unroll
+    for (int u = 0; u < MAXT; ++u) acc[u] = f32x16{};
+    constexpr int pieces = SW * (int)sizeof(T) / 16;   // 16-byte pieces per slab row
+    for (int n0 = 0; n0 < a.N; n0 += SW) {
+        __syncthreads();   // the previous slab has been read
+        for (int idx = tid; idx < a.Qp * pieces; idx += 256) {
+            const int r = idx / pieces, c = (idx % pieces) * (16 / (int)sizeof(T));
+            uint4 vb = {0u, 0u, 0u, 0u}, vc = {0u, 0u, 0u, 0u};
+            // (N is a multiple of 16, so a 16-byte piece is wholly inside or past a row)
+            if (r < len && n0 + c < a.N) {
+                const int64_t off = (((rowc + r) * a.G + g) * (int64_t)a.N + n0 + c) * (int64_t)sizeof(T);
+                vb = *reinterpret_cast<const uint4*>(Bp + off);
+                vc = *reinterpret_cast<const uint4*>(Cp + off);
+            }
+            *reinterpret_cast<uint4*>(Bs + r * SS + c) = vb;
+            *reinterpret_cast<uint4*>(Cs + r * SS + c) = vc;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < MAXT; ++u) {
+            if (wave + 4 * u >= a.ntile) break;
+#pragma unroll
+            for (int ks = 0; ks < SW / 16; ++ks) {
+                const frag av = E::lds8(Bs + (32 * tj[u] + lr) * SS + 16 * ks + 8 * lg);
+                const frag bv = E::lds8(Cs + (32 * ti[u] + lr) * SS + 16 * ks + 8 * lg);
+                acc[u] = E::mma(acc[u], av, bv);
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < MAXT; ++u) {
+        const int t = wave + 4 * u;
+        if (t >= a.ntile) break;
+        T* out = static_cast<T*>(a.cb) + ((int64_t)(k * a.G + g) * a.ntile + t) * 1024;
+        if (ti[u] == tj[u]) {
+            // diagonal tiles carry the causal mask: (C B^T)_{ls} = 0 for s > l
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (acc_row(e, lane) > lr) acc[u][e] = 0.f;
         }
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-            if (kb + q < nks) acc = E::mma(acc, av[q], bv[q]);
-    }
-    T* out = static_cast<T*>(a.cb) + ((int64_t)(k * a.G + g) * a.ntile + t) * 1024;
-    if (i == j) {
-        // diagonal tiles carry the causal mask: (C B^T)_{ls} = 0 for s > l
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-            if (acc_row(e, lane) > lr) acc[e] = 0.f;
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        // rows s = 8q + 4lg + 0..3 of this lane's column l = lr
-        T* o = out + (((q >> 1) * 64 + (q & 1) * 32 + lr) * 8 + 4 * lg);
-        E::st4(o, acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+        for (int q = 0; q < 4; ++q) {
+            // rows s = 8q + 4lg + 0..3 of this lane's column l = lr
+            T* o = out + (((q >> 1) * 64 + (q & 1) * 32 + lr) * 8 + 4 * lg);
+            E::st4(o, acc[u][4 * q], acc[u][4 * q + 1], acc[u][4 * q + 2], acc[u][4 * q + 3]);
+        }
     }
 }
 

@@ -1,0 +1,118 @@
+"""GPU parity of ssd_backward against the float64 adjoint recurrence of the oracle.
+
+For L = <dY, Y> + <dF, final>: dX, dlogA, dB, dC and dinit from the HIP path (three
+forward passes on re-arranged operands plus small kernels) against ``oracle.backward``
+on the same, already quantized, inputs.  Metric per gradient: max|out - ref| / max|ref|.
+Bars: 2e-4 for float32 inputs (the three passes and the cumsum of the decay gradient
+each add float32 rounding to the forward pass's 1e-4), 2e-2 for bfloat16 inputs (the
+forward pass's bar; the per-head partial gradients are rounded to bfloat16 before their
+sum over the heads of a group, as the outputs are).
+
+dlogA is the reverse cumsum of dy . y - x . dx: a difference of two cumulative sums that
+are several times larger than itself (pairs of tokens on the same side of t enter both
+and cancel).  With bfloat16 operands y and dx carry relative errors of a few 1e-3, so
+its error scales with those sums, not with dlogA: for bfloat16 its metric divides by
+max(max|ref|, max_t |sum_{k >= t} dy_k . y_k|) (oracle values).  float32 keeps the plain
+metric and bar, which pins the computation itself.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from workloads import bf16_round, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 2e-4, "bf16": 2e-2}
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def rel_err(out, ref):
+    return float(np.max(np.abs(out - ref))) / max(float(np.max(np.abs(ref))), 1e-30)
+
+
+def cumsum_scale(inp, dY):
+    """max over sequences, heads and tokens t of |sum_{k >= t} dy_k . y_k| (oracle Y)."""
+    Y, _ = oracle.recurrence(inp.X, inp.logA, inp.B, inp.C, inp.init, inp.seq_offsets)
+    r = np.sum(dY.astype(np.float64) * Y, axis=-1).reshape(-1, Y.shape[2])   # [rows, H]
+    b, T = Y.shape[0], Y.shape[1]
+    bounds = ([(s * T, (s + 1) * T) for s in range(b)] if inp.seq_offsets is None
+              else list(zip(inp.seq_offsets[:-1], inp.seq_offsets[1:])))
+    m = 0.0
+    for r0, r1 in bounds:
+        if r1 > r0:
+            m = max(m, float(np.max(np.abs(np.cumsum(r[r0:r1][::-1], axis=0)))))
+    return m
+
+
+def check_backward(inp, Q, label, with_dfinal=True, seed=0):
+    import mamba_ssd_scan_forward_amd as ssd
+    torch = _torch()
+    dt = torch.bfloat16 if inp.dtype == "bf16" else torch.float32
+    q = bf16_round if inp.dtype == "bf16" else (lambda a: a.astype(np.float32))
+    rng = np.random.default_rng(seed)
+    nseq = inp.X.shape[0] if inp.seq_offsets is None else len(inp.seq_offsets) - 1
+    H, P = inp.X.shape[2], inp.X.shape[3]
+    N = inp.B.shape[3]
+    dY = q(rng.standard_normal(inp.X.shape))
+    dF = (rng.standard_normal((nseq, H, P, N)) * 0.5).astype(np.float32) if with_dfinal else None
+    print(f"[backward] {label} X{tuple(inp.X.shape)} G={inp.B.shape[2]} N={N} Q={Q} {inp.dtype} "
+          f"init={inp.init is not None} varlen={inp.seq_offsets is not None} dF={with_dfinal}", flush=True)
+    dev = lambda a, t=dt: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(t).cuda()
+    X, logA, B, C = dev(inp.X), dev(inp.logA, torch.float32), dev(inp.B), dev(inp.C)
+    init = dev(inp.init, torch.float32)
+    off = None if inp.seq_offsets is None else torch.from_numpy(inp.seq_offsets).cuda()
+    Y, F = ssd.forward(X, logA, B, C, Q, init, off)
+    grads = ssd.backward(X, logA, B, C, Q, Y, dev(dY), init, off, F, dev(dF, torch.float32))
+    torch.cuda.synchronize()
+    got = [None if g is None else g.float().cpu().numpy().astype(np.float64) for g in grads]
+    ref = oracle.backward(inp.X, inp.logA, inp.B, inp.C, inp.init, inp.seq_offsets, dY, dF)
+    names = ["dX", "dlogA", "dB", "dC", "dinit"]
+    errs = {}
+    for name, g, r in zip(names, got, ref):
+        if r is None:
+            continue
+        assert np.all(np.isfinite(g)), name
+        errs[name] = rel_err(g, r)
+    if inp.dtype == "bf16":
+        scale = cumsum_scale(inp, dY)
+        errs["dlogA"] = float(np.max(np.abs(got[1] - ref[1]))) / max(float(np.max(np.abs(ref[1]))), scale)
+    print("[backward]   " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert v <= TOL[inp.dtype], (k, v)
+    return got, ref
+
+
+@pytest.mark.parametrize("case", ["layer_shape", "varlen", "f32_general", "bf16_q64", "no_init_no_dfinal",
+                                  "segmented", "headdim128"])
+def test_backward_matches_oracle(case):
+    if case == "layer_shape":
+        inp = make_inputs(2, 600, 4, 64, 128, 2, "bf16", seed=2000, init_state=True)
+        check_backward(inp, 256, case)
+    elif case == "varlen":
+        lens = [5, 0, 300, 1, 256, 257, 33]
+        inp = make_inputs(1, sum(lens), 4, 64, 128, 2, "bf16", seed=2001, init_state=True, seq_lengths=lens)
+        got, ref = check_backward(inp, 256, case)
+        # the empty sequence hands dF straight back as dinit
+        np.testing.assert_allclose(got[4][1], ref[4][1], rtol=0, atol=0)
+    elif case == "f32_general":
+        inp = make_inputs(2, 200, 3, 32, 64, 1, "f32", seed=2002, init_state=True)
+        check_backward(inp, 64, case)
+    elif case == "bf16_q64":
+        inp = make_inputs(1, 300, 2, 64, 64, 1, "bf16", seed=2003, init_state=True)
+        check_backward(inp, 64, case)
+    elif case == "no_init_no_dfinal":
+        inp = make_inputs(2, 400, 2, 64, 128, 1, "bf16", seed=2004)
+        check_backward(inp, 256, case, with_dfinal=False)
+    elif case == "segmented":
+        inp = make_inputs(1, 2100, 4, 64, 128, 1, "bf16", seed=2005, init_state=True)
+        check_backward(inp, 256, case)
+    else:
+        inp = make_inputs(2, 520, 3, 128, 64, 1, "bf16", seed=2006, init_state=True)
+        check_backward(inp, 256, case)

@@ -23,9 +23,9 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["ssd_abi_version", "ssd_check_problem", "ssd_decode_step",
-                                           "ssd_forward", "ssd_forward_stage", "ssd_status_string",
-                                           "ssd_workspace_bytes"])
+    assert declared_functions() == sorted(["ssd_abi_version", "ssd_backward", "ssd_backward_workspace_bytes",
+                                           "ssd_check_problem", "ssd_decode_step", "ssd_forward",
+                                           "ssd_forward_stage", "ssd_status_string", "ssd_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -194,3 +194,43 @@ def test_decode_rejects_null_and_misaligned_pointers(name):
 def test_decode_rejects_aliased_outputs(out, inp):
     assert dcall(dprob(), **{out: DADDR[inp]}) == ssd.SSD_ERR_INVALID_ARG
 
+
+
+# ssd_backward: validation on the host with fake addresses, as above.
+BADDR = dict(ADDR, Yf=10 * GB, dY=11 * GB, dF=12 * GB, dX=13 * GB, dlogA=14 * GB, dB=15 * GB, dC=16 * GB,
+             dinit=17 * GB, bws=18 * GB)
+
+
+def bcall(p, ws_bytes=None, **over):
+    a = dict(BADDR)
+    a.update(over)
+    wsb = ssd.ssd_backward_workspace_bytes(p) if ws_bytes is None else ws_bytes
+    return ssd.ssd_backward(p, a["X"], a["logA"], a["B"], a["C"], a["init"], a["off"], a["Yf"], a["final"],
+                            a["dY"], a["dF"], a["dX"], a["dlogA"], a["dB"], a["dC"], a["dinit"], a["bws"], wsb, None)
+
+
+def test_backward_workspace_covers_the_forward_workspaces():
+    p = prob()
+    q = prob(headdim=128, dstate=64, ngroups=4)   # the transposed problem of p
+    assert ssd.ssd_backward_workspace_bytes(p) > max(ssd.ssd_workspace_bytes(p), ssd.ssd_workspace_bytes(q))
+    assert ssd.ssd_backward_workspace_bytes(prob(nheads=3)) == 0
+
+
+@pytest.mark.parametrize("name", ["X", "logA", "B", "C", "Yf", "dY", "dX", "dlogA", "dB", "dC", "bws"])
+def test_backward_rejects_null_required_pointer(name):
+    assert bcall(prob(), off=None, **{name: None}) == ssd.SSD_ERR_INVALID_ARG
+
+
+def test_backward_needs_final_state_with_dfinal():
+    assert bcall(prob(), off=None, final=None) == ssd.SSD_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("out,inp", [("dX", "X"), ("dB", "dY"), ("dinit", "init"), ("dC", "bws"), ("dB", "dC")])
+def test_backward_rejects_aliased_outputs(out, inp):
+    assert bcall(prob(), off=None, **{out: BADDR[inp]}) == ssd.SSD_ERR_INVALID_ARG
+
+
+def test_backward_rejects_small_workspace_and_misalignment():
+    p = prob()
+    assert bcall(p, ws_bytes=ssd.ssd_backward_workspace_bytes(p) - 256, off=None) == ssd.SSD_ERR_WORKSPACE
+    assert bcall(p, off=None, dlogA=BADDR["dlogA"] + 4) == ssd.SSD_ERR_INVALID_ARG
