@@ -101,6 +101,7 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"])
     args = ap.parse_args()
 
@@ -213,6 +214,36 @@ def main():
                "frac_hbm": round(dbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         log(f"[bench] decode step {us:.2f} us, {dec['achieved_gbs']} GB/s")
 
+    # the backward pass of the same workload (gradients of <dY, Y> + <dF, final>), all
+    # buffers and the workspace allocated before the timed region
+    bwd = None
+    if not args.no_backward:
+        g = torch.Generator(device="cpu").manual_seed(6)
+        dYb = torch.randn(Y.shape, generator=g).to(dt).to(dev)
+        dFb = torch.randn(final.shape, generator=g).to(dev)
+        outs = [torch.empty_like(X), torch.empty_like(logA), torch.empty_like(B), torch.empty_like(C),
+                torch.empty_like(final)]
+        bwsb = ssd.ssd_backward_workspace_bytes(prob)
+        bws = torch.empty(bwsb, dtype=torch.uint8, device=dev)
+        bptr = [X.data_ptr(), logA.data_ptr(), B.data_ptr(), C.data_ptr(),
+                None if init is None else init.data_ptr(), None if off is None else off.data_ptr(),
+                Y.data_ptr(), final.data_ptr(), dYb.data_ptr(), dFb.data_ptr()] + [o.data_ptr() for o in outs] + \
+               [bws.data_ptr(), bwsb, sp]
+        for _ in range(2):
+            assert ssd.ssd_backward(prob, *bptr) == 0
+        torch.cuda.synchronize()
+        nb = max(3, args.steps // 5)
+        e0.record(stream)
+        for _ in range(nb):
+            ssd.ssd_backward(prob, *bptr)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / nb
+        bwd = {"us_per_step": round(us, 1), "tokens_per_s": round(w.batch * w.seqlen / (us * 1e-6), 1),
+               "vs_forward_step": round(us / (ms_step * 1e3), 2)}
+        log(f"[bench] backward {us:.1f} us")
+        del outs, bws
+
     lens = [w.seqlen] * w.batch if not w.varlen else list(np.diff(inp.seq_offsets))
     tokens = w.batch * w.seqlen
     fl = flops_pages(w, chunk_lengths(w, [int(v) for v in lens]))
@@ -261,6 +292,8 @@ def main():
 
     if dec is not None:
         result["decode"] = dec
+    if bwd is not None:
+        result["backward"] = bwd
 
     if not args.no_cpu_baseline:
         import oracle
