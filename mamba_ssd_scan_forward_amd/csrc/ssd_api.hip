@@ -28,8 +28,9 @@ struct Plan {
     size_t cs_off, cb_off, bt_off, ct_off, ws_bytes;
     int lds_bytes, xs_off, xts_off, bs_off, hs_off, cs_lds_off;
     int split;        // the split-role walker (bf16, 256-row chunks, d_state 64 / 128)
-    int nseg;         // segments per sequence of a batch without seq_offsets
+    int nseg;         // segments per segmented sequence of a batch without seq_offsets
     int nsplit;       // summary parts per segment
+    int64_t ntail;    // items walked in segments: the last ones
     int summary_lds;
     size_t seg_off, segd_off;
     walk_fn_t walk;   // the walk kernel instance for this plan
@@ -145,19 +146,25 @@ int make_plan(const ssd_problem* p, Plan* pl) {
     const size_t bt_bytes = pl->split ? (size_t)pl->nslots * p->ngroups * ssd::split_bt_bytes(N) : 0;
     pl->ct_off = align_up(pl->bt_off + bt_bytes, 256);
     pl->seg_off = align_up(pl->ct_off + bt_bytes, 256);   // C fragments: as many bytes as B^T
-    // Segmented walk: when the (sequence, head, P tile) items of a batch cannot fill the
-    // 256 compute units of the part, each sequence is walked as nseg segments of at
-    // least 4 chunks, after a pass that sums up every segment but the last, in parts
-    // of at least 2 chunks, about two summary workgroups per compute unit.
+    // Segmented walk: the (sequence, head, P tile) items of a batch run one workgroup per
+    // CU.  The items of the last round, when they are too few to fill the 256 compute
+    // units of the part (all items, for a small batch), are walked as nseg segments of
+    // at least 8 chunks each, after a pass that sums up every segment but the last in
+    // parts of at least 2 chunks, about two summary workgroups per compute unit.  (A
+    // summary part costs about half a walked chunk and its first loads are exposed, so
+    // segments shorter than 8 chunks do not pay back.)
     pl->nseg = 1;
     pl->nsplit = 1;
+    pl->ntail = 0;
     if (pl->split) {
         const int64_t items = p->nseq * p->nheads * (P / 64);
-        int64_t k = kComputeUnits / items;
-        if (k > nc / 4) k = nc / 4;
+        const int64_t tail = items % kComputeUnits;
+        int64_t k = tail > 0 ? kComputeUnits / tail : 1;
+        if (k > nc / 8) k = nc / 8;
         if (k > 1) {
             pl->nseg = (int)k;
-            int64_t m = 2 * kComputeUnits / (items * (k - 1));
+            pl->ntail = tail;
+            int64_t m = 2 * kComputeUnits / (tail * (k - 1));
             if (m > nc / k / 2) m = nc / k / 2;
             pl->nsplit = m > 1 ? (int)m : 1;
         }
@@ -369,13 +376,15 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
     wa.cs_off = pl.cs_lds_off;
     wa.nseg = nseg;
     wa.nsplit = pl.nsplit;
+    wa.ntail = nseg > 1 ? (int)pl.ntail : 0;
+    wa.nwhole = (int)(pl.nitems - wa.ntail);
     wa.seg_state = reinterpret_cast<float*>(ws + pl.seg_off);
     wa.seg_decay = reinterpret_cast<float*>(ws + pl.segd_off);
     if ((stages & 2) && nseg > 1) {
-        wa.nitems = (int)(pl.nitems * (nseg - 1) * pl.nsplit);
+        wa.nitems = wa.ntail * (nseg - 1) * pl.nsplit;
         hipLaunchKernelGGL(pl.summary, dim3((unsigned)wa.nitems), dim3(kWalkThreads / 2), pl.summary_lds, stream, wa);
     }
-    wa.nitems = (int)(pl.nitems * nseg);
+    wa.nitems = wa.nwhole + wa.ntail * nseg;
     if (stages & 2)
         hipLaunchKernelGGL(walk, dim3((unsigned)wa.nitems), dim3(kWalkThreads), pl.lds_bytes, stream, wa);
     if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;

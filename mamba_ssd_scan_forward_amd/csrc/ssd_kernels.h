@@ -65,8 +65,9 @@ struct WalkArgs {
     const void* ct;   // C fragments (split-role walker only)
     float* seg_state;   // segmented walk: [nseq][nseg - 1][nsplit][H][P][N] float32
     float* seg_decay;   // states of the summed-up parts and their total log2 decays
-    int nseg;           // segments per sequence (1 unless the split walker segments)
+    int nseg;           // segments per segmented sequence (1: none is segmented)
     int nsplit;         // summary parts per segment
+    int nwhole, ntail;  // items walked whole, then items walked in nseg segments
     int64_t T;
     int H, P, N, G, Q, Qp, ntile, nseq, ptiles, nitems, qb;
     int cb_lds;                                    // stage off-diagonal C B^T tiles in LDS

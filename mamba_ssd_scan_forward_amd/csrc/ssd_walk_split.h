@@ -75,6 +75,7 @@ __host__ __device__ constexpr int split_bt_bytes(int N) { return N * 512; }
 // per (sequence, segment, head, P tile), so that few sequences still fill the chip.
 // This is the chunk recurrence h_{c+1} = a_c h_c + S_c taken two levels deep, as in a
 // scan over an associative operator on pairs (a, S):
+// (Only some items may be segmented: those of the last, partial round of workgroups.)
 //   SUMMARY = true : every segment but the last is cut into nsplit parts; for each part
 //                    the state waves alone walk its chunks from a zero state and store
 //                    that state and the part's total log2 decay (256 threads per
@@ -101,19 +102,37 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
     // the wavefront index is uniform: keep it (and every role offset) in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int item = xcd_remap(blockIdx.x, gridDim.x);
+    // The whole items and the segments of the tail are remapped to XCDs separately, so
+    // that every XCD gets its share of both (dispatch follows the block index).
+    const int bid = blockIdx.x;
+    const int item = (SUMMARY || a.nwhole == 0) ? xcd_remap(bid, gridDim.x)
+                     : bid < a.nwhole ? xcd_remap(bid, a.nwhole)
+                                      : a.nwhole + xcd_remap(bid - a.nwhole, gridDim.x - a.nwhole);
     if (item >= a.nitems) return;
-    // item = ((s * nseg + segment) * H + h) * ptiles + pt for the walk and
-    // (((s * (nseg - 1) + segment) * nsplit + part) * H + h) * ptiles + pt for the
-    // summaries: the heads of one stretch of chunks sit next to each other (one XCD,
-    // one L2)
-    const int pt = item % a.ptiles;
-    const int sk = item / a.ptiles / a.H;
-    const int h = item / a.ptiles % a.H;
-    const int part = SUMMARY ? sk % a.nsplit : 0;
-    const int skk = SUMMARY ? sk / a.nsplit : sk;
-    const int nsk = SUMMARY ? a.nseg - 1 : a.nseg;
-    const int s = skk / nsk, seg = skk % nsk;
+    // Work items are the (sequence, head, P tile) triples, gi = (s * H + h) * ptiles + pt.
+    // The first nwhole walk their whole sequence; each of the other ntail is walked as
+    // nseg segments, so that the last round of workgroups still fills the chip.  The walk
+    // launch has nwhole + ntail * nseg workgroups (the tail segment-major), the summary
+    // launch ntail * (nseg - 1) * nsplit ((segment, part)-major): consecutive workgroups
+    // of an XCD share one stretch of chunks and its B, C and C B^T in L2.
+    int gi, seg = 0, part = 0, nseg = 1;
+    if (SUMMARY) {
+        gi = a.nwhole + item % a.ntail;
+        const int sp = item / a.ntail;
+        part = sp % a.nsplit;
+        seg = sp / a.nsplit;
+        nseg = a.nseg;
+    } else if (item < a.nwhole) {
+        gi = item;
+    } else {
+        const int u = item - a.nwhole;
+        gi = a.nwhole + u % a.ntail;
+        seg = u / a.ntail;
+        nseg = a.nseg;
+    }
+    const int pt = gi % a.ptiles;
+    const int h = gi / a.ptiles % a.H;
+    const int s = gi / a.ptiles / a.H;
     const int g = h / (a.H / a.G);
     const int p_base = pt * 64;
     const int H = a.H, P = a.P, N = a.N, G = a.G;
@@ -130,11 +149,11 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
         slot0 = 0;
         for (int u = 0; u < s; ++u) slot0 += (a.seq_offsets[u + 1] - a.seq_offsets[u] + 255) / 256;
     }
-    if (a.nseg > 1) {
+    if (nseg > 1) {
         // segments of a batch without seq_offsets: chunks [c0, c1) of sequence s; every
         // segment but the last holds whole chunks only
         const int nc = (len_seq + 255) / 256;
-        int c0 = (int)((int64_t)seg * nc / a.nseg), c1 = (int)((int64_t)(seg + 1) * nc / a.nseg);
+        int c0 = (int)((int64_t)seg * nc / nseg), c1 = (int)((int64_t)(seg + 1) * nc / nseg);
         if (SUMMARY) {
             const int l = c1 - c0;
             c1 = c0 + (part + 1) * l / a.nsplit;
@@ -421,7 +440,7 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
             __syncthreads();   // B_end
             store_y(c, 0);
         }
-        if (a.final_state && seg == a.nseg - 1) put_state(a.final_state + state_base);
+        if (a.final_state && seg == nseg - 1) put_state(a.final_state + state_base);
     } else if constexpr (!SUMMARY) {
         // ========================================================== output waves
         // The two blocks are done one after the other, the later one (longer chain)

@@ -111,7 +111,7 @@ def test_backward_matches_oracle(case):
         inp = make_inputs(2, 400, 2, 64, 128, 1, "bf16", seed=2004)
         check_backward(inp, 256, case, with_dfinal=False)
     elif case == "segmented":
-        inp = make_inputs(1, 2100, 4, 64, 128, 1, "bf16", seed=2005, init_state=True)
+        inp = make_inputs(1, 4200, 4, 64, 128, 1, "bf16", seed=2005, init_state=True)
         check_backward(inp, 256, case)
     else:
         inp = make_inputs(2, 520, 3, 128, 64, 1, "bf16", seed=2006, init_state=True)

@@ -192,21 +192,26 @@ def test_layer_shape_walker_edges(case):
 # Few long sequences: each is walked as several segments of chunks (a first pass sums
 # up every segment but the last; each segment then starts from the combined state).
 # The plan picks the segment count from the number of (sequence, head, P tile) items and
-# chunks: 2 here for 8 items and 9 chunks, 3 for 4 items and 12 chunks.
-@pytest.mark.parametrize("case", ["two_segments", "three_segments_mixed", "a_one", "strong_decay"])
+# chunks (at least 8 chunks per segment): 2 here for 9 to 23 chunks, 3 for 24 or more.
+@pytest.mark.parametrize("case", ["two_segments", "three_segments_mixed", "a_one", "strong_decay",
+                                  "partial_tail"])
 def test_segmented_walk(case):
-    if case == "two_segments":
-        inp = make_inputs(2, 2100, 4, 64, 128, 2, "bf16", seed=1200, init_state=True)
+    if case == "partial_tail":
+        # 260 items (P = 128: two tiles per head): the first 256 walk whole, the last 4
+        # in two segments each
+        inp = make_inputs(2, 4096, 65, 128, 64, 1, "bf16", seed=1204, init_state=True)
+    elif case == "two_segments":
+        inp = make_inputs(2, 4100, 4, 64, 128, 2, "bf16", seed=1200, init_state=True)
     elif case == "three_segments_mixed":
-        inp = make_inputs(1, 3000, 2, 128, 64, 1, "bf16", seed=1201, init_state=True)
-        for t0 in (100, 1030, 2300):
+        inp = make_inputs(1, 6200, 2, 128, 64, 1, "bf16", seed=1201, init_state=True)
+        for t0 in (100, 2030, 4300):
             inp.logA[:, t0:t0 + 3, :] = -30.0
-        inp.logA[0, 1800, 1] = -70.0
+        inp.logA[0, 3800, 1] = -70.0
     elif case == "a_one":
-        inp = make_inputs(1, 2048, 2, 64, 128, 1, "bf16", seed=1202, init_state=True)
+        inp = make_inputs(1, 4096, 2, 64, 128, 1, "bf16", seed=1202, init_state=True)
         inp.logA[:] = 0.0
     else:
-        inp = make_inputs(1, 2048, 2, 64, 64, 1, "bf16", seed=1203, init_state=True)
+        inp = make_inputs(1, 4096, 2, 64, 64, 1, "bf16", seed=1203, init_state=True)
         inp.logA[:] = -1e4
     check(inp, 256, "segmented " + case)
 
@@ -215,10 +220,10 @@ def test_segmented_walk_matches_whole_walk():
     """The same sequence as a batch of one (segmented) and as one packed sequence
     (walked whole): both within the bar of each other."""
     import copy
-    inp = make_inputs(1, 2600, 4, 64, 128, 1, "bf16", seed=1210, init_state=True)
+    inp = make_inputs(1, 4200, 4, 64, 128, 1, "bf16", seed=1210, init_state=True)
     Y1, F1 = run_gpu(inp, 256)
     packed = copy.deepcopy(inp)
-    packed.seq_offsets = np.array([0, 2600], dtype=np.int32)
+    packed.seq_offsets = np.array([0, 4200], dtype=np.int32)
     Y2, F2 = run_gpu(packed, 256)
     assert rel_err(Y1, Y2) <= 2e-2 and rel_err(F1, F2) <= 2e-2
 
