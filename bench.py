@@ -17,7 +17,6 @@ counter summary when it was taken on the current kernel source, else null.
 program for the FETCH_SIZE / WRITE_SIZE counters.
 """
 import argparse
-import glob
 import hashlib
 import json
 import os
@@ -39,10 +38,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# the sources of the forward kernels and of their launch plan (the backward pass's files
+# are not among them)
+FORWARD_SOURCES = ("ssd_device.h", "ssd_kernels.h", "ssd_walk_split.h", "ssd_api.hip")
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "mamba_ssd_scan_forward_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
+    for name in FORWARD_SOURCES:
+        with open(os.path.join(ROOT, "mamba_ssd_scan_forward_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -50,7 +54,7 @@ def kernel_source_hash():
 def walk_kernel_name(w):
     """The walk kernel that the library's planner picks for this workload."""
     if w.dtype == "bf16" and w.chunk_len == 256 and w.dstate in (64, 128) and w.headdim % 64 == 0:
-        return f"ssd_walk_split_kernel<{w.dstate}>"
+        return f"ssd_walk_split_kernel<{w.dstate}, false>"
     return "ssd_walk_kernel"
 
 
