@@ -378,6 +378,7 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
     wa.nsplit = pl.nsplit;
     wa.ntail = nseg > 1 ? (int)pl.ntail : 0;
     wa.nwhole = (int)(pl.nitems - wa.ntail);
+    wa.lpt = (pl.split && seq_offsets && p->nseq <= 64 && (p->nseq * G) % 8 == 0) ? 1 : 0;
     wa.seg_state = reinterpret_cast<float*>(ws + pl.seg_off);
     wa.seg_decay = reinterpret_cast<float*>(ws + pl.segd_off);
     if ((stages & 2) && nseg > 1) {

@@ -68,6 +68,7 @@ struct WalkArgs {
     int nseg;           // segments per segmented sequence (1: none is segmented)
     int nsplit;         // summary parts per segment
     int nwhole, ntail;  // items walked whole, then items walked in nseg segments
+    int lpt;            // packed sequences: (sequence, group) units dealt to XCDs longest first
     int64_t T;
     int H, P, N, G, Q, Qp, ntile, nseq, ptiles, nitems, qb;
     int cb_lds;                                    // stage off-diagonal C B^T tiles in LDS

@@ -130,6 +130,31 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
         seg = u / a.ntail;
         nseg = a.nseg;
     }
+    if (!SUMMARY && a.lpt) {
+        // Packed sequences of different lengths: the units (sequence, group) are dealt to
+        // the XCDs round-robin, longest sequence first, each XCD taking its units in that
+        // order.  Every XCD gets an equal share of every length (the contiguous ranges
+        // above would give one XCD all heads of a long sequence), and the heads of a
+        // group, which share B, C and C B^T, stay on one XCD.
+        const int ipu = a.H / a.G * a.ptiles;              // items per unit
+        const int xcd = bid % 8, slot = bid / 8;
+        const int u = (slot / ipu) * 8 + xcd, within = slot % ipu;
+        const int r = u / a.G, gg = u % a.G;
+        // the sequence of length rank r (longest first, ties by index): one lane per sequence
+        const int* off = a.seq_offsets;
+        bool mine = false;
+        if (lane < a.nseq) {
+            const int L = off[lane + 1] - off[lane];
+            int rank = 0;
+            for (int v = 0; v < a.nseq; ++v) {
+                const int Lv = off[v + 1] - off[v];
+                rank += (Lv > L) || (Lv == L && v < lane);
+            }
+            mine = rank == r;
+        }
+        const int sr = __builtin_ctzll(__ballot(mine));
+        gi = (sr * a.H + gg * (a.H / a.G)) * a.ptiles + within;
+    }
     const int pt = gi % a.ptiles;
     const int h = gi / a.ptiles % a.H;
     const int s = gi / a.ptiles / a.H;

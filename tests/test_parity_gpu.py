@@ -156,9 +156,17 @@ def test_bitwise_repeatable():
 
 # The common layer shapes (bf16, 256-row chunks, d_state 64 or 128, head dimension a
 # multiple of 64) run on their own walker; these cases reach its edges.
-@pytest.mark.parametrize("case", ["varlen", "strong_decay", "mixed_decay", "headdim128", "one_chunk_n64", "a_one"])
+@pytest.mark.parametrize("case", ["varlen", "varlen_ties", "strong_decay", "mixed_decay", "headdim128",
+                                  "one_chunk_n64", "a_one"])
 def test_layer_shape_walker_edges(case):
-    if case == "varlen":
+    if case == "varlen_ties":
+        # packed sequences dealt to XCDs longest first: equal lengths, an empty one
+        lens = [300, 300, 5, 0, 300, 77, 256, 1]
+        inp = make_inputs(1, sum(lens), 3, 64, 128, 1, "bf16", seed=1006, init_state=True,
+                          seq_lengths=lens)
+        Y, F = check(inp, 256, case)
+        np.testing.assert_array_equal(F[3], inp.init[3].astype(np.float64))
+    elif case == "varlen":
         lens = [5, 0, 300, 1, 256, 257, 600, 33]
         inp = make_inputs(1, sum(lens), 4, 64, 128, 2, "bf16", seed=1000, init_state=True,
                           seq_lengths=lens)
