@@ -339,7 +339,7 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
     pa.cb_blocks = (int)(nslots * G);
     pa.bt = pl.split ? ws + pl.bt_off : nullptr;
     pa.ct = pl.split ? ws + pl.ct_off : nullptr;
-    const int64_t prep_blocks = nslots * pa.hblocks + nslots * G + (pl.split ? nslots * G * 8 : 0);
+    const int64_t prep_blocks = nslots * pa.hblocks + nslots * G;
     if (prep_blocks > INT32_MAX) return SSD_ERR_UNSUPPORTED;
     if (stages & 1)
         hipLaunchKernelGGL(prep, dim3((unsigned)prep_blocks), dim3(kPrepThreads), 0, stream, pa);

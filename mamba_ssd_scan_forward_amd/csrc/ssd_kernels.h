@@ -48,7 +48,7 @@ struct PrepArgs {
     void* bt;         // optional: B^T of every 256-row chunk in MFMA A-operand fragment
                       // order, [nslots, G, N/32, 8, 2, 64 lanes, 8], and
     void* ct;         // C in MFMA B-operand fragment order, [nslots, G, 8, N/16, 64 lanes,
-                      // 8]; workgroups nslots * G * 8 follow the C B^T role
+                      // 8]; written by the C B^T role (bf16 only)
 };
 
 struct WalkArgs {
@@ -151,15 +151,10 @@ __global__ void __launch_bounds__(256, 2) ssd_prep_kernel(PrepArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lg = lane >> 5;
     int bid = blockIdx.x;
     const bool cs_role = bid < a.cs_blocks;
-    const bool bt_role = !cs_role && bid >= a.cs_blocks + a.cb_blocks;
     int k, rest;
     if (cs_role) {
         k = bid / a.hblocks;
         rest = bid % a.hblocks;
-    } else if (bt_role) {
-        bid -= a.cs_blocks + a.cb_blocks;
-        k = bid / (a.G * 8);
-        rest = bid % (a.G * 8);
     } else {
         bid -= a.cs_blocks;
         k = bid / a.G;
@@ -168,43 +163,6 @@ __global__ void __launch_bounds__(256, 2) ssd_prep_kernel(PrepArgs a) {
     int64_t rowc;
     int len;
     if (!locate_chunk(k, a.seq_offsets, a.T, a.Q, a.nseq, &rowc, &len)) return;
-
-    if (bt_role) {
-        // (c) B^T of 32-row block j of the chunk for the split-role walker: rows staged
-        //     in LDS (zero past the chunk), then written as A-operand fragments, fragment
-        //     (nt, ks) lane (lr, lg) holding B[32 j + 16 ks + 8 lg + q][32 nt + lr].
-        const int g = rest >> 3, j = rest & 7;
-        const T* Bp = static_cast<const T*>(a.B);
-        T* tile = reinterpret_cast<T*>(&lt[0][0]);   // [32][N]
-        const int useg = a.N / 8;
-        for (int u = tid; u < 32 * useg; u += 256) {
-            const int r = u / useg, c8 = (u % useg) * 8;
-            const int row = 32 * j + r;
-            const frag v = row < len ? E::ldg8(Bp + ((rowc + row) * a.G + g) * (int64_t)a.N + c8) : E::zero();
-            *reinterpret_cast<frag*>(tile + r * a.N + c8) = v;
-        }
-        __syncthreads();
-        const int ntn = a.N / 32;
-        T* out = static_cast<T*>(a.bt) + (int64_t)(k * a.G + g) * ntn * 16 * 512;
-        for (int o = tid; o < ntn * 128; o += 256) {
-            const int ln = o & 63, ks = (o >> 6) & 1, nt = o >> 7;
-            frag v;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = tile[(16 * ks + 8 * (ln >> 5) + q) * a.N + 32 * nt + (ln & 31)];
-            *reinterpret_cast<frag*>(out + ((nt * 8 + j) * 2 + ks) * 512 + ln * 8) = v;
-        }
-        // C rows of the same block as B-operand fragments: fragment (j, ks) lane (lr, lg)
-        // holds C[32 j + lr][16 ks + 8 lg + q], so one fragment is 1 KB of contiguous memory
-        const T* Cp = static_cast<const T*>(a.C);
-        T* cout = static_cast<T*>(a.ct) + ((int64_t)(k * a.G + g) * 8 + j) * (a.N / 16) * 512;
-        for (int o = tid; o < (a.N / 16) * 64; o += 256) {
-            const int ln = o & 63, ks = o >> 6;
-            const int row = 32 * j + (ln & 31);
-            const frag v = row < len ? E::ldg8(Cp + ((rowc + row) * a.G + g) * (int64_t)a.N + 16 * ks + 8 * (ln >> 5)) : E::zero();
-            *reinterpret_cast<frag*>(cout + o * 8) = v;
-        }
-        return;
-    }
 
     if (cs_role) {
         // (a) a Qp x 16 block of logA (tokens x heads) through LDS with coalesced loads,
@@ -287,6 +245,27 @@ __global__ void __launch_bounds__(256, 2) ssd_prep_kernel(PrepArgs a) {
             *reinterpret_cast<uint4*>(Cs + r * SS + c) = vc;
         }
         __syncthreads();
+        if constexpr (sizeof(T) == 2) {
+            if (a.bt) {
+                // (c) for the split walker (256-row chunks, this slab = n tile n0 / 32): B^T
+                //     as A-operand fragments, (nt, j, ks) lane (lr, lg) holding
+                //     B[32 j + 16 ks + 8 lg + q][32 nt + lr], and C as B-operand fragments,
+                //     (j, ks) lane (lr, lg) holding C[32 j + lr][16 ks + 8 lg + q]: one
+                //     fragment is 1 KB of contiguous memory
+                const int nt = n0 / 32;
+                T* bto = static_cast<T*>(a.bt) + (int64_t)(k * a.G + g) * (a.N / 32) * 16 * 512;
+                T* cto = static_cast<T*>(a.ct) + (int64_t)(k * a.G + g) * 8 * (a.N / 16) * 512;
+                for (int o = tid; o < 16 * 64; o += 256) {
+                    const int ln = o & 63, f = o >> 6, j = f >> 1, ks = f & 1;
+                    frag v;
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) v[q] = Bs[(32 * j + 16 * ks + 8 * (ln >> 5) + q) * SS + (ln & 31)];
+                    *reinterpret_cast<frag*>(bto + ((nt * 8 + j) * 2 + ks) * 512 + ln * 8) = v;
+                    const frag w = E::lds8(Cs + (32 * j + (ln & 31)) * SS + 16 * ks + 8 * (ln >> 5));
+                    *reinterpret_cast<frag*>(cto + (j * (a.N / 16) + n0 / 16 + ks) * 512 + ln * 8) = w;
+                }
+            }
+        }
 #pragma unroll
         for (int u = 0; u < MAXT; ++u) {
             if (wave + 4 * u >= a.ntile) break;
