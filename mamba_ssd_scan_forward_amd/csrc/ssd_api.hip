@@ -264,10 +264,12 @@ size_t ssd_workspace_bytes(const ssd_problem* p) {
 
 namespace {
 
-// stages: bit 0 = prep launch, bit 1 = walk launch
+// stages: bit 0 = prep launch, bit 1 = walk launch.  x_heads: X rows per token (the
+// heads share them in contiguous runs of H / x_heads); 0 means one per head.
 int run_forward(int stages, const ssd_problem* p, const void* X, const float* logA, const void* B,
                 const void* C, const float* init_state, const int32_t* seq_offsets, void* Y,
-                float* final_state, void* workspace, size_t workspace_bytes, void* hip_stream) {
+                float* final_state, void* workspace, size_t workspace_bytes, void* hip_stream,
+                int64_t x_heads = 0) {
     Plan pl;
     int rc = make_plan(p, &pl);
     if (rc != SSD_OK) return rc;
@@ -284,14 +286,16 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
     const size_t es = p->dtype == SSD_DTYPE_BF16 ? 2 : 4;
     const int64_t b = p->batch, T = p->seqlen, H = p->nheads, P = p->headdim, N = p->dstate,
                   G = p->ngroups;
-    const size_t nx = (size_t)(b * T * H * P) * es;
+    if (x_heads == 0) x_heads = H;
+    if (x_heads < 1 || H % x_heads != 0) return SSD_ERR_INVALID_ARG;
+    const size_t nx = (size_t)(b * T * H * P) * es, nxin = (size_t)(b * T * x_heads * P) * es;
     const size_t na = (size_t)(b * T * H) * sizeof(float);
     const size_t nbc = (size_t)(b * T * G * N) * es;
     const size_t ns = (size_t)(p->nseq * H * P * N) * sizeof(float);
     const size_t no = seq_offsets ? (size_t)(p->nseq + 1) * sizeof(int32_t) : 0;
     // outputs must not overlap inputs, each other or the workspace
     const void* ins[] = {X, logA, B, C, init_state, seq_offsets, workspace};
-    const size_t nin[] = {nx, na, nbc, nbc, init_state ? ns : 0, no, workspace_bytes};
+    const size_t nin[] = {nxin, na, nbc, nbc, init_state ? ns : 0, no, workspace_bytes};
     for (int i = 0; i < 7; ++i) {
         if (overlap(Y, nx, ins[i], nin[i])) return SSD_ERR_INVALID_ARG;
         if (final_state && overlap(final_state, ns, ins[i], nin[i])) return SSD_ERR_INVALID_ARG;
@@ -374,6 +378,7 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
     wa.bs_off = pl.bs_off;
     wa.hs_off = pl.hs_off;
     wa.cs_off = pl.cs_lds_off;
+    wa.xh = (int)x_heads;
     wa.nseg = nseg;
     wa.nsplit = pl.nsplit;
     wa.ntail = nseg > 1 ? (int)pl.ntail : 0;

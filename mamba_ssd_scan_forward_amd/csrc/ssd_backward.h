@@ -12,10 +12,10 @@
 //   dX, dinit: time reversed within every sequence, X' = dY, B' = C, C' = B, the
 //              decays shifted by one token (logA'_0 = 0, logA'_j = logA_{len-j}), the
 //              initial state dF: Y' is dX reversed, the final state is G_0;
-//   dB:        time reversed, X' = C (each head its group's row), B' = dY, C' = X,
-//              initial state dF^T: Y' reversed is dB per head;
-//   dC:        forward time, X' = B per head, B' = X, C' = dY, initial state init^T:
-//              Y' is dC per head;
+//   dB:        time reversed, X' = C (the heads of a group read its row), B' = dY,
+//              C' = X, initial state dF^T: Y' reversed is dB per head;
+//   dC:        forward time, X' = B (read per group), B' = X, C' = dY, initial state
+//              init^T: Y' is dC per head;
 // then per-group sums over heads.  The decay gradient uses the identity
 //     dL/dcs_k = dy_k . y_k - x_k . dx_k  (+ <dF, final> at a sequence's last token)
 // for the inclusive cumsum cs of logA, and dlogA_t = sum_{k >= t} dL/dcs_k.

@@ -11,7 +11,7 @@ struct BwdPlan {
     ssd_problem p1;   // dX pass: the layer's own shape
     ssd_problem p2;   // dB and dC passes: head dimension N, state P, one group per head
     size_t fws_bytes;
-    size_t la, revdy, revc, revb, tmpp, rr, xn, revx, tmpn, st, bytes;
+    size_t la, revdy, revc, revb, tmpp, rr, revx, tmpn, st, bytes;
 };
 
 int make_bwd_plan(const ssd_problem* p, BwdPlan* bp) {
@@ -42,7 +42,6 @@ int make_bwd_plan(const ssd_problem* p, BwdPlan* bp) {
     bp->revb = take(rows * G * N * es);
     bp->tmpp = take(rows * H * P * es);
     bp->rr = take(rows * H * 4);
-    bp->xn = take(rows * H * N * es);
     bp->revx = take(rows * H * P * es);
     bp->tmpn = take(rows * H * N * es);
     bp->st = take(ns * H * P * N * 4);
@@ -114,12 +113,11 @@ int ssd_backward(const ssd_problem* p, const void* X, const float* logA, const v
     void* revb = ws + bp.revb;
     void* tmpp = ws + bp.tmpp;
     float* rr = reinterpret_cast<float*>(ws + bp.rr);
-    void* xn = ws + bp.xn;
     void* revx = ws + bp.revx;
     void* tmpn = ws + bp.tmpn;
     float* st = reinterpret_cast<float*>(ws + bp.st);
     const ssd::RowMap fwd{seq_offsets, T, (int)nseq, 0}, rev{seq_offsets, T, (int)nseq, 1};
-    const int segx = (int)(H * P * es / 16), segbc = (int)(G * N * es / 16), segn = (int)(N * es / 16);
+    const int segx = (int)(H * P * es / 16), segbc = (int)(G * N * es / 16);
     auto remap = [&](const void* in, void* out, int K, int Kin, int seg, const ssd::RowMap& m) {
         hipLaunchKernelGGL(ssd::ssd_bwd_remap_kernel, dim3(grid_for(rows * K * seg)), dim3(256), 0, stream,
                            static_cast<const uint4*>(in), static_cast<uint4*>(out), rows, K, Kin, seg, m);
@@ -163,19 +161,18 @@ int ssd_backward(const ssd_problem* p, const void* X, const float* logA, const v
                            static_cast<const float*>(X), static_cast<const float*>(dX), rr, rows, (int)H, (int)P);
     hipLaunchKernelGGL(ssd::ssd_bwd_dlogA_kernel, dim3((unsigned)(nseq * H)), dim3(64), 0, stream, rr, dfinal,
                        final_state, dlogA, T, seq_offsets, (int)H, (int)(P * N));
-    // dB: reversed, X' = C per head, B' = dY, C' = X, initial state dF^T
-    remap(C, xn, (int)H, (int)G, segn, rev);
+    // dB: reversed, X' = C (the reversed copy of the dX pass, read per group), B' = dY,
+    // C' = X, initial state dF^T
     remap(X, revx, 1, 1, segx, rev);
     if (dfinal) transpose(dfinal, st);
-    rc = run_forward(3, &bp.p2, xn, la, revdy, revx, dfinal ? st : nullptr, seq_offsets, tmpn, nullptr, ws,
-                     bp.fws_bytes, hip_stream);
+    rc = run_forward(3, &bp.p2, revc, la, revdy, revx, dfinal ? st : nullptr, seq_offsets, tmpn, nullptr, ws,
+                     bp.fws_bytes, hip_stream, G);
     if (rc != SSD_OK) return rc;
     group_sum(tmpn, dB, rev);
-    // dC: forward time, X' = B per head, B' = X, C' = dY, initial state init^T
-    remap(B, xn, (int)H, (int)G, segn, fwd);
+    // dC: forward time, X' = B (read per group), B' = X, C' = dY, initial state init^T
     if (init_state) transpose(init_state, st);
-    rc = run_forward(3, &bp.p2, xn, logA, X, dY, init_state ? st : nullptr, seq_offsets, tmpn, nullptr, ws,
-                     bp.fws_bytes, hip_stream);
+    rc = run_forward(3, &bp.p2, B, logA, X, dY, init_state ? st : nullptr, seq_offsets, tmpn, nullptr, ws,
+                     bp.fws_bytes, hip_stream, G);
     if (rc != SSD_OK) return rc;
     group_sum(tmpn, dC, fwd);
     if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;

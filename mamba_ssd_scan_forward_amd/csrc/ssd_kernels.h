@@ -69,6 +69,7 @@ struct WalkArgs {
     int nsplit;         // summary parts per segment
     int nwhole, ntail;  // items walked whole, then items walked in nseg segments
     int lpt;            // packed sequences: (sequence, group) units dealt to XCDs longest first
+    int xh;             // X rows per token: H (one per head), or fewer, shared by H / xh heads
     int64_t T;
     int H, P, N, G, Q, Qp, ntile, nseq, ptiles, nitems, qb;
     int cb_lds;                                    // stage off-diagonal C B^T tiles in LDS
@@ -401,6 +402,7 @@ __global__ void __launch_bounds__(512) ssd_walk_kernel(WalkArgs a) {
     const T* Cg = static_cast<const T*>(a.C);
     T* Y = static_cast<T*>(a.Y);
     const int64_t state_base = ((int64_t)s * H + h) * P * (int64_t)N;
+    const int XH = a.xh, xhi = h / (H / XH);   // X row of this head
 
     // ---- state h (P tile x N) in accumulators: wave owns tiles wave, wave + 8, ...
     //      tile t -> (n tile t / PSUB, p sub-tile t % PSUB); element i is (n, p) =
@@ -451,7 +453,7 @@ __global__ void __launch_bounds__(512) ssd_walk_kernel(WalkArgs a) {
     float pcs;
     constexpr uint32_t ES = sizeof(T);
     auto x_rsrc = [&](int64_t rowc, int len) {
-        return make_rsrc(X + rowc * H * (int64_t)P, (uint32_t)len * H * P * ES);
+        return make_rsrc(X + rowc * XH * (int64_t)P, (uint32_t)len * XH * P * ES);
     };
     auto bc_rsrc = [&](const T* base, int64_t rowc, int len) {
         return make_rsrc(base + rowc * G * (int64_t)N, (uint32_t)len * G * N * ES);
@@ -467,7 +469,7 @@ __global__ void __launch_bounds__(512) ssd_walk_kernel(WalkArgs a) {
             const int idx = tid + 512 * k;
             const int r = idx / XSEG, c8 = (idx % XSEG) * 8;
             const int p = p_base + c8;
-            px[k] = E::ldb8(xr, p < P ? (uint32_t)((r * H + h) * P + p) * ES : kOutOfRange);
+            px[k] = E::ldb8(xr, p < P ? (uint32_t)((r * XH + xhi) * P + p) * ES : kOutOfRange);
             pcs_r[k] = ldb_f32(csr, 4u * r);
             pcs_e[k] = ldb_f32(csr, 4u * (r | 31));
         }

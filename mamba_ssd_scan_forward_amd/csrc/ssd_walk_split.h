@@ -196,6 +196,7 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
     const __bf16* CTg = static_cast<const __bf16*>(a.ct);
     __bf16* Y = static_cast<__bf16*>(a.Y);
     const int64_t state_base = ((int64_t)s * H + h) * P * (int64_t)N;
+    const int XH = a.xh, xhi = h / (H / XH);   // X row of this head
 
     auto xts_buf = [&](int c) { return reinterpret_cast<__bf16*>(smem + L::xts + (c & 1) * 256 * 64 * 2); };
     auto cs_buf = [&](int c) { return reinterpret_cast<float*>(smem + L::cs + (c & 1) * 256 * 4); };
@@ -230,9 +231,9 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
             int64_t rowc;
             int len;
             chunk_at(c, &rowc, &len);
-            const rsrc_t xr = make_rsrc(X + rowc * H * (int64_t)P, (uint32_t)len * H * P * 2);
-            const uint32_t xb = opaque((uint32_t)(((ts >> 3) * H + h) * P + p_base + (ts & 7) * 8) * 2);
-            const uint32_t xstep = (uint32_t)(32 * H * P * 2);
+            const rsrc_t xr = make_rsrc(X + rowc * XH * (int64_t)P, (uint32_t)len * XH * P * 2);
+            const uint32_t xb = opaque((uint32_t)(((ts >> 3) * XH + xhi) * P + p_base + (ts & 7) * 8) * 2);
+            const uint32_t xstep = (uint32_t)(32 * XH * P * 2);
 #pragma unroll
             for (int k = 0; k < 8; ++k) px[k] = E::ldb8(xr, xb + k * xstep);
         };
@@ -602,7 +603,7 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
                     // (opaque: the row indexes of this cold path are not worth registers
                     // held across the loop)
                     const int r = 8 * k + (int)opaque((uint32_t)lane >> 3), c8 = (lane & 7) * 8;
-                    const frag v = l0 + r < len ? E::ldg8(X + ((rowc + l0 + r) * H + h) * (int64_t)P + p_base + c8) : E::zero();
+                    const frag v = l0 + r < len ? E::ldg8(X + ((rowc + l0 + r) * XH + xhi) * (int64_t)P + p_base + c8) : E::zero();
                     *reinterpret_cast<frag*>(xb + XL::idx(r, c8)) = v;
                 }
                 xsrc = xb;
