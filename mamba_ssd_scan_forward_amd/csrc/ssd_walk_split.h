@@ -19,8 +19,8 @@
 //
 //   The state waves also stage the next chunk (X~ and the cumsum) and h_{c+1}.  X~
 //   and the cumsum are double-buffered, h is not, which gives two barriers per chunk:
-//     state waves : state(c)                          | B_mid | store Y of block i2,
-//                                                      |       | write h, X~ of c+1
+//     state waves : state(c), X~ of c+1               | B_mid | store Y of block i2,
+//                                                      |       | write h of c+1
 //     output waves: block i2 whole, block i1 up to its | B_mid | block i1's diagonal
 //                   chain                              |       |
 //     then B_end, after which the state waves store Y of block i1.  (h of chunk c is
@@ -458,11 +458,13 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
             load_bt(cn);
             put_cs(c + 1);
             scale_x(c + 1);
+            // X~ of chunk c + 1 goes to the other buffer, which nobody reads in chunk c:
+            // written while the output waves are still before B_mid
+            commit_x(c + 1);
             pack_h();
             __syncthreads();   // B_mid: h of chunk c is no longer read
             store_y(c, 1);
             write_h();
-            commit_x(c + 1);
             __syncthreads();   // B_end
             store_y(c, 0);
         }
