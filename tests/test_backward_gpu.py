@@ -116,3 +116,53 @@ def test_backward_matches_oracle(case):
     else:
         inp = make_inputs(2, 520, 3, 128, 64, 1, "bf16", seed=2006, init_state=True)
         check_backward(inp, 256, case)
+
+
+@pytest.mark.parametrize("name,sample", [("cfg1_mamba2_2.7b_bf16", [0, 7]), ("cfg4_varlen32k_bf16", [6, 13])])
+def test_backward_full_size_sampled_sequences(name, sample):
+    """The backward pass of a whole workload configuration in the launch configuration the
+    benchmark times; the oracle recomputes the gradients of two sampled sequences (the
+    sequences are independent, so their slices of every gradient are exact references)."""
+    import copy
+    import mamba_ssd_scan_forward_amd as ssd
+    from workloads import CONFIGS, workload_inputs
+    torch = _torch()
+    w = CONFIGS[name]
+    inp = workload_inputs(w)
+    rng = np.random.default_rng(77)
+    nseq = w.batch if inp.seq_offsets is None else len(inp.seq_offsets) - 1
+    dY = bf16_round(rng.standard_normal(inp.X.shape))
+    dF = (rng.standard_normal((nseq, w.nheads, w.headdim, w.dstate)) * 0.5).astype(np.float32)
+    print(f"[backward] full size {name}, sampled sequences {sample}", flush=True)
+    dt = torch.bfloat16
+    dev = lambda a, t=dt: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(t).cuda()
+    X, logA, B, C = dev(inp.X), dev(inp.logA, torch.float32), dev(inp.B), dev(inp.C)
+    init = dev(inp.init, torch.float32)
+    off = None if inp.seq_offsets is None else torch.from_numpy(inp.seq_offsets).cuda()
+    Y, F = ssd.forward(X, logA, B, C, w.chunk_len, init, off)
+    grads = ssd.backward(X, logA, B, C, w.chunk_len, Y, dev(dY), init, off, F, dev(dF, torch.float32))
+    torch.cuda.synchronize()
+    got = [g.float().cpu().numpy().astype(np.float64) for g in grads]
+    for s in sample:
+        if inp.seq_offsets is None:
+            rows = slice(None)
+            sub = copy.deepcopy(inp)
+            sub.X, sub.logA, sub.B, sub.C = (a[s:s + 1] for a in (inp.X, inp.logA, inp.B, inp.C))
+            sub.init = None if inp.init is None else inp.init[s:s + 1]
+            sl = lambda a: a[s:s + 1]
+        else:
+            r0, r1 = int(inp.seq_offsets[s]), int(inp.seq_offsets[s + 1])
+            sub = copy.deepcopy(inp)
+            sub.X, sub.logA, sub.B, sub.C = (a[:, r0:r1] for a in (inp.X, inp.logA, inp.B, inp.C))
+            sub.init = None if inp.init is None else inp.init[s:s + 1]
+            sub.seq_offsets = None
+            sl = lambda a: a[:, r0:r1]
+        ref = oracle.backward(sub.X, sub.logA, sub.B, sub.C, sub.init, None, sl(dY), dF[s:s + 1])
+        mine = [sl(got[0]), sl(got[1]), sl(got[2]), sl(got[3]), got[4][s:s + 1]]
+        errs = {n: rel_err(g, r) for n, g, r in zip(["dX", "dlogA", "dB", "dC", "dinit"], mine, ref)
+                if r is not None}
+        scale = cumsum_scale(sub, sl(dY))
+        errs["dlogA"] = float(np.max(np.abs(mine[1] - ref[1]))) / max(float(np.max(np.abs(ref[1]))), scale)
+        print(f"[backward]   seq {s}: " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+        for k, v in errs.items():
+            assert v <= TOL["bf16"], (s, k, v)
