@@ -124,8 +124,20 @@ __global__ void __launch_bounds__(256) ssd_bwd_group_sum_kernel(const T* in, T* 
         const int64_t r = rg / G;
         const int64_t src = m.src(r);
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
-            const frag x = E::ldg8(in + (src * H + h) * (int64_t)N + 8 * v);
+        const T* base = in + (src * H + g * hpg) * (int64_t)N + 8 * v;
+        int h = 0;
+        // eight heads' loads in flight at a time
+        for (; h + 8 <= hpg; h += 8) {
+            frag x[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) x[k] = E::ldg8(base + (int64_t)(h + k) * N);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[q] += E::to_f(x[k][q]);
+        }
+        for (; h < hpg; ++h) {
+            const frag x = E::ldg8(base + (int64_t)h * N);
 #pragma unroll
             for (int q = 0; q < 8; ++q) acc[q] += E::to_f(x[q]);
         }
@@ -179,17 +191,32 @@ __global__ void __launch_bounds__(64) ssd_bwd_dlogA_kernel(const float* rr, cons
     float carry = 0.f;
     if (dF) {
         float acc = 0.f;
-        for (int i = lane; i < PN; i += 64) acc += dF[(int64_t)sh * PN + i] * F[(int64_t)sh * PN + i];
+        const f32x4* a4 = reinterpret_cast<const f32x4*>(dF + (int64_t)sh * PN);
+        const f32x4* b4 = reinterpret_cast<const f32x4*>(F + (int64_t)sh * PN);
+#pragma unroll 8
+        for (int i = lane; i < PN / 4; i += 64) {
+            const f32x4 x = a4[i], y = b4[i];
+            acc += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+        }
         carry = __shfl(wave_inclusive_sum(acc, lane), 63, 64);
     }
     int64_t r0, r1;
     seq_rows(s, T, off, &r0, &r1);
-    for (int64_t top = r1; top > r0; top -= 64) {
-        const int64_t t = top - 1 - lane;
-        const float v = t >= r0 ? rr[t * H + h] : 0.f;
-        const float sum = wave_inclusive_sum(v, lane);
-        if (t >= r0) dlogA[t * H + h] = carry + sum;
-        carry += __shfl(sum, 63, 64);
+    // 16 steps of 64 tokens loaded at once, then scanned one after the other
+    for (int64_t top = r1; top > r0; top -= 16 * 64) {
+        float v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int64_t t = top - 1 - 64 * k - lane;
+            v[k] = t >= r0 ? rr[t * H + h] : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int64_t t = top - 1 - 64 * k - lane;
+            const float sum = wave_inclusive_sum(v[k], lane);
+            if (t >= r0) dlogA[t * H + h] = carry + sum;
+            carry += __shfl(sum, 63, 64);
+        }
     }
 }
 
