@@ -234,3 +234,11 @@ def test_backward_rejects_small_workspace_and_misalignment():
     p = prob()
     assert bcall(p, ws_bytes=ssd.ssd_backward_workspace_bytes(p) - 256, off=None) == ssd.SSD_ERR_WORKSPACE
     assert bcall(p, off=None, dlogA=BADDR["dlogA"] + 4) == ssd.SSD_ERR_INVALID_ARG
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    # no fallback: a missing libssd.so is an import error, not a silent CPU path
+    monkeypatch.setattr(ssd, "_lib", None)
+    monkeypatch.setattr(ssd, "lib_path", lambda: str(tmp_path / "libssd.so"))
+    with pytest.raises(ImportError):
+        ssd.load_library()
