@@ -33,6 +33,8 @@ struct Plan {
     int64_t ntail;    // items walked in segments: the last ones
     int summary_lds;
     size_t seg_off, segd_off;
+    int npass;        // d_state walked as npass passes of N / npass columns (1 or 2)
+    size_t pass_ws, y2_off;   // workspace of one pass; the second pass's output
     walk_fn_t walk;   // the walk kernel instance for this plan
     walk_fn_t summary;   // the segment-summary instance (nseg > 1)
 };
@@ -117,6 +119,23 @@ int make_plan(const ssd_problem* p, Plan* pl) {
     if (rc != SSD_OK) return rc;
     pl->dtype = p->dtype;
     pl->summary = nullptr;
+    pl->npass = 1;
+    // d_state 256 on the layer-shape walker: the layer is linear in C B^T and its state
+    // splits by columns, so it is the sum of two d_state-128 problems on the column
+    // halves of B, C and the state (init and final state each take their half).  Each
+    // half gets its own workspace; the second writes its output to the workspace and a
+    // last kernel adds it to Y.
+    if (p->dtype == SSD_DTYPE_BF16 && p->chunk_len == 256 && p->dstate == 256 && p->headdim % 64 == 0) {
+        ssd_problem q = *p;
+        q.dstate = 128;
+        const int qrc = make_plan(&q, pl);
+        if (qrc != SSD_OK) return qrc;
+        pl->npass = 2;
+        pl->pass_ws = pl->ws_bytes;
+        pl->y2_off = 2 * pl->pass_ws;
+        pl->ws_bytes = align_up(pl->y2_off + (size_t)(p->batch * p->seqlen * p->nheads * p->headdim) * 2, 256);
+        return SSD_OK;
+    }
     const int es = p->dtype == SSD_DTYPE_BF16 ? 2 : 4;
     pl->Q = (int)p->chunk_len;
     pl->Qp = (pl->Q + 31) / 32 * 32;
@@ -316,83 +335,107 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
     }
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    unsigned char* ws = static_cast<unsigned char*>(workspace);
-    float* cs = reinterpret_cast<float*>(ws + pl.cs_off);
-    void* cb = ws + pl.cb_off;
     // slots actually addressed by this call
     const int64_t nc = (T + pl.Q - 1) / pl.Q;
     const int64_t nslots = seq_offsets ? nc + p->nseq : b * nc;
+    const int64_t NPASS = N / pl.npass;   // state columns of one pass
+    auto pass_args = [&](int k, ssd::PrepArgs* ppa, ssd::WalkArgs* pwa) {
+        unsigned char* ws = static_cast<unsigned char*>(workspace) + k * pl.pass_ws;
+        float* cs = reinterpret_cast<float*>(ws + pl.cs_off);
+        void* cb = ws + pl.cb_off;
+        ssd::PrepArgs& pa = *ppa;
+        pa.logA = logA;
+        pa.B = B;
+        pa.C = C;
+        pa.seq_offsets = seq_offsets;
+        pa.cs = cs;
+        pa.cb = cb;
+        pa.T = T;
+        pa.H = (int)H;
+        pa.N = (int)NPASS;
+        pa.G = (int)G;
+        pa.Q = pl.Q;
+        pa.Qp = pl.Qp;
+        pa.ntile = pl.ntile;
+        pa.nseq = (int)p->nseq;
+        pa.hblocks = (int)((H + ssd::kPrepHeads - 1) / ssd::kPrepHeads);
+        pa.cs_blocks = (int)(nslots * pa.hblocks);
+        pa.cb_blocks = (int)(nslots * G);
+        pa.bt = pl.split ? ws + pl.bt_off : nullptr;
+        pa.ct = pl.split ? ws + pl.ct_off : nullptr;
+        pa.ldn = (int)N;
+        pa.n0 = (int)(k * NPASS);
 
-    ssd::PrepArgs pa;
-    pa.logA = logA;
-    pa.B = B;
-    pa.C = C;
-    pa.seq_offsets = seq_offsets;
-    pa.cs = cs;
-    pa.cb = cb;
-    pa.T = T;
-    pa.H = (int)H;
-    pa.N = (int)N;
-    pa.G = (int)G;
-    pa.Q = pl.Q;
-    pa.Qp = pl.Qp;
-    pa.ntile = pl.ntile;
-    pa.nseq = (int)p->nseq;
-    pa.hblocks = (int)((H + ssd::kPrepHeads - 1) / ssd::kPrepHeads);
-    pa.cs_blocks = (int)(nslots * pa.hblocks);
-    pa.cb_blocks = (int)(nslots * G);
-    pa.bt = pl.split ? ws + pl.bt_off : nullptr;
-    pa.ct = pl.split ? ws + pl.ct_off : nullptr;
-    const int64_t prep_blocks = nslots * pa.hblocks + nslots * G;
+        ssd::WalkArgs& wa = *pwa;
+        wa.X = X;
+        wa.B = B;
+        wa.C = C;
+        wa.init = init_state;
+        wa.seq_offsets = seq_offsets;
+        wa.Y = k == 0 ? Y : static_cast<unsigned char*>(workspace) + pl.y2_off;
+        wa.final_state = final_state;
+        wa.cs = cs;
+        wa.cb = cb;
+        wa.bt = ws + pl.bt_off;
+        wa.ct = ws + pl.ct_off;
+        wa.T = T;
+        wa.H = (int)H;
+        wa.P = (int)P;
+        wa.N = (int)NPASS;
+        wa.G = (int)G;
+        wa.Q = pl.Q;
+        wa.Qp = pl.Qp;
+        wa.ntile = pl.ntile;
+        wa.nseq = (int)p->nseq;
+        wa.ptiles = pl.ptiles;
+        wa.nitems = (int)pl.nitems;
+        wa.qb = pl.qb;
+        wa.cb_lds = pl.cb_lds;
+        wa.xs_off = pl.xs_off;
+        wa.xts_off = pl.xts_off;
+        wa.bs_off = pl.bs_off;
+        wa.hs_off = pl.hs_off;
+        wa.cs_off = pl.cs_lds_off;
+        wa.xh = (int)x_heads;
+        wa.ldn = (int)N;
+        wa.ns0 = (int)(k * NPASS);
+        wa.nseg = nseg;
+        wa.nsplit = pl.nsplit;
+        wa.ntail = nseg > 1 ? (int)pl.ntail : 0;
+        wa.nwhole = (int)(pl.nitems - wa.ntail);
+        wa.lpt = (pl.split && seq_offsets && p->nseq <= 64 && (p->nseq * G) % 8 == 0) ? 1 : 0;
+        wa.seg_state = reinterpret_cast<float*>(ws + pl.seg_off);
+        wa.seg_decay = reinterpret_cast<float*>(ws + pl.segd_off);
+    };
+    const int64_t prep_blocks = nslots * ((H + ssd::kPrepHeads - 1) / ssd::kPrepHeads) + nslots * G;
     if (prep_blocks > INT32_MAX) return SSD_ERR_UNSUPPORTED;
-    if (stages & 1)
-        hipLaunchKernelGGL(prep, dim3((unsigned)prep_blocks), dim3(kPrepThreads), 0, stream, pa);
-
+    ssd::PrepArgs pa;
     ssd::WalkArgs wa;
-    wa.X = X;
-    wa.B = B;
-    wa.C = C;
-    wa.init = init_state;
-    wa.seq_offsets = seq_offsets;
-    wa.Y = Y;
-    wa.final_state = final_state;
-    wa.cs = cs;
-    wa.cb = cb;
-    wa.bt = ws + pl.bt_off;
-    wa.ct = ws + pl.ct_off;
-    wa.T = T;
-    wa.H = (int)H;
-    wa.P = (int)P;
-    wa.N = (int)N;
-    wa.G = (int)G;
-    wa.Q = pl.Q;
-    wa.Qp = pl.Qp;
-    wa.ntile = pl.ntile;
-    wa.nseq = (int)p->nseq;
-    wa.ptiles = pl.ptiles;
-    wa.nitems = (int)pl.nitems;
-    wa.qb = pl.qb;
-    wa.cb_lds = pl.cb_lds;
-    wa.xs_off = pl.xs_off;
-    wa.xts_off = pl.xts_off;
-    wa.bs_off = pl.bs_off;
-    wa.hs_off = pl.hs_off;
-    wa.cs_off = pl.cs_lds_off;
-    wa.xh = (int)x_heads;
-    wa.nseg = nseg;
-    wa.nsplit = pl.nsplit;
-    wa.ntail = nseg > 1 ? (int)pl.ntail : 0;
-    wa.nwhole = (int)(pl.nitems - wa.ntail);
-    wa.lpt = (pl.split && seq_offsets && p->nseq <= 64 && (p->nseq * G) % 8 == 0) ? 1 : 0;
-    wa.seg_state = reinterpret_cast<float*>(ws + pl.seg_off);
-    wa.seg_decay = reinterpret_cast<float*>(ws + pl.segd_off);
-    if ((stages & 2) && nseg > 1) {
-        wa.nitems = wa.ntail * (nseg - 1) * pl.nsplit;
-        hipLaunchKernelGGL(pl.summary, dim3((unsigned)wa.nitems), dim3(kWalkThreads / 2), pl.summary_lds, stream, wa);
+    if (stages & 1) {
+        for (int k = 0; k < pl.npass; ++k) {
+            pass_args(k, &pa, &wa);
+            hipLaunchKernelGGL(prep, dim3((unsigned)prep_blocks), dim3(kPrepThreads), 0, stream, pa);
+        }
     }
-    wa.nitems = wa.nwhole + wa.ntail * nseg;
-    if (stages & 2)
-        hipLaunchKernelGGL(walk, dim3((unsigned)wa.nitems), dim3(kWalkThreads), pl.lds_bytes, stream, wa);
+    if (stages & 2) {
+        for (int k = 0; k < pl.npass; ++k) {
+            pass_args(k, &pa, &wa);
+            if (nseg > 1) {
+                wa.nitems = wa.ntail * (nseg - 1) * pl.nsplit;
+                hipLaunchKernelGGL(pl.summary, dim3((unsigned)wa.nitems), dim3(kWalkThreads / 2), pl.summary_lds,
+                                   stream, wa);
+            }
+            wa.nitems = wa.nwhole + wa.ntail * nseg;
+            hipLaunchKernelGGL(walk, dim3((unsigned)wa.nitems), dim3(kWalkThreads), pl.lds_bytes, stream, wa);
+        }
+        if (pl.npass == 2) {
+            const int64_t n8 = b * T * H * P / 8;
+            const int64_t blocks = (n8 + 255) / 256 < 16384 ? (n8 + 255) / 256 : 16384;
+            hipLaunchKernelGGL(ssd::ssd_add_kernel<__bf16>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                               static_cast<__bf16*>(Y),
+                               reinterpret_cast<const __bf16*>(static_cast<unsigned char*>(workspace) + pl.y2_off), n8);
+        }
+    }
     if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
     return SSD_OK;
 }

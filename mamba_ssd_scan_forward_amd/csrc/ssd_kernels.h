@@ -45,6 +45,7 @@ struct PrepArgs {
     int cs_blocks;    // workgroups of the cumsum role: nslots * hblocks
     int hblocks;      // 64-head blocks per chunk
     int cb_blocks;    // workgroups of the C B^T role: nslots * G
+    int ldn, n0;      // B, C rows hold ldn values; this call uses columns [n0, n0 + N)
     void* bt;         // optional: B^T of every 256-row chunk in MFMA A-operand fragment
                       // order, [nslots, G, N/32, 8, 2, 64 lanes, 8], and
     void* ct;         // C in MFMA B-operand fragment order, [nslots, G, 8, N/16, 64 lanes,
@@ -70,6 +71,7 @@ struct WalkArgs {
     int nwhole, ntail;  // items walked whole, then items walked in nseg segments
     int lpt;            // packed sequences: (sequence, group) units dealt to XCDs longest first
     int xh;             // X rows per token: H (one per head), or fewer, shared by H / xh heads
+    int ldn, ns0;       // init / final state rows hold ldn values; this call's are [ns0, ns0 + N)
     int64_t T;
     int H, P, N, G, Q, Qp, ntile, nseq, ptiles, nitems, qb;
     int cb_lds;                                    // stage off-diagonal C B^T tiles in LDS
@@ -238,7 +240,7 @@ __global__ void __launch_bounds__(256, 2) ssd_prep_kernel(PrepArgs a) {
             uint4 vb = {0u, 0u, 0u, 0u}, vc = {0u, 0u, 0u, 0u};
             // (N is a multiple of 16, so a 16-byte piece is wholly inside or past a row)
             if (r < len && n0 + c < a.N) {
-                const int64_t off = (((rowc + r) * a.G + g) * (int64_t)a.N + n0 + c) * (int64_t)sizeof(T);
+                const int64_t off = (((rowc + r) * a.G + g) * (int64_t)a.ldn + a.n0 + n0 + c) * (int64_t)sizeof(T);
                 vb = *reinterpret_cast<const uint4*>(Bp + off);
                 vc = *reinterpret_cast<const uint4*>(Cp + off);
             }
@@ -295,6 +297,21 @@ __global__ void __launch_bounds__(256, 2) ssd_prep_kernel(PrepArgs a) {
             T* o = out + (((q >> 1) * 64 + (q & 1) * 32 + lr) * 8 + 4 * lg);
             E::st4(o, acc[u][4 * q], acc[u][4 * q + 1], acc[u][4 * q + 2], acc[u][4 * q + 3]);
         }
+    }
+}
+
+// y <- y + z elementwise (float32 sums, stored in the element type), 8 values per thread:
+// the two column halves of a d_state that is walked as two passes
+template <typename T>
+__global__ void __launch_bounds__(256) ssd_add_kernel(T* y, const T* z, int64_t n8) {
+    using E = Elem<T>;
+    typedef typename E::frag frag;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
+        const frag a = E::ldg8(y + 8 * i), b = E::ldg8(z + 8 * i);
+        frag o;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) o[q] = E::from_f(E::to_f(a[q]) + E::to_f(b[q]));
+        *reinterpret_cast<frag*>(y + 8 * i) = o;
     }
 }
 

@@ -195,7 +195,9 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
     const __bf16* BTg = static_cast<const __bf16*>(a.bt);
     const __bf16* CTg = static_cast<const __bf16*>(a.ct);
     __bf16* Y = static_cast<__bf16*>(a.Y);
-    const int64_t state_base = ((int64_t)s * H + h) * P * (int64_t)N;
+    // init / final state of this (sequence, head): rows of ldn values, this call's
+    // columns from ns0 (a d_state walked in two passes of half the columns)
+    const int64_t state_base = ((int64_t)s * H + h) * P * (int64_t)a.ldn + a.ns0;
     const int XH = a.xh, xhi = h / (H / XH);   // X row of this head
 
     auto xts_buf = [&](int c) { return reinterpret_cast<__bf16*>(smem + L::xts + (c & 1) * 256 * 64 * 2); };
@@ -351,27 +353,27 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
         };
         auto state_chunk = [&](int c) { state_chunk_with(c, pbt); };
 
-        // the state tiles of this wave from / to a [P][N] float32 state at `base`
-        auto add_state = [&](const float* base, float f) {
+        // the state tiles of this wave from / to a float32 state at `base`, rows of ld values
+        auto add_state = [&](const float* base, int64_t ld, float f) {
 #pragma unroll
             for (int u = 0; u < TPS; ++u) {
                 const int n0 = tile_n0(u), p = p_base + tile_p0(u) + lr;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const f32x4 v = *reinterpret_cast<const f32x4*>(base + (int64_t)p * N + n0 + 8 * q + 4 * lg);
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(base + (int64_t)p * ld + n0 + 8 * q + 4 * lg);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) hacc[u][4 * q + e] = hacc[u][4 * q + e] * f + v[e];
                 }
             }
         };
-        auto put_state = [&](float* base) {
+        auto put_state = [&](float* base, int64_t ld) {
 #pragma unroll
             for (int u = 0; u < TPS; ++u) {
                 const int n0 = tile_n0(u), p = p_base + tile_p0(u) + lr;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const f32x4 v = {hacc[u][4 * q], hacc[u][4 * q + 1], hacc[u][4 * q + 2], hacc[u][4 * q + 3]};
-                    *reinterpret_cast<f32x4*>(base + (int64_t)p * N + n0 + 8 * q + 4 * lg) = v;
+                    *reinterpret_cast<f32x4*>(base + (int64_t)p * ld + n0 + 8 * q + 4 * lg) = v;
                 }
             }
         };
@@ -419,16 +421,16 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
                 summary_step(c, pbt, pbt2);
                 summary_step(c + 1, pbt2, pbt);
             }
-            put_state(a.seg_state + summary_at(seg, part) * pn);
+            put_state(a.seg_state + summary_at(seg, part) * pn, N);
             if (sw == 0 && pt == 0 && lane == 0) a.seg_decay[summary_at(seg, part)] = dsum;
             return;
         }
 
         // the entry state of this segment
-        if (a.init) add_state(a.init + state_base, 0.f);
+        if (a.init) add_state(a.init + state_base, a.ldn, 0.f);
         for (int k = 0; k < seg; ++k)
             for (int j = 0; j < a.nsplit; ++j)
-                add_state(a.seg_state + summary_at(k, j) * pn, fast_exp2(a.seg_decay[summary_at(k, j)]));
+                add_state(a.seg_state + summary_at(k, j) * pn, N, fast_exp2(a.seg_decay[summary_at(k, j)]));
 
         if (nchunks > 0) {
             load_cs(0);
@@ -468,7 +470,7 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
             __syncthreads();   // B_end
             store_y(c, 0);
         }
-        if (a.final_state && seg == nseg - 1) put_state(a.final_state + state_base);
+        if (a.final_state && seg == nseg - 1) put_state(a.final_state + state_base, a.ldn);
     } else if constexpr (!SUMMARY) {
         // ========================================================== output waves
         // The two blocks are done one after the other, the later one (longer chain)

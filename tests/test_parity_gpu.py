@@ -157,9 +157,23 @@ def test_bitwise_repeatable():
 # The common layer shapes (bf16, 256-row chunks, d_state 64 or 128, head dimension a
 # multiple of 64) run on their own walker; these cases reach its edges.
 @pytest.mark.parametrize("case", ["varlen", "varlen_ties", "strong_decay", "mixed_decay", "headdim128",
-                                  "one_chunk_n64", "a_one"])
+                                  "one_chunk_n64", "a_one", "state256", "state256_varlen",
+                                  "state256_segmented"])
 def test_layer_shape_walker_edges(case):
-    if case == "varlen_ties":
+    if case.startswith("state256"):
+        # d_state 256: two passes over the column halves of B, C and the state
+        if case == "state256":
+            inp = make_inputs(2, 600, 4, 64, 256, 2, "bf16", seed=1007, init_state=True)
+        elif case == "state256_varlen":
+            lens = [300, 0, 513, 7, 256, 90, 1, 44]
+            inp = make_inputs(1, sum(lens), 2, 64, 256, 1, "bf16", seed=1008, init_state=True,
+                              seq_lengths=lens)
+        else:
+            inp = make_inputs(1, 4200, 2, 128, 256, 2, "bf16", seed=1009, init_state=True)
+        Y, F = check(inp, 256, case)
+        if case == "state256_varlen":
+            np.testing.assert_array_equal(F[1], inp.init[1].astype(np.float64))
+    elif case == "varlen_ties":
         # packed sequences dealt to XCDs longest first: equal lengths, an empty one
         lens = [300, 300, 5, 0, 300, 77, 256, 1]
         inp = make_inputs(1, sum(lens), 3, 64, 128, 1, "bf16", seed=1006, init_state=True,
