@@ -36,6 +36,7 @@ struct Plan {
     int npass;        // d_state walked as npass passes of N / npass columns (1 or 2)
     size_t pass_ws, y2_off;   // workspace of one pass; the second pass's output
     walk_fn_t walk;   // the walk kernel instance for this plan
+    walk_fn_t walk_left;   // the second pass of a two-pass d_state (left factors only)
     walk_fn_t summary;   // the segment-summary instance (nseg > 1)
 };
 
@@ -119,6 +120,7 @@ int make_plan(const ssd_problem* p, Plan* pl) {
     if (rc != SSD_OK) return rc;
     pl->dtype = p->dtype;
     pl->summary = nullptr;
+    pl->walk_left = nullptr;
     pl->npass = 1;
     // d_state 256 on the layer-shape walker: the layer is linear in C B^T and its state
     // splits by columns, so it is the sum of two d_state-128 problems on the column
@@ -131,6 +133,7 @@ int make_plan(const ssd_problem* p, Plan* pl) {
         const int qrc = make_plan(&q, pl);
         if (qrc != SSD_OK) return qrc;
         pl->npass = 2;
+        pl->walk_left = ssd::ssd_walk_split_kernel<128, false, true>;
         pl->pass_ws = pl->ws_bytes;
         pl->y2_off = 2 * pl->pass_ws;
         pl->ws_bytes = align_up(pl->y2_off + (size_t)(p->batch * p->seqlen * p->nheads * p->headdim) * 2, 256);
@@ -327,6 +330,10 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
                                               : ssd::ssd_prep_kernel<float>;
     rc = ensure_lds_limit(reinterpret_cast<const void*>(walk));
     if (rc != SSD_OK) return rc;
+    if (pl.npass == 2) {
+        rc = ensure_lds_limit(reinterpret_cast<const void*>(pl.walk_left));
+        if (rc != SSD_OK) return rc;
+    }
     // packed sequences are walked whole
     const int nseg = seq_offsets ? 1 : pl.nseg;
     if (nseg > 1) {
@@ -365,6 +372,9 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
         pa.ct = pl.split ? ws + pl.ct_off : nullptr;
         pa.ldn = (int)N;
         pa.n0 = (int)(k * NPASS);
+        // the first pass's tiles contract all columns (its walk adds the whole
+        // within-chunk part); the second pass only needs its fragment copies
+        pa.cb_n = k == 0 ? (int)N : 0;
 
         ssd::WalkArgs& wa = *pwa;
         wa.X = X;
@@ -426,7 +436,8 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
                                    stream, wa);
             }
             wa.nitems = wa.nwhole + wa.ntail * nseg;
-            hipLaunchKernelGGL(walk, dim3((unsigned)wa.nitems), dim3(kWalkThreads), pl.lds_bytes, stream, wa);
+            hipLaunchKernelGGL(k == 0 ? walk : pl.walk_left, dim3((unsigned)wa.nitems), dim3(kWalkThreads),
+                               pl.lds_bytes, stream, wa);
         }
         if (pl.npass == 2) {
             const int64_t n8 = b * T * H * P / 8;

@@ -45,7 +45,8 @@ struct PrepArgs {
     int cs_blocks;    // workgroups of the cumsum role: nslots * hblocks
     int hblocks;      // 64-head blocks per chunk
     int cb_blocks;    // workgroups of the C B^T role: nslots * G
-    int ldn, n0;      // B, C rows hold ldn values; this call uses columns [n0, n0 + N)
+    int ldn, n0;      // B, C rows hold ldn values; the fragment copies take columns [n0, n0 + N)
+    int cb_n;         // C B^T contracts columns [0, cb_n) (ldn: all of them), or 0: no tiles
     void* bt;         // optional: B^T of every 256-row chunk in MFMA A-operand fragment
                       // order, [nslots, G, N/32, 8, 2, 64 lanes, 8], and
     void* ct;         // C in MFMA B-operand fragment order, [nslots, G, 8, N/16, 64 lanes,
@@ -233,14 +234,17 @@ __global__ void __launch_bounds__(256, 2) ssd_prep_kernel(PrepArgs a) {
 #pragma unroll
     for (int u = 0; u < MAXT; ++u) acc[u] = f32x16{};
     constexpr int pieces = SW * (int)sizeof(T) / 16;   // 16-byte pieces per slab row
-    for (int n0 = 0; n0 < a.N; n0 += SW) {
+    // global columns walked: [0, cb_n) for the tiles, or only the fragment copies' range
+    const int col_lo = a.cb_n > 0 ? 0 : a.n0, col_hi = a.cb_n > 0 ? a.cb_n : a.n0 + a.N;
+    for (int cg = col_lo; cg < col_hi; cg += SW) {
+        const int n0 = cg - a.n0;   // column within the fragment copies' range
         __syncthreads();   // the previous slab has been read
         for (int idx = tid; idx < a.Qp * pieces; idx += 256) {
             const int r = idx / pieces, c = (idx % pieces) * (16 / (int)sizeof(T));
             uint4 vb = {0u, 0u, 0u, 0u}, vc = {0u, 0u, 0u, 0u};
-            // (N is a multiple of 16, so a 16-byte piece is wholly inside or past a row)
-            if (r < len && n0 + c < a.N) {
-                const int64_t off = (((rowc + r) * a.G + g) * (int64_t)a.ldn + a.n0 + n0 + c) * (int64_t)sizeof(T);
+            // (the widths are multiples of 16, so a 16-byte piece is wholly inside or past)
+            if (r < len && cg + c < col_hi) {
+                const int64_t off = (((rowc + r) * a.G + g) * (int64_t)a.ldn + cg + c) * (int64_t)sizeof(T);
                 vb = *reinterpret_cast<const uint4*>(Bp + off);
                 vc = *reinterpret_cast<const uint4*>(Cp + off);
             }
@@ -249,7 +253,7 @@ __global__ void __launch_bounds__(256, 2) ssd_prep_kernel(PrepArgs a) {
         }
         __syncthreads();
         if constexpr (sizeof(T) == 2) {
-            if (a.bt) {
+            if (a.bt && n0 >= 0 && n0 < a.N) {
                 // (c) for the split walker (256-row chunks, this slab = n tile n0 / 32): B^T
                 //     as A-operand fragments, (nt, j, ks) lane (lr, lg) holding
                 //     B[32 j + 16 ks + 8 lg + q][32 nt + lr], and C as B-operand fragments,
@@ -269,6 +273,7 @@ __global__ void __launch_bounds__(256, 2) ssd_prep_kernel(PrepArgs a) {
                 }
             }
         }
+        if (a.cb_n == 0) continue;
 #pragma unroll
         for (int u = 0; u < MAXT; ++u) {
             if (wave + 4 * u >= a.ntile) break;
@@ -280,6 +285,7 @@ __global__ void __launch_bounds__(256, 2) ssd_prep_kernel(PrepArgs a) {
             }
         }
     }
+    if (a.cb_n == 0) return;
 #pragma unroll
     for (int u = 0; u < MAXT; ++u) {
         const int t = wave + 4 * u;

@@ -84,7 +84,10 @@ __host__ __device__ constexpr int split_bt_bytes(int N) { return N * 512; }
 //                    the parts of segments 0 .. k-1 in order, E <- 2^(decay) E + state,
 //                    in the prologue; it then walks its chunks in full.  Only the last
 //                    segment writes the final state.
-template <int NP, bool SUMMARY>
+// LEFT = true: the output waves compute only the left factors 2^(cs[l]) C_l h of every
+// block (no C B^T chains or diagonal blocks): the second pass of a d_state walked as two
+// column halves, whose within-chunk part the first pass, which sees the full C B^T, holds.
+template <int NP, bool SUMMARY, bool LEFT = false>
 __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
     typedef Elem<__bf16> E;
     typedef bf16x8 frag;
@@ -646,6 +649,56 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
                            acc[v][4 * q + 2], acc[v][4 * q + 3]);
         };
 
+        if constexpr (LEFT) {
+            // left factor of block u scaled by its rows' decay from the chunk start, then
+            // to this wave's LDS area (block slot u) for the state waves to store
+            auto left_only = [&](int c, int u) {
+                const int i = u == 0 ? i1 : i2;
+                acc[0] = f32x16{};
+                acc[1] = f32x16{};
+                frag hv[2][2];
+#pragma unroll
+                for (int v = 0; v < 2; ++v) hv[0][v] = E::lds8(hs + (32 * v + lr) * HS + 8 * lg);
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    if (ks + 1 < NKS) {
+#pragma unroll
+                        for (int v = 0; v < 2; ++v)
+                            hv[(ks + 1) & 1][v] = E::lds8(hs + (32 * v + lr) * HS + 16 * (ks + 1) + 8 * lg);
+                    }
+#pragma unroll
+                    for (int v = 0; v < 2; ++v) acc[v] = E::mma(acc[v], hv[ks & 1][v], pc[u][ks]);
+                }
+                load_c(min(c + 1, nchunks - 1), u);
+                const float f = fast_exp2(cs_buf(c)[32 * i + lr]);
+                acc[0] *= f;
+                acc[1] *= f;
+            };
+            auto store_acc = [&](int u) {
+                __bf16* ys = reinterpret_cast<__bf16*>(smem + L::ys) + (u * 4 + ok_) * 32 * L::ystride;
+#pragma unroll
+                for (int v = 0; v < 2; ++v)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        E::st4(ys + lr * L::ystride + 32 * v + 8 * q + 4 * lg, acc[v][4 * q], acc[v][4 * q + 1],
+                               acc[v][4 * q + 2], acc[v][4 * q + 3]);
+            };
+            if (nchunks > 0) {
+                load_c(0, 1);
+                load_c(0, 0);
+            }
+            __syncthreads();
+            __syncthreads();
+            for (int c = 0; c < nchunks; ++c) {
+                left_only(c, 1);
+                store_acc(1);
+                left_only(c, 0);
+                __syncthreads();   // B_mid
+                store_acc(0);
+                __syncthreads();   // B_end
+            }
+            return;
+        }
         if (nchunks > 0) {
             load_c(0, 1);
             load_c(0, 0);
