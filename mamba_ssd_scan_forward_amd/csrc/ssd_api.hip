@@ -37,6 +37,7 @@ struct Plan {
     size_t pass_ws, y2_off;   // workspace of one pass; the second pass's output
     walk_fn_t walk;   // the walk kernel instance for this plan
     walk_fn_t walk_left;   // the second pass of a two-pass d_state (left factors only)
+    void (*walk_pair)(ssd::WalkArgs, ssd::WalkArgs);   // both passes in one launch
     walk_fn_t summary;   // the segment-summary instance (nseg > 1)
 };
 
@@ -121,6 +122,7 @@ int make_plan(const ssd_problem* p, Plan* pl) {
     pl->dtype = p->dtype;
     pl->summary = nullptr;
     pl->walk_left = nullptr;
+    pl->walk_pair = nullptr;
     pl->npass = 1;
     // d_state 256 on the layer-shape walker: the layer is linear in C B^T and its state
     // splits by columns, so it is the sum of two d_state-128 problems on the column
@@ -134,6 +136,18 @@ int make_plan(const ssd_problem* p, Plan* pl) {
         if (qrc != SSD_OK) return qrc;
         pl->npass = 2;
         pl->walk_left = ssd::ssd_walk_split_kernel<128, false, true>;
+        pl->walk_pair = ssd::ssd_walk_split_pair_kernel<128>;
+        // both passes side by side fill twice the compute units: segment only if even
+        // that leaves a partial last round
+        {
+            const int64_t items2 = 2 * p->nseq * p->nheads * (p->headdim / 64);
+            const int64_t tail2 = items2 % kComputeUnits;
+            if (tail2 == 0 || items2 >= kComputeUnits) {
+                pl->nseg = 1;
+                pl->nsplit = 1;
+                pl->ntail = 0;
+            }
+        }
         pl->pass_ws = pl->ws_bytes;
         pl->y2_off = 2 * pl->pass_ws;
         pl->ws_bytes = align_up(pl->y2_off + (size_t)(p->batch * p->seqlen * p->nheads * p->headdim) * 2, 256);
@@ -332,6 +346,7 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
     if (rc != SSD_OK) return rc;
     if (pl.npass == 2) {
         rc = ensure_lds_limit(reinterpret_cast<const void*>(pl.walk_left));
+        if (rc == SSD_OK) rc = ensure_lds_limit(reinterpret_cast<const void*>(pl.walk_pair));
         if (rc != SSD_OK) return rc;
     }
     // packed sequences are walked whole
@@ -427,7 +442,16 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
             hipLaunchKernelGGL(prep, dim3((unsigned)prep_blocks), dim3(kPrepThreads), 0, stream, pa);
         }
     }
-    if (stages & 2) {
+    if ((stages & 2) && pl.npass == 2 && nseg == 1) {
+        // both column halves in one launch
+        ssd::WalkArgs wb;
+        pass_args(0, &pa, &wa);
+        pass_args(1, &pa, &wb);
+        wa.nitems = wa.nwhole;
+        wb.nitems = wb.nwhole;
+        hipLaunchKernelGGL(pl.walk_pair, dim3((unsigned)(wa.nitems + wb.nitems)), dim3(kWalkThreads), pl.lds_bytes,
+                           stream, wa, wb);
+    } else if (stages & 2) {
         for (int k = 0; k < pl.npass; ++k) {
             pass_args(k, &pa, &wa);
             if (nseg > 1) {
@@ -439,13 +463,13 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
             hipLaunchKernelGGL(k == 0 ? walk : pl.walk_left, dim3((unsigned)wa.nitems), dim3(kWalkThreads),
                                pl.lds_bytes, stream, wa);
         }
-        if (pl.npass == 2) {
-            const int64_t n8 = b * T * H * P / 8;
-            const int64_t blocks = (n8 + 255) / 256 < 16384 ? (n8 + 255) / 256 : 16384;
-            hipLaunchKernelGGL(ssd::ssd_add_kernel<__bf16>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                               static_cast<__bf16*>(Y),
-                               reinterpret_cast<const __bf16*>(static_cast<unsigned char*>(workspace) + pl.y2_off), n8);
-        }
+    }
+    if ((stages & 2) && pl.npass == 2) {
+        const int64_t n8 = b * T * H * P / 8;
+        const int64_t blocks = (n8 + 255) / 256 < 16384 ? (n8 + 255) / 256 : 16384;
+        hipLaunchKernelGGL(ssd::ssd_add_kernel<__bf16>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           static_cast<__bf16*>(Y),
+                           reinterpret_cast<const __bf16*>(static_cast<unsigned char*>(workspace) + pl.y2_off), n8);
     }
     if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
     return SSD_OK;

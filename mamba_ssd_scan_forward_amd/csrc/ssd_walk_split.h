@@ -87,8 +87,8 @@ __host__ __device__ constexpr int split_bt_bytes(int N) { return N * 512; }
 // LEFT = true: the output waves compute only the left factors 2^(cs[l]) C_l h of every
 // block (no C B^T chains or diagonal blocks): the second pass of a d_state walked as two
 // column halves, whose within-chunk part the first pass, which sees the full C B^T, holds.
-template <int NP, bool SUMMARY, bool LEFT = false>
-__global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
+template <int NP, bool SUMMARY, bool LEFT>
+__device__ __forceinline__ void walk_split_body(const WalkArgs& a, const int bid, const int nblocks) {
     typedef Elem<__bf16> E;
     typedef bf16x8 frag;
     typedef std::conditional_t<SUMMARY, SummaryLds<NP>, SplitLds<NP>> L;
@@ -107,10 +107,9 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // The whole items and the segments of the tail are remapped to XCDs separately, so
     // that every XCD gets its share of both (dispatch follows the block index).
-    const int bid = blockIdx.x;
-    const int item = (SUMMARY || a.nwhole == 0) ? xcd_remap(bid, gridDim.x)
+    const int item = (SUMMARY || a.nwhole == 0) ? xcd_remap(bid, nblocks)
                      : bid < a.nwhole ? xcd_remap(bid, a.nwhole)
-                                      : a.nwhole + xcd_remap(bid - a.nwhole, gridDim.x - a.nwhole);
+                                      : a.nwhole + xcd_remap(bid - a.nwhole, nblocks - a.nwhole);
     if (item >= a.nitems) return;
     // Work items are the (sequence, head, P tile) triples, gi = (s * H + h) * ptiles + pt.
     // The first nwhole walk their whole sequence; each of the other ntail is walked as
@@ -725,6 +724,21 @@ __global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
             default: output_role(std::integral_constant<int, 3>{}); break;
         }
     }
+}
+
+template <int NP, bool SUMMARY, bool LEFT = false>
+__global__ void __launch_bounds__(512) ssd_walk_split_kernel(WalkArgs a) {
+    walk_split_body<NP, SUMMARY, LEFT>(a, blockIdx.x, gridDim.x);
+}
+
+// Both passes of a d_state walked as two column halves in one launch (they are independent
+// until their outputs are added): blocks [0, a0.nitems) walk the first half, the rest the
+// second (left factors only).  Each range is remapped to the XCDs on its own.
+template <int NP>
+__global__ void __launch_bounds__(512) ssd_walk_split_pair_kernel(WalkArgs a0, WalkArgs a1) {
+    const int bid = blockIdx.x;
+    if (bid < a0.nitems) walk_split_body<NP, false, false>(a0, bid, a0.nitems);
+    else walk_split_body<NP, false, true>(a1, bid - a0.nitems, a1.nitems);
 }
 
 }  // namespace ssd
