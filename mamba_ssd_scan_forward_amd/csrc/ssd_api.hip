@@ -363,7 +363,8 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
     const int64_t NPASS = N / pl.npass;   // state columns of one pass
     auto pass_args = [&](int k, ssd::PrepArgs* ppa, ssd::WalkArgs* pwa) {
         unsigned char* ws = static_cast<unsigned char*>(workspace) + k * pl.pass_ws;
-        float* cs = reinterpret_cast<float*>(ws + pl.cs_off);
+        // the cumsum of logA is the same for both passes: the first pass's serves both
+        float* cs = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + pl.cs_off);
         void* cb = ws + pl.cb_off;
         ssd::PrepArgs& pa = *ppa;
         pa.logA = logA;
@@ -390,6 +391,9 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
         // the first pass's tiles contract all columns (its walk adds the whole
         // within-chunk part); the second pass only needs its fragment copies
         pa.cb_n = k == 0 ? (int)N : 0;
+        // one prep serves both passes: it walks every column for the tiles anyway
+        pa.bt2 = (pl.npass == 2 && k == 0) ? static_cast<unsigned char*>(workspace) + pl.pass_ws + pl.bt_off : nullptr;
+        pa.ct2 = (pl.npass == 2 && k == 0) ? static_cast<unsigned char*>(workspace) + pl.pass_ws + pl.ct_off : nullptr;
 
         ssd::WalkArgs& wa = *pwa;
         wa.X = X;
@@ -437,10 +441,8 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
     ssd::PrepArgs pa;
     ssd::WalkArgs wa;
     if (stages & 1) {
-        for (int k = 0; k < pl.npass; ++k) {
-            pass_args(k, &pa, &wa);
-            hipLaunchKernelGGL(prep, dim3((unsigned)prep_blocks), dim3(kPrepThreads), 0, stream, pa);
-        }
+        pass_args(0, &pa, &wa);
+        hipLaunchKernelGGL(prep, dim3((unsigned)prep_blocks), dim3(kPrepThreads), 0, stream, pa);
     }
     if ((stages & 2) && pl.npass == 2 && nseg == 1) {
         // both column halves in one launch

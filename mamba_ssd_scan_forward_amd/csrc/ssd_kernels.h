@@ -47,6 +47,8 @@ struct PrepArgs {
     int cb_blocks;    // workgroups of the C B^T role: nslots * G
     int ldn, n0;      // B, C rows hold ldn values; the fragment copies take columns [n0, n0 + N)
     int cb_n;         // C B^T contracts columns [0, cb_n) (ldn: all of them), or 0: no tiles
+    void* bt2;        // optional: fragment copies of columns [n0 + N, n0 + 2 N) (the second
+    void* ct2;        // column half of a d_state walked in two passes)
     void* bt;         // optional: B^T of every 256-row chunk in MFMA A-operand fragment
                       // order, [nslots, G, N/32, 8, 2, 64 lanes, 8], and
     void* ct;         // C in MFMA B-operand fragment order, [nslots, G, 8, N/16, 64 lanes,
@@ -253,15 +255,17 @@ __global__ void __launch_bounds__(256, 2) ssd_prep_kernel(PrepArgs a) {
         }
         __syncthreads();
         if constexpr (sizeof(T) == 2) {
-            if (a.bt && n0 >= 0 && n0 < a.N) {
+            const bool second = a.bt2 && n0 >= a.N && n0 < 2 * a.N;
+            if (a.bt && ((n0 >= 0 && n0 < a.N) || second)) {
                 // (c) for the split walker (256-row chunks, this slab = n tile n0 / 32): B^T
                 //     as A-operand fragments, (nt, j, ks) lane (lr, lg) holding
                 //     B[32 j + 16 ks + 8 lg + q][32 nt + lr], and C as B-operand fragments,
                 //     (j, ks) lane (lr, lg) holding C[32 j + lr][16 ks + 8 lg + q]: one
                 //     fragment is 1 KB of contiguous memory
-                const int nt = n0 / 32;
-                T* bto = static_cast<T*>(a.bt) + (int64_t)(k * a.G + g) * (a.N / 32) * 16 * 512;
-                T* cto = static_cast<T*>(a.ct) + (int64_t)(k * a.G + g) * 8 * (a.N / 16) * 512;
+                const int nf = second ? n0 - a.N : n0;   // column within its half
+                const int nt = nf / 32;
+                T* bto = static_cast<T*>(second ? a.bt2 : a.bt) + (int64_t)(k * a.G + g) * (a.N / 32) * 16 * 512;
+                T* cto = static_cast<T*>(second ? a.ct2 : a.ct) + (int64_t)(k * a.G + g) * 8 * (a.N / 16) * 512;
                 for (int o = tid; o < 16 * 64; o += 256) {
                     const int ln = o & 63, f = o >> 6, j = f >> 1, ks = f & 1;
                     frag v;
@@ -269,7 +273,7 @@ __global__ void __launch_bounds__(256, 2) ssd_prep_kernel(PrepArgs a) {
                     for (int q = 0; q < 8; ++q) v[q] = Bs[(32 * j + 16 * ks + 8 * (ln >> 5) + q) * SS + (ln & 31)];
                     *reinterpret_cast<frag*>(bto + ((nt * 8 + j) * 2 + ks) * 512 + ln * 8) = v;
                     const frag w = E::lds8(Cs + (32 * j + (ln & 31)) * SS + 16 * ks + 8 * (ln >> 5));
-                    *reinterpret_cast<frag*>(cto + (j * (a.N / 16) + n0 / 16 + ks) * 512 + ln * 8) = w;
+                    *reinterpret_cast<frag*>(cto + (j * (a.N / 16) + nf / 16 + ks) * 512 + ln * 8) = w;
                 }
             }
         }
