@@ -54,9 +54,9 @@ def kernel_source_hash():
 def walk_kernel_name(w):
     """The walk kernel that the library's planner picks for this workload."""
     if w.dtype == "bf16" and w.chunk_len == 256 and w.dstate in (64, 128) and w.headdim % 64 == 0:
-        return f"ssd_walk_split_kernel<{w.dstate}, false>"
+        return f"ssd_walk_split_kernel<{w.dstate}, false, false>"
     if w.dtype == "bf16" and w.chunk_len == 256 and w.dstate == 256 and w.headdim % 64 == 0:
-        return "ssd_walk_split_kernel<128, false> x 2 passes"
+        return "ssd_walk_split_pair_kernel<128>"
     return "ssd_walk_kernel"
 
 
