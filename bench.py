@@ -15,6 +15,12 @@ counter summary when it was taken on the current kernel source, else null.
 
 ``--mode copy`` runs only a plain device copy of known size; it is the calibration
 program for the FETCH_SIZE / WRITE_SIZE counters.
+
+``--mode report`` prints one JSON line per workload configuration (all of them, or the
+one ``--workload`` names): the median of per-step HIP-event times with the last-level
+cache flushed before every step (a 512 MiB write) and without, the FLOP rates by the
+pages' count and by its causal half, and the fractions of the MFMA peak and of the
+roofline (the parity of each configuration is the full-size tests' business).
 """
 import argparse
 import hashlib
@@ -80,6 +86,15 @@ def flops_pages(w, chunk_lens):
     return f
 
 
+def flops_causal(w, chunk_lens):
+    """The same count with only the causal half of each chunk's Q x Q blocks: q(q+1)/2."""
+    f = 0
+    for q in chunk_lens:
+        tri = q * (q + 1) // 2
+        f += 2 * (w.ngroups * tri * w.dstate + w.nheads * (tri * w.headdim + 2 * q * w.dstate * w.headdim))
+    return f
+
+
 def chunk_lengths(w, lens):
     out = []
     for L in lens:
@@ -99,6 +114,99 @@ def run_copy_mode(steps):
     print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "launches": steps}))
 
 
+def run_report_mode(args):
+    """One JSON line per workload configuration (the measurement table of the layer)."""
+    import numpy as np
+    import torch
+
+    import mamba_ssd_scan_forward_amd as ssd
+    from workloads import CONFIGS, workload_inputs
+
+    names = [args.workload] if args.workload else list(CONFIGS)
+    dev = torch.device("cuda", 0)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    steps = max(args.steps, 1)
+    for name in names:
+        w = CONFIGS[name]
+        inp = workload_inputs(w)
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        es = 2 if w.dtype == "bf16" else 4
+        X = torch.from_numpy(inp.X).to(dt).to(dev)
+        logA = torch.from_numpy(inp.logA).to(dev)
+        B = torch.from_numpy(inp.B).to(dt).to(dev)
+        C = torch.from_numpy(inp.C).to(dt).to(dev)
+        init = None if inp.init is None else torch.from_numpy(inp.init).to(dev)
+        off = None if inp.seq_offsets is None else torch.from_numpy(inp.seq_offsets).to(dev)
+        nseq = w.nseq if w.varlen else w.batch
+        prob = ssd.problem_for(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_len,
+                               nseq, ssd.SSD_DTYPE_BF16 if w.dtype == "bf16" else ssd.SSD_DTYPE_F32)
+        wsb = ssd.ssd_workspace_bytes(prob)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+        Y = torch.empty_like(X)
+        final = torch.empty((nseq, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=dev)
+        stream = torch.cuda.current_stream(dev)
+        ptrs = [X.data_ptr(), logA.data_ptr(), B.data_ptr(), C.data_ptr(),
+                None if init is None else init.data_ptr(), None if off is None else off.data_ptr(),
+                Y.data_ptr(), final.data_ptr(), ws.data_ptr(), wsb, stream.cuda_stream]
+
+        def step():
+            rc = ssd.ssd_forward(prob, *ptrs)
+            if rc != 0:
+                raise ssd.SsdError(rc)
+
+        def timed(cold):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(steps)]
+            for i, (a, b) in enumerate(evs):
+                if cold:
+                    flush.fill_(i & 0xFF)
+                a.record(stream)
+                step()
+                b.record(stream)
+            torch.cuda.synchronize()
+            return statistics.median(a.elapsed_time(b) * 1e3 for a, b in evs)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        warm_us = timed(False)
+        cold_us = timed(True)
+
+        lens = [w.seqlen] * w.batch if not w.varlen else [int(v) for v in np.diff(inp.seq_offsets)]
+        cl = chunk_lengths(w, lens)
+        fp, fc = flops_pages(w, cl), flops_causal(w, cl)
+        abytes = algorithmic_bytes(w, es)
+        peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+        t_roof = max(fp / (peak * 1e12), abytes / (HBM_PEAK_GBS * 1e9)) * 1e6
+        tokens = w.batch * w.seqlen
+        line = {
+            "workload": name, "config": w.shape_dict(), "chunk_len": w.chunk_len,
+            "time_us": round(cold_us, 2), "time_us_warm": round(warm_us, 2),
+            "timing": f"median of {steps} HIP-event-timed steps; 'time_us' with a 512 MiB write "
+                      f"before each step, 'time_us_warm' back to back",
+            "tokens_per_s": round(tokens / (cold_us * 1e-6), 1),
+            "tokens_per_s_warm": round(tokens / (warm_us * 1e-6), 1),
+            "gflop_pages": round(fp / 1e9, 3), "gflop_causal": round(fc / 1e9, 3),
+            "tflops_pages": round(fp / (cold_us * 1e-6) / 1e12, 2),
+            "tflops_causal": round(fc / (cold_us * 1e-6) / 1e12, 2),
+            "frac_mfma_peak": round(fp / (cold_us * 1e-6) / 1e12 / peak, 4),
+            "mfma_peak_tflops": peak,
+            "algorithmic_bytes": abytes,
+            # a problem whose roofline time is below a couple of microseconds is bound by
+            # launch and dependency latency, not by either unit
+            "bound": ("latency" if t_roof < 2.0 else
+                      "hbm" if abytes / (HBM_PEAK_GBS * 1e9) >= fp / (peak * 1e12) else "mfma"),
+            "roofline_us": round(t_roof, 2),
+            "frac_roofline": round(t_roof / cold_us, 4),
+            "frac_roofline_warm": round(t_roof / warm_us, 4),
+        }
+        if w.varlen:
+            line["seq_lengths"] = lens
+        print(json.dumps(line), flush=True)
+        del X, B, C, Y, final, ws, init, off
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,7 +216,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
-    ap.add_argument("--mode", default="bench", choices=["bench", "copy"])
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "report"])
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -117,6 +225,9 @@ def main():
         sys.exit(2)
     if args.mode == "copy":
         run_copy_mode(args.steps)
+        return
+    if args.mode == "report":
+        run_report_mode(args)
         return
 
     import numpy as np
