@@ -15,7 +15,6 @@ namespace {
 
 constexpr int kLdsMax = 160 * 1024;   // LDS per workgroup on gfx950
 constexpr int kWalkThreads = 512;
-constexpr int kPrepThreads = 256;
 constexpr int kComputeUnits = 256;     // MI355X: 8 XCDs x 32 CUs
 
 typedef void (*walk_fn_t)(ssd::WalkArgs);
@@ -442,7 +441,7 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
     ssd::WalkArgs wa;
     if (stages & 1) {
         pass_args(0, &pa, &wa);
-        hipLaunchKernelGGL(prep, dim3((unsigned)prep_blocks), dim3(kPrepThreads), 0, stream, pa);
+        hipLaunchKernelGGL(prep, dim3((unsigned)prep_blocks), dim3(ssd::kPrepThreads), 0, stream, pa);
     }
     if ((stages & 2) && pl.npass == 2 && nseg == 1) {
         // both column halves in one launch

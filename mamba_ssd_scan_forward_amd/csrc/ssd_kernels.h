@@ -140,21 +140,27 @@ __device__ __forceinline__ float wave_inclusive_sum(float x, int lane) {
 
 constexpr int kPrepHeads = 16;   // heads per cumsum workgroup (small LDS tile: the C B^T role
                                  // shares the launch and its occupancy)
+constexpr int kPrepThreads = 512;                 // 8 wavefronts per workgroup
+constexpr int kPrepWaves = kPrepThreads / 64;
 
-// The C B^T role stages the chunk's B and C rows in LDS in slabs of kCbSlab<T> columns
-// (rows padded by 16 bytes): 40 KB for either element type.
-template <typename T> constexpr int kCbSlab = sizeof(T) == 2 ? 32 : 16;
+// The C B^T role stages the chunk's B and C rows in LDS in slabs of kCbSlab<T> columns,
+// 128 bytes of each row (a whole cache line: a narrower slab would leave the rest of the
+// line to be fetched again by the next one when rows are far apart, G > 1); rows padded
+// by 16 bytes: 72 KB for either element type.
+template <typename T> constexpr int kCbSlab = 128 / (int)sizeof(T);
 template <typename T> constexpr int kCbStride = kCbSlab<T> + 16 / (int)sizeof(T);
 template <typename T> constexpr int kPrepLds = 2 * 256 * kCbStride<T> * (int)sizeof(T);
 
 template <typename T>
-__global__ void __launch_bounds__(256, 2) ssd_prep_kernel(PrepArgs a) {
+__global__ void __launch_bounds__(kPrepThreads, 2) ssd_prep_kernel(PrepArgs a) {
     using E = Elem<T>;
     typedef typename E::frag frag;
     static_assert(kPrepLds<T> >= 256 * (kPrepHeads + 1) * 4, "cumsum tile must fit");
     __shared__ __align__(16) unsigned char smem[kPrepLds<T>];
     float (*lt)[kPrepHeads + 1] = reinterpret_cast<float (*)[kPrepHeads + 1]>(smem);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 31, lg = lane >> 5;
+    // (the wavefront index is uniform: in a scalar register, so are the tile coordinates)
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 31, lg = lane >> 5;
     int bid = blockIdx.x;
     const bool cs_role = bid < a.cs_blocks;
     int k, rest;
@@ -175,22 +181,23 @@ __global__ void __launch_bounds__(256, 2) ssd_prep_kernel(PrepArgs a) {
         //     then one wavefront per head: 4 consecutive tokens per lane and a lane scan.
         const int h0 = rest * kPrepHeads;
         const int nh = min(kPrepHeads, a.H - h0);
-        for (int base = 0; base < a.Qp * kPrepHeads; base += 16 * 256) {
-            float v[16];
+        constexpr int per = 256 * kPrepHeads / kPrepThreads;   // values per thread for Qp = 256
+        for (int base = 0; base < a.Qp * kPrepHeads; base += per * kPrepThreads) {
+            float v[per];
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int idx = base + tid + 256 * q;
+            for (int q = 0; q < per; ++q) {
+                const int idx = base + tid + kPrepThreads * q;
                 const int r = idx / kPrepHeads, hh = idx % kPrepHeads;
                 v[q] = (r < len && hh < nh) ? a.logA[(rowc + r) * a.H + h0 + hh] : 0.f;
             }
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int idx = base + tid + 256 * q;
+            for (int q = 0; q < per; ++q) {
+                const int idx = base + tid + kPrepThreads * q;
                 if (idx < a.Qp * kPrepHeads) lt[idx / kPrepHeads][idx % kPrepHeads] = v[q];
             }
         }
         __syncthreads();
-        for (int hh = wave; hh < nh; hh += 4) {
+        for (int hh = wave; hh < nh; hh += kPrepWaves) {
             float v[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) v[j] = (4 * lane + j < a.Qp) ? lt[4 * lane + j][hh] : 0.f;
@@ -217,7 +224,7 @@ __global__ void __launch_bounds__(256, 2) ssd_prep_kernel(PrepArgs a) {
     // at ((s / 16) * 64 + ((s % 16) / 8) * 32 + l) * 8 + s % 8, so one fragment of one
     // wavefront is 1 KB of contiguous memory.
     constexpr int SW = kCbSlab<T>, SS = kCbStride<T>;
-    constexpr int MAXT = 9;   // ceil(36 / 4): tiles per wavefront for 256-row chunks
+    constexpr int MAXT = (36 + kPrepWaves - 1) / kPrepWaves;   // tiles per wavefront, 256-row chunks
     const int g = rest;
     T* Bs = reinterpret_cast<T*>(smem);
     T* Cs = Bs + 256 * SS;
@@ -226,7 +233,7 @@ __global__ void __launch_bounds__(256, 2) ssd_prep_kernel(PrepArgs a) {
     int ti[MAXT], tj[MAXT];
 #pragma unroll
     for (int u = 0; u < MAXT; ++u) {
-        const int t = wave + 4 * u;
+        const int t = wave + kPrepWaves * u;
         int i = 0;
         while ((i + 1) * (i + 2) / 2 <= t) ++i;
         ti[u] = i;
@@ -236,43 +243,65 @@ __global__ void __launch_bounds__(256, 2) ssd_prep_kernel(PrepArgs a) {
 #pragma unroll
     for (int u = 0; u < MAXT; ++u) acc[u] = f32x16{};
     constexpr int pieces = SW * (int)sizeof(T) / 16;   // 16-byte pieces per slab row
+    constexpr int PPT = 256 * pieces / kPrepThreads;   // pieces per thread for 256 rows
     // global columns walked: [0, cb_n) for the tiles, or only the fragment copies' range
     const int col_lo = a.cb_n > 0 ? 0 : a.n0, col_hi = a.cb_n > 0 ? a.cb_n : a.n0 + a.N;
-    for (int cg = col_lo; cg < col_hi; cg += SW) {
-        const int n0 = cg - a.n0;   // column within the fragment copies' range
-        __syncthreads();   // the previous slab has been read
-        for (int idx = tid; idx < a.Qp * pieces; idx += 256) {
+    // One slab's pieces are loaded into registers at once (all of a thread's loads in
+    // flight together), and the next slab's loads are issued before the current slab is
+    // used, so their latency overlaps the MFMAs and the fragment stores.
+    uint4 rb[PPT], rc[PPT];
+    auto load_slab = [&](int cg) {
+#pragma unroll
+        for (int u = 0; u < PPT; ++u) {
+            const int idx = tid + kPrepThreads * u;
             const int r = idx / pieces, c = (idx % pieces) * (16 / (int)sizeof(T));
-            uint4 vb = {0u, 0u, 0u, 0u}, vc = {0u, 0u, 0u, 0u};
+            rb[u] = uint4{0u, 0u, 0u, 0u};
+            rc[u] = uint4{0u, 0u, 0u, 0u};
             // (the widths are multiples of 16, so a 16-byte piece is wholly inside or past)
             if (r < len && cg + c < col_hi) {
                 const int64_t off = (((rowc + r) * a.G + g) * (int64_t)a.ldn + cg + c) * (int64_t)sizeof(T);
-                vb = *reinterpret_cast<const uint4*>(Bp + off);
-                vc = *reinterpret_cast<const uint4*>(Cp + off);
+                rb[u] = *reinterpret_cast<const uint4*>(Bp + off);
+                rc[u] = *reinterpret_cast<const uint4*>(Cp + off);
             }
-            *reinterpret_cast<uint4*>(Bs + r * SS + c) = vb;
-            *reinterpret_cast<uint4*>(Cs + r * SS + c) = vc;
+        }
+    };
+    load_slab(col_lo);
+    for (int cg = col_lo; cg < col_hi; cg += SW) {
+        const int n0 = cg - a.n0;   // column within the fragment copies' range
+        __syncthreads();   // the previous slab has been read
+#pragma unroll
+        for (int u = 0; u < PPT; ++u) {
+            const int idx = tid + kPrepThreads * u;
+            const int r = idx / pieces, c = (idx % pieces) * (16 / (int)sizeof(T));
+            if (r < a.Qp) {
+                *reinterpret_cast<uint4*>(Bs + r * SS + c) = rb[u];
+                *reinterpret_cast<uint4*>(Cs + r * SS + c) = rc[u];
+            }
         }
         __syncthreads();
+        if (cg + SW < col_hi) load_slab(cg + SW);
         if constexpr (sizeof(T) == 2) {
-            const bool second = a.bt2 && n0 >= a.N && n0 < 2 * a.N;
-            if (a.bt && ((n0 >= 0 && n0 < a.N) || second)) {
-                // (c) for the split walker (256-row chunks, this slab = n tile n0 / 32): B^T
-                //     as A-operand fragments, (nt, j, ks) lane (lr, lg) holding
-                //     B[32 j + 16 ks + 8 lg + q][32 nt + lr], and C as B-operand fragments,
-                //     (j, ks) lane (lr, lg) holding C[32 j + lr][16 ks + 8 lg + q]: one
-                //     fragment is 1 KB of contiguous memory
-                const int nf = second ? n0 - a.N : n0;   // column within its half
-                const int nt = nf / 32;
-                T* bto = static_cast<T*>(second ? a.bt2 : a.bt) + (int64_t)(k * a.G + g) * (a.N / 32) * 16 * 512;
-                T* cto = static_cast<T*>(second ? a.ct2 : a.ct) + (int64_t)(k * a.G + g) * 8 * (a.N / 16) * 512;
-                for (int o = tid; o < 16 * 64; o += 256) {
-                    const int ln = o & 63, f = o >> 6, j = f >> 1, ks = f & 1;
+            // (c) for the split walker (256-row chunks; the slab holds n tiles n0 / 32 and
+            //     n0 / 32 + 1): B^T as A-operand fragments, (nt, j, ks) lane (lr, lg)
+            //     holding B[32 j + 16 ks + 8 lg + q][32 nt + lr], and C as B-operand
+            //     fragments, (j, ks) lane (lr, lg) holding C[32 j + lr][16 ks + 8 lg + q]:
+            //     one fragment is 1 KB of contiguous memory
+            if (a.bt) {
+                for (int o = tid; o < (SW / 32) * 16 * 64; o += kPrepThreads) {
+                    const int sub = o >> 10, ln = o & 63, f = (o >> 6) & 15, j = f >> 1, ks = f & 1;
+                    const int ns = n0 + 32 * sub;   // the n tile's first column within the copies' range
+                    const bool second = a.bt2 && ns >= a.N && ns < 2 * a.N;
+                    if (!((ns >= 0 && ns < a.N) || second)) continue;
+                    const int nf = second ? ns - a.N : ns;   // column within its half
+                    const int nt = nf / 32;
+                    T* bto = static_cast<T*>(second ? a.bt2 : a.bt) + (int64_t)(k * a.G + g) * (a.N / 32) * 16 * 512;
+                    T* cto = static_cast<T*>(second ? a.ct2 : a.ct) + (int64_t)(k * a.G + g) * 8 * (a.N / 16) * 512;
                     frag v;
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) v[q] = Bs[(32 * j + 16 * ks + 8 * (ln >> 5) + q) * SS + (ln & 31)];
+                    for (int q = 0; q < 8; ++q)
+                        v[q] = Bs[(32 * j + 16 * ks + 8 * (ln >> 5) + q) * SS + 32 * sub + (ln & 31)];
                     *reinterpret_cast<frag*>(bto + ((nt * 8 + j) * 2 + ks) * 512 + ln * 8) = v;
-                    const frag w = E::lds8(Cs + (32 * j + (ln & 31)) * SS + 16 * ks + 8 * (ln >> 5));
+                    const frag w = E::lds8(Cs + (32 * j + (ln & 31)) * SS + 32 * sub + 16 * ks + 8 * (ln >> 5));
                     *reinterpret_cast<frag*>(cto + (j * (a.N / 16) + nf / 16 + ks) * 512 + ln * 8) = w;
                 }
             }
@@ -280,7 +309,7 @@ __global__ void __launch_bounds__(256, 2) ssd_prep_kernel(PrepArgs a) {
         if (a.cb_n == 0) continue;
 #pragma unroll
         for (int u = 0; u < MAXT; ++u) {
-            if (wave + 4 * u >= a.ntile) break;
+            if (wave + kPrepWaves * u >= a.ntile) break;
 #pragma unroll
             for (int ks = 0; ks < SW / 16; ++ks) {
                 const frag av = E::lds8(Bs + (32 * tj[u] + lr) * SS + 16 * ks + 8 * lg);
@@ -292,7 +321,7 @@ __global__ void __launch_bounds__(256, 2) ssd_prep_kernel(PrepArgs a) {
     if (a.cb_n == 0) return;
 #pragma unroll
     for (int u = 0; u < MAXT; ++u) {
-        const int t = wave + 4 * u;
+        const int t = wave + kPrepWaves * u;
         if (t >= a.ntile) break;
         T* out = static_cast<T*>(a.cb) + ((int64_t)(k * a.G + g) * a.ntile + t) * 1024;
         if (ti[u] == tj[u]) {
