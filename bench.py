@@ -46,7 +46,7 @@ def log(*a):
 
 # the sources of the forward kernels and of their launch plan (the backward pass's files
 # are not among them)
-FORWARD_SOURCES = ("ssd_device.h", "ssd_kernels.h", "ssd_walk_split.h", "ssd_api.hip")
+FORWARD_SOURCES = ("ssd_device.h", "ssd_kernels.h", "ssd_walk_split.h", "ssd_walk_quad.h", "ssd_api.hip")
 
 
 def kernel_source_hash():
@@ -60,6 +60,10 @@ def kernel_source_hash():
 def walk_kernel_name(w):
     """The walk kernel that the library's planner picks for this workload."""
     if w.dtype == "bf16" and w.chunk_len == 256 and w.dstate in (64, 128) and w.headdim % 64 == 0:
+        hpg = w.nheads // w.ngroups
+        nseq = w.nseq if w.varlen else w.batch
+        if w.headdim == 64 and hpg >= 2 and nseq * w.ngroups * ((hpg + 3) // 4) >= 128:
+            return f"ssd_walk_quad_kernel<{w.dstate}, 1>"
         return f"ssd_walk_split_kernel<{w.dstate}, false, false>"
     if w.dtype == "bf16" and w.chunk_len == 256 and w.dstate == 256 and w.headdim % 64 == 0:
         return "ssd_walk_split_pair_kernel<128>"

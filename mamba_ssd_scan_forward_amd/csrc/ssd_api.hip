@@ -9,6 +9,7 @@
 #include "ssd.h"
 #include "ssd_kernels.h"
 #include "ssd_walk_split.h"
+#include "ssd_walk_quad.h"
 #include "ssd_backward.h"
 
 namespace {
@@ -16,6 +17,12 @@ namespace {
 constexpr int kLdsMax = 160 * 1024;   // LDS per workgroup on gfx950
 constexpr int kWalkThreads = 512;
 constexpr int kComputeUnits = 256;     // MI355X: 8 XCDs x 32 CUs
+// the quad walker's 32-wide p sub-tiles per wavefront: 1 = two wavefronts per head, two
+// per SIMD (2 = one wavefront per head)
+#ifndef SSD_QUAD_PW
+#define SSD_QUAD_PW 1
+#endif
+constexpr int kQuadPW = SSD_QUAD_PW;
 
 typedef void (*walk_fn_t)(ssd::WalkArgs);
 
@@ -38,6 +45,9 @@ struct Plan {
     walk_fn_t walk_left;   // the second pass of a two-pass d_state (left factors only)
     void (*walk_pair)(ssd::WalkArgs, ssd::WalkArgs);   // both passes in one launch
     walk_fn_t summary;   // the segment-summary instance (nseg > 1)
+    int quad;         // the four-heads-per-workgroup walker (and its prep options)
+    int quads;        // its workgroups per group
+    size_t xflag_off; // its per-(chunk, head) flags of very steep decay
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -115,10 +125,12 @@ walk_fn pick_walk_bf16(int PT, int NP, bool cbl) {
 
 // Workspace and launch plan.  `nseq_total` slots: batch mode has batch * ceil(T/Q)
 // chunks; a packed batch has at most ceil(T/Q) + nseq (one ragged chunk per sequence).
-int make_plan(const ssd_problem* p, Plan* pl) {
+int make_plan(const ssd_problem* p, Plan* pl, bool allow_quad = true) {
     const int rc = check_problem(p);
     if (rc != SSD_OK) return rc;
     pl->dtype = p->dtype;
+    pl->quad = 0;
+    pl->quads = 0;
     pl->summary = nullptr;
     pl->walk_left = nullptr;
     pl->walk_pair = nullptr;
@@ -131,7 +143,7 @@ int make_plan(const ssd_problem* p, Plan* pl) {
     if (p->dtype == SSD_DTYPE_BF16 && p->chunk_len == 256 && p->dstate == 256 && p->headdim % 64 == 0) {
         ssd_problem q = *p;
         q.dstate = 128;
-        const int qrc = make_plan(&q, pl);
+        const int qrc = make_plan(&q, pl, false);
         if (qrc != SSD_OK) return qrc;
         pl->npass = 2;
         pl->walk_left = ssd::ssd_walk_split_kernel<128, false, true>;
@@ -238,6 +250,28 @@ int make_plan(const ssd_problem* p, Plan* pl) {
             pl->lds_bytes = ssd::SplitLds<128>::bytes;
             pl->summary_lds = ssd::SummaryLds<128>::bytes;
         }
+        // Head dimension 64 with several heads per group: four heads per workgroup share
+        // one load of the group's operands, when the (sequence, group, quad) workgroups
+        // fill at least half of the compute units without segmenting (the quad walker
+        // walks whole sequences).
+        const int64_t hpg = p->nheads / p->ngroups;
+        const int64_t nq = (hpg + 3) / 4;
+        const int64_t qitems = p->nseq * p->ngroups * nq;
+        // (its loads address the workspace from the C B^T tiles to the end of the C
+        // fragments, and the cumsum, with 32-bit offsets)
+        const bool small_ws = pl->seg_off - pl->cb_off < ((size_t)1 << 31) && cs_bytes < ((size_t)1 << 31);
+        if (allow_quad && P == 64 && hpg >= 2 && qitems >= kComputeUnits / 2 && small_ws) {
+            pl->quad = 1;
+            pl->quads = (int)nq;
+            pl->nitems = qitems;
+            pl->nseg = 1;
+            pl->nsplit = 1;
+            pl->ntail = 0;
+            pl->walk = N == 64 ? ssd::ssd_walk_quad_kernel<64, kQuadPW> : ssd::ssd_walk_quad_kernel<128, kQuadPW>;
+            pl->xflag_off = pl->ws_bytes;
+            pl->ws_bytes = align_up(pl->xflag_off + (size_t)pl->nslots * p->nheads * sizeof(int), 256);
+            pl->lds_bytes = 0;   // static LDS
+        }
     }
     return SSD_OK;
 }
@@ -341,7 +375,8 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
     walk_fn walk = pl.walk;
     prep_fn prep = p->dtype == SSD_DTYPE_BF16 ? ssd::ssd_prep_kernel<__bf16>
                                               : ssd::ssd_prep_kernel<float>;
-    rc = ensure_lds_limit(reinterpret_cast<const void*>(walk));
+    // (the quad walker's LDS is static: no dynamic LDS to allow)
+    rc = pl.quad ? SSD_OK : ensure_lds_limit(reinterpret_cast<const void*>(walk));
     if (rc != SSD_OK) return rc;
     if (pl.npass == 2) {
         rc = ensure_lds_limit(reinterpret_cast<const void*>(pl.walk_left));
@@ -393,6 +428,10 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
         // one prep serves both passes: it walks every column for the tiles anyway
         pa.bt2 = (pl.npass == 2 && k == 0) ? static_cast<unsigned char*>(workspace) + pl.pass_ws + pl.bt_off : nullptr;
         pa.ct2 = (pl.npass == 2 && k == 0) ? static_cast<unsigned char*>(workspace) + pl.pass_ws + pl.ct_off : nullptr;
+        // the quad walker takes C in its accumulator-row K order and only diagonal tiles
+        pa.ct_perm = pl.quad;
+        pa.cb_diag = pl.quad;
+        pa.xflag = pl.quad ? reinterpret_cast<int*>(static_cast<unsigned char*>(workspace) + pl.xflag_off) : nullptr;
 
         ssd::WalkArgs& wa = *pwa;
         wa.X = X;
@@ -434,6 +473,8 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
         wa.lpt = (pl.split && seq_offsets && p->nseq <= 64 && (p->nseq * G) % 8 == 0) ? 1 : 0;
         wa.seg_state = reinterpret_cast<float*>(ws + pl.seg_off);
         wa.seg_decay = reinterpret_cast<float*>(ws + pl.segd_off);
+        wa.quads = pl.quads;
+        wa.xflag = pa.xflag;
     };
     const int64_t prep_blocks = nslots * ((H + ssd::kPrepHeads - 1) / ssd::kPrepHeads) + nslots * G;
     if (prep_blocks > INT32_MAX) return SSD_ERR_UNSUPPORTED;
@@ -461,7 +502,7 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
                                    stream, wa);
             }
             wa.nitems = wa.nwhole + wa.ntail * nseg;
-            hipLaunchKernelGGL(k == 0 ? walk : pl.walk_left, dim3((unsigned)wa.nitems), dim3(kWalkThreads),
+            hipLaunchKernelGGL(k == 0 ? walk : pl.walk_left, dim3((unsigned)wa.nitems), dim3(pl.quad ? 512 / kQuadPW : kWalkThreads),
                                pl.lds_bytes, stream, wa);
         }
     }

@@ -266,3 +266,23 @@ def test_full_size_config(name):
     ey, ef = rel_err(Y, Yr), rel_err(F, Fr)
     print(f"[parity]   {name}: max_rel_err_Y {ey:.3e} max_rel_err_final {ef:.3e}", flush=True)
     assert ey <= TOL[w.dtype] and ef <= TOL[w.dtype], (ey, ef)
+
+
+# Shapes that fill at least half of the chip with (sequence, group, quad of heads)
+# workgroups, so the library walks them four heads per workgroup: ragged chunks with
+# an initial state; d_state 64 with groups of six heads (the second quad of a group
+# half empty); a packed batch with empty and length-1 sequences (longest-first dealing);
+# strong decay, where most 32-row blocks take the exact-mask path.
+@pytest.mark.parametrize("case", ["ragged_init", "state64_partial_quads", "packed", "strong_decay"])
+def test_quad_walker(case):
+    if case == "ragged_init":
+        inp = make_inputs(32, 300, 16, 64, 128, 1, "bf16", seed=1300, init_state=True)
+    elif case == "state64_partial_quads":
+        inp = make_inputs(32, 520, 12, 64, 64, 2, "bf16", seed=1301, init_state=True)
+    elif case == "packed":
+        lens = [1, 0, 300, 257, 5, 1200, 256, 31, 0, 700, 64, 129, 2, 500, 33, 522]
+        inp = make_inputs(1, sum(lens), 80, 64, 128, 8, "bf16", seed=1302, init_state=True, seq_lengths=lens)
+    else:
+        inp = make_inputs(32, 300, 16, 64, 128, 1, "bf16", seed=1303, init_state=True)
+        inp.logA = (inp.logA * 40.0).astype(np.float32)
+    check(inp, 256, case)
