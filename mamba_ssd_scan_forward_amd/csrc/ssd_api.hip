@@ -48,6 +48,7 @@ struct Plan {
     int quad;         // the four-heads-per-workgroup walker (and its prep options)
     int quads;        // its workgroups per group
     size_t xflag_off; // its per-(chunk, head) flags of very steep decay
+    size_t dx_off;    // its per-row decays to the end of the row's 32-row block
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -259,7 +260,7 @@ int make_plan(const ssd_problem* p, Plan* pl, bool allow_quad = true) {
         const int64_t qitems = p->nseq * p->ngroups * nq;
         // (its loads address the workspace from the C B^T tiles to the end of the C
         // fragments, and the cumsum, with 32-bit offsets)
-        const bool small_ws = pl->seg_off - pl->cb_off < ((size_t)1 << 31) && cs_bytes < ((size_t)1 << 31);
+        const bool small_ws = pl->seg_off - pl->cb_off < ((size_t)1 << 31) && pl->ws_bytes + cs_bytes < ((size_t)1 << 31);
         if (allow_quad && P == 64 && hpg >= 2 && qitems >= kComputeUnits / 2 && small_ws) {
             pl->quad = 1;
             pl->quads = (int)nq;
@@ -269,7 +270,8 @@ int make_plan(const ssd_problem* p, Plan* pl, bool allow_quad = true) {
             pl->ntail = 0;
             pl->walk = N == 64 ? ssd::ssd_walk_quad_kernel<64, kQuadPW> : ssd::ssd_walk_quad_kernel<128, kQuadPW>;
             pl->xflag_off = pl->ws_bytes;
-            pl->ws_bytes = align_up(pl->xflag_off + (size_t)pl->nslots * p->nheads * sizeof(int), 256);
+            pl->dx_off = align_up(pl->xflag_off + (size_t)pl->nslots * p->nheads * sizeof(int), 256);
+            pl->ws_bytes = align_up(pl->dx_off + cs_bytes, 256);
             pl->lds_bytes = 0;   // static LDS
         }
     }
@@ -432,6 +434,7 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
         pa.ct_perm = pl.quad;
         pa.cb_diag = pl.quad;
         pa.xflag = pl.quad ? reinterpret_cast<int*>(static_cast<unsigned char*>(workspace) + pl.xflag_off) : nullptr;
+        pa.dx = pl.quad ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + pl.dx_off) : nullptr;
 
         ssd::WalkArgs& wa = *pwa;
         wa.X = X;
@@ -475,6 +478,7 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
         wa.seg_decay = reinterpret_cast<float*>(ws + pl.segd_off);
         wa.quads = pl.quads;
         wa.xflag = pa.xflag;
+        wa.dx = pa.dx;
     };
     const int64_t prep_blocks = nslots * ((H + ssd::kPrepHeads - 1) / ssd::kPrepHeads) + nslots * G;
     if (prep_blocks > INT32_MAX) return SSD_ERR_UNSUPPORTED;

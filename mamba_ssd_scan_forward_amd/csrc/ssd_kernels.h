@@ -57,6 +57,7 @@ struct PrepArgs {
     int cb_diag;      // compute and store only the diagonal tiles (i, i)
     int* xflag;       // optional: [nslots, H], whether the chunk has a 32-row block whose
                       // cumsum falls by more than 100 (log2 units) from its first row to its last
+    float* dx;        // optional: [nslots, H, Qp], 2^(cs[last row of the row's 32-row block] - cs[row])
 };
 
 struct WalkArgs {
@@ -81,6 +82,7 @@ struct WalkArgs {
     int ldn, ns0;       // init / final state rows hold ldn values; this call's are [ns0, ns0 + N)
     int quads;          // quad walker: workgroups (quads of heads) per group
     const int* xflag;   // quad walker: [nslots, H] chunks with a block of very steep decay
+    const float* dx;    // quad walker: [nslots, H, 256] decay of each row to its 32-row block's end
     int64_t T;
     int H, P, N, G, Q, Qp, ntile, nseq, ptiles, nitems, qb;
     int cb_lds;                                    // stage off-diagonal C B^T tiles in LDS
@@ -214,6 +216,13 @@ __global__ void __launch_bounds__(kPrepThreads, 2) ssd_prep_kernel(PrepArgs a) {
             const f32x4 o = {(excl + v[0]) * kLog2e, (excl + v[1]) * kLog2e, (excl + v[2]) * kLog2e,
                              (excl + v[3]) * kLog2e};
             if (4 * lane < a.Qp) *reinterpret_cast<f32x4*>(a.cs + ((int64_t)k * a.H + h0 + hh) * a.Qp + 4 * lane) = o;
+            if (a.dx) {
+                // the decay of each row to the end of its 32-row block (lane 8 j + 7 holds
+                // that row of block j)
+                const float eb = __shfl(o[3], (lane & ~7) + 7, 64);
+                const f32x4 d = {fast_exp2(eb - o[0]), fast_exp2(eb - o[1]), fast_exp2(eb - o[2]), fast_exp2(eb - o[3])};
+                if (4 * lane < a.Qp) *reinterpret_cast<f32x4*>(a.dx + ((int64_t)k * a.H + h0 + hh) * a.Qp + 4 * lane) = d;
+            }
             if (a.xflag) {
                 // block j's rows are lanes 8 j .. 8 j + 7: first row o[0] of lane 8 j, last
                 // row o[3] of lane 8 j + 7 (the same stored values the walker compares)

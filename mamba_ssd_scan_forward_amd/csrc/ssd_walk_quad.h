@@ -39,7 +39,7 @@ namespace ssd {
 
 // LDS of the quad walker: a ring of four slots, each with the block's shared fragments
 // (B^T [N/16], C [N/16], diagonal C B^T [2], 1 KB each), the four heads' X rows
-// [4][32][64] (swizzled) and their cumsums [4][64] (rows 32..63 repeat 0..31); per wave
+// [4][32][64] (swizzled) and their rows' cumsums and decays to the block's end [4][2][32]; per wave
 // its Y tile on the way to global memory [32][32 PW + 8].  The slots are separate
 // arrays, so that the compiler can tell a slot being filled (by direct-to-LDS loads)
 // from the slot being read.
@@ -336,8 +336,11 @@ __device__ __forceinline__ void quad_walk(const WalkArgs& a, unsigned char* ring
     // X: lane i of each 1 KB piece fills 16-byte unit i % 8 of row 8 q + i / 8, which
     // holds column unit (i % 8) ^ swz(row); swz depends on row % 4 = (i / 8) % 4 only
     const uint32_t xlane = opaque((uint32_t)(((lane >> 3) * XH + xhi) * 64 + 8 * ((lane & 7) ^ XL::swz(lane >> 3))) * 2);
+    // cumsum (lanes 0..31) and per-row decays to the block's end (lanes 32..63) of the
+    // block's rows, in one load: the decays' array lies after the cumsum's in the workspace
     const rsrc_t csr = make_rsrc(a.cs, 0xFFFFFFFFu);
-    const uint32_t cslane = opaque(4u * lr);
+    const uint32_t cslane =
+        opaque(4u * lr + (lg ? (uint32_t)(reinterpret_cast<const char*>(a.dx) - reinterpret_cast<const char*>(a.cs)) : 0u));
     auto issue = [&](int b, auto kc) __attribute__((always_inline)) {
         b = min(b, nb - 1);
         const int c = b >> 3, j = b & 7;
@@ -363,8 +366,8 @@ __device__ __forceinline__ void quad_walk(const WalkArgs& a, unsigned char* ring
             const int q = (wave % WPH) + WPH * i;
             load_lds16(xrs, xs + q * 1024, xlane + (uint32_t)((32 * j + 8 * q) * XH * 64 * 2));
         }
-        // the cumsum of the block's rows (lanes 32..63 repeat them; the waves of a head
-        // write the same bytes)
+        // the cumsum and the decays of the block's rows (the waves of a head write the
+        // same bytes)
         load_lds4(csr, sb + L::cs + hw * 256, cslane, (((uint32_t)sl * H + h) * 256 + 32 * j) * 4);
     };
 
@@ -429,18 +432,19 @@ __device__ __forceinline__ void quad_walk(const WalkArgs& a, unsigned char* ring
             if constexpr (PW == 1) x_frags_tr(base + 2u * (uint32_t)XL::idx(row, col), xf);
             else x_frags_tr(base + 2u * (uint32_t)XL::idx(row, col), base + 2u * (uint32_t)XL::idx(row, col + 32), xf);
         }
-        // X~' = X 2^(e - cs[s] - lsig): X~ divided by the state's scale (lsig after this block)
+        // X~' = X 2^(e - cs[s] - lsig): X~ divided by the state's scale (lsig after this
+        // block), from the rows' decays to the block's end 2^(e - cs[s]) (prep kernel)
         auto scale_x = [&](frag (&xt)[PW][2]) __attribute__((always_inline)) {
+            const float isig = fast_exp2(-lsig);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const f32x4 c0 = *reinterpret_cast<const f32x4*>(csb + 16 * ks + 8 * lg);
-                const f32x4 c1 = *reinterpret_cast<const f32x4*>(csb + 16 * ks + 8 * lg + 4);
-                const float eo = e - lsig;
+                const f32x4 c0 = *reinterpret_cast<const f32x4*>(csb + 32 + 16 * ks + 8 * lg);
+                const f32x4 c1 = *reinterpret_cast<const f32x4*>(csb + 32 + 16 * ks + 8 * lg + 4);
                 float fs[8];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    fs[q] = fast_exp2(eo - c0[q]);
-                    fs[4 + q] = fast_exp2(eo - c1[q]);
+                    fs[q] = c0[q] * isig;
+                    fs[4 + q] = c1[q] * isig;
                 }
 #pragma unroll
                 for (int v = 0; v < PW; ++v)
