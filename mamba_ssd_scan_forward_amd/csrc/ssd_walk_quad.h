@@ -79,20 +79,26 @@ __device__ __forceinline__ void load_lds4(rsrc_t r, void* dst, uint32_t voff, ui
 
 // The transposing LDS reads of one block's X operand fragments, per p sub-tile v: two
 // K-steps x two 4-row halves from a[v] (rows + 4 are 512 bytes on, K-step 1 is 2048 bytes
-// on: row + 16 keeps the swizzle).  One asm block that waits for its own reads before it
+// on: row + 16 keeps the swizzle), and the four 4-value pieces of the rows' decays
+// (rows 8 lg + 16 ks + 0..7 from d0).  One asm block that waits for its own reads before it
 // ends (its results are complete when the compiler sees them), and that the compiler's
 // wait-count analysis does not take for a read of the slots being filled by
 // direct-to-LDS loads (it would wait for all of them).
-__device__ __forceinline__ void x_frags_tr(uint32_t a0, bf16x8 (&xf)[1][2]) {
+__device__ __forceinline__ void x_frags_tr(uint32_t a0, uint32_t d0, bf16x8 (&xf)[1][2], f32x4 (&dxr)[2][2]) {
     u32x2 r[4];
     asm volatile(
-        "ds_read_b64_tr_b16 %0, %4\n"
-        "ds_read_b64_tr_b16 %1, %4 offset:512\n"
-        "ds_read_b64_tr_b16 %2, %4 offset:2048\n"
-        "ds_read_b64_tr_b16 %3, %4 offset:2560\n"
+        "ds_read_b128 %4, %9\n"
+        "ds_read_b128 %5, %9 offset:16\n"
+        "ds_read_b128 %6, %9 offset:64\n"
+        "ds_read_b128 %7, %9 offset:80\n"
+        "ds_read_b64_tr_b16 %0, %8\n"
+        "ds_read_b64_tr_b16 %1, %8 offset:512\n"
+        "ds_read_b64_tr_b16 %2, %8 offset:2048\n"
+        "ds_read_b64_tr_b16 %3, %8 offset:2560\n"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-        : "v"(a0)
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(dxr[0][0]), "=&v"(dxr[0][1]), "=&v"(dxr[1][0]),
+          "=&v"(dxr[1][1])
+        : "v"(a0), "v"(d0)
         : "memory");
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -100,20 +106,26 @@ __device__ __forceinline__ void x_frags_tr(uint32_t a0, bf16x8 (&xf)[1][2]) {
         xf[0][ks] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
 }
-__device__ __forceinline__ void x_frags_tr(uint32_t a0, uint32_t a1, bf16x8 (&xf)[2][2]) {
+__device__ __forceinline__ void x_frags_tr(uint32_t a0, uint32_t a1, uint32_t d0, bf16x8 (&xf)[2][2],
+                                           f32x4 (&dxr)[2][2]) {
     u32x2 r[8];
     asm volatile(
-        "ds_read_b64_tr_b16 %0, %8\n"
-        "ds_read_b64_tr_b16 %1, %8 offset:512\n"
-        "ds_read_b64_tr_b16 %2, %8 offset:2048\n"
-        "ds_read_b64_tr_b16 %3, %8 offset:2560\n"
-        "ds_read_b64_tr_b16 %4, %9\n"
-        "ds_read_b64_tr_b16 %5, %9 offset:512\n"
-        "ds_read_b64_tr_b16 %6, %9 offset:2048\n"
-        "ds_read_b64_tr_b16 %7, %9 offset:2560\n"
+        "ds_read_b128 %8, %14\n"
+        "ds_read_b128 %9, %14 offset:16\n"
+        "ds_read_b128 %10, %14 offset:64\n"
+        "ds_read_b128 %11, %14 offset:80\n"
+        "ds_read_b64_tr_b16 %0, %12\n"
+        "ds_read_b64_tr_b16 %1, %12 offset:512\n"
+        "ds_read_b64_tr_b16 %2, %12 offset:2048\n"
+        "ds_read_b64_tr_b16 %3, %12 offset:2560\n"
+        "ds_read_b64_tr_b16 %4, %13\n"
+        "ds_read_b64_tr_b16 %5, %13 offset:512\n"
+        "ds_read_b64_tr_b16 %6, %13 offset:2048\n"
+        "ds_read_b64_tr_b16 %7, %13 offset:2560\n"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-        : "v"(a0), "v"(a1)
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+          "=&v"(dxr[0][0]), "=&v"(dxr[0][1]), "=&v"(dxr[1][0]), "=&v"(dxr[1][1])
+        : "v"(a0), "v"(a1), "v"(d0)
         : "memory");
 #pragma unroll
     for (int v = 0; v < 2; ++v)
@@ -421,6 +433,10 @@ __device__ __forceinline__ void quad_walk(const WalkArgs& a, unsigned char* ring
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
             dg[ks] = E::lds8(reinterpret_cast<const __bf16*>(sb + L::cb + ks * 1024) + 8 * lane);
+        // the rows' decays to the block's end: 2^(e - cs[s]) for s = 16 ks + 8 lg + q (read
+        // with X below)
+        f32x4 dxr[2][2];
+        const float cs0 = csb[0];
         const __bf16* xs = reinterpret_cast<const __bf16*>(sb + L::x + hw * 32 * 64 * 2);
         // X of the block as operand fragments: lane holds X[16 ks + 8 lg + q][32 (ps0 + v) + lr]
         // (the addressing of LdsCol: lane i of each 16 reads 4 elements of row i / 4)
@@ -429,8 +445,11 @@ __device__ __forceinline__ void quad_walk(const WalkArgs& a, unsigned char* ring
             const int row = 8 * lg + ((lane & 15) >> 2);
             const int col = 32 * ps0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
             const uint32_t base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) __bf16*)xs;
-            if constexpr (PW == 1) x_frags_tr(base + 2u * (uint32_t)XL::idx(row, col), xf);
-            else x_frags_tr(base + 2u * (uint32_t)XL::idx(row, col), base + 2u * (uint32_t)XL::idx(row, col + 32), xf);
+            const uint32_t d0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float*)(csb + 32 + 8 * lg);
+            if constexpr (PW == 1) x_frags_tr(base + 2u * (uint32_t)XL::idx(row, col), d0, xf, dxr);
+            else
+                x_frags_tr(base + 2u * (uint32_t)XL::idx(row, col), base + 2u * (uint32_t)XL::idx(row, col + 32), d0, xf,
+                           dxr);
         }
         // X~' = X 2^(e - cs[s] - lsig): X~ divided by the state's scale (lsig after this
         // block), from the rows' decays to the block's end 2^(e - cs[s]) (prep kernel)
@@ -438,8 +457,7 @@ __device__ __forceinline__ void quad_walk(const WalkArgs& a, unsigned char* ring
             const float isig = fast_exp2(-lsig);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const f32x4 c0 = *reinterpret_cast<const f32x4*>(csb + 32 + 16 * ks + 8 * lg);
-                const f32x4 c1 = *reinterpret_cast<const f32x4*>(csb + 32 + 16 * ks + 8 * lg + 4);
+                const f32x4 c0 = dxr[ks][0], c1 = dxr[ks][1];
                 float fs[8];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -458,7 +476,7 @@ __device__ __forceinline__ void quad_walk(const WalkArgs& a, unsigned char* ring
         frag xt[PW][2];
         // The block's row span R = cs[first row] - e decides the path (uniform).
         bool moderate = true;
-        if constexpr (EXACT) moderate = __builtin_amdgcn_readfirstlane((int)(csb[0] - e <= 100.f)) != 0;
+        if constexpr (EXACT) moderate = __builtin_amdgcn_readfirstlane((int)(cs0 - e <= 100.f)) != 0;
         if (!EXACT || moderate) {
             // ---- moderate span (every block of Mamba-2's parameter ranges).  The state's
             // scale becomes lsig + dlt while that stays above 2^-64; otherwise g is first
