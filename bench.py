@@ -62,8 +62,16 @@ def walk_kernel_name(w):
     if w.dtype == "bf16" and w.chunk_len == 256 and w.dstate in (64, 128) and w.headdim % 64 == 0:
         hpg = w.nheads // w.ngroups
         nseq = w.nseq if w.varlen else w.batch
-        if w.headdim == 64 and hpg >= 2 and nseq * w.ngroups * ((hpg + 3) // 4) >= 128:
-            return f"ssd_walk_quad_kernel<{w.dstate}, 1>"
+        it4 = nseq * w.ngroups * ((hpg + 3) // 4)
+        if w.headdim == 64 and hpg >= 2 and it4 >= 128:
+            hq = 4
+            if hpg >= 3:
+                it3 = nseq * w.ngroups * ((hpg + 2) // 3)
+                if w.varlen:
+                    hq = 3 if 85 * it3 < 100 * it4 else 4
+                else:
+                    hq = 3 if 85 * -(-it3 // 256) < 100 * -(-it4 // 256) else 4
+            return f"ssd_walk_quad_kernel<{w.dstate}, 1, {hq}>"
         return f"ssd_walk_split_kernel<{w.dstate}, false, false>"
     if w.dtype == "bf16" and w.chunk_len == 256 and w.dstate == 256 and w.headdim % 64 == 0:
         return "ssd_walk_split_pair_kernel<128>"

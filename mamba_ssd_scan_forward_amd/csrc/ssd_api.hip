@@ -45,7 +45,7 @@ struct Plan {
     walk_fn_t walk_left;   // the second pass of a two-pass d_state (left factors only)
     void (*walk_pair)(ssd::WalkArgs, ssd::WalkArgs);   // both passes in one launch
     walk_fn_t summary;   // the segment-summary instance (nseg > 1)
-    int quad;         // the four-heads-per-workgroup walker (and its prep options)
+    int quad;         // heads per workgroup of the quad walker (3 or 4; 0: not used)
     int quads;        // its workgroups per group
     size_t xflag_off; // its per-(chunk, head) flags of very steep decay
     size_t dx_off;    // its per-row decays to the end of the row's 32-row block
@@ -256,19 +256,37 @@ int make_plan(const ssd_problem* p, Plan* pl, bool allow_quad = true) {
         // fill at least half of the compute units without segmenting (the quad walker
         // walks whole sequences).
         const int64_t hpg = p->nheads / p->ngroups;
-        const int64_t nq = (hpg + 3) / 4;
-        const int64_t qitems = p->nseq * p->ngroups * nq;
+        const int64_t qitems = p->nseq * p->ngroups * ((hpg + 3) / 4);
+        // Three heads per workgroup instead of four: more, smaller workgroups.  One of
+        // three heads walks a block in about 0.85 of the time of one of four (measured at
+        // d_state 128); it is taken when that shortens the estimated walk: the rounds of
+        // workgroups over the compute units for sequences of one length, the total work
+        // for packed sequences.
+        int hq = 4;
+        if (hpg >= 3) {
+            const int64_t it3 = p->nseq * p->ngroups * ((hpg + 2) / 3);
+            const int64_t cost4 = p->nseq == p->batch ? 100 * ((qitems + kComputeUnits - 1) / kComputeUnits) : 100 * qitems;
+            const int64_t cost3 = p->nseq == p->batch ? 85 * ((it3 + kComputeUnits - 1) / kComputeUnits) : 85 * it3;
+            if (cost3 < cost4) hq = 3;
+        }
+        const int64_t nq = (hpg + hq - 1) / hq;
         // (its loads address the workspace from the C B^T tiles to the end of the C
         // fragments, and the cumsum, with 32-bit offsets)
         const bool small_ws = pl->seg_off - pl->cb_off < ((size_t)1 << 31) && pl->ws_bytes + cs_bytes < ((size_t)1 << 31);
-        if (allow_quad && P == 64 && hpg >= 2 && qitems >= kComputeUnits / 2 && small_ws) {
-            pl->quad = 1;
+        // (its prep writes each block's B^T, C and diagonal C B^T fragments together, over
+        // the C B^T, B^T and C arrays: [nslots, G, 8, N/8 + 2 KB])
+        const bool fits = (size_t)pl->nslots * p->ngroups * 8 * (N / 8 + 2) * 1024 <= pl->seg_off - pl->cb_off;
+        if (allow_quad && P == 64 && hpg >= 2 && qitems >= kComputeUnits / 2 && small_ws && fits) {
+            pl->quad = hq;
             pl->quads = (int)nq;
-            pl->nitems = qitems;
+            pl->nitems = p->nseq * p->ngroups * nq;
             pl->nseg = 1;
             pl->nsplit = 1;
             pl->ntail = 0;
-            pl->walk = N == 64 ? ssd::ssd_walk_quad_kernel<64, kQuadPW> : ssd::ssd_walk_quad_kernel<128, kQuadPW>;
+            if (hq == 3)
+                pl->walk = N == 64 ? ssd::ssd_walk_quad_kernel<64, kQuadPW, 3> : ssd::ssd_walk_quad_kernel<128, kQuadPW, 3>;
+            else
+                pl->walk = N == 64 ? ssd::ssd_walk_quad_kernel<64, kQuadPW, 4> : ssd::ssd_walk_quad_kernel<128, kQuadPW, 4>;
             pl->xflag_off = pl->ws_bytes;
             pl->dx_off = align_up(pl->xflag_off + (size_t)pl->nslots * p->nheads * sizeof(int), 256);
             pl->ws_bytes = align_up(pl->dx_off + cs_bytes, 256);
@@ -431,8 +449,9 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
         pa.bt2 = (pl.npass == 2 && k == 0) ? static_cast<unsigned char*>(workspace) + pl.pass_ws + pl.bt_off : nullptr;
         pa.ct2 = (pl.npass == 2 && k == 0) ? static_cast<unsigned char*>(workspace) + pl.pass_ws + pl.ct_off : nullptr;
         // the quad walker takes C in its accumulator-row K order and only diagonal tiles
-        pa.ct_perm = pl.quad;
-        pa.cb_diag = pl.quad;
+        pa.ct_perm = pl.quad != 0;
+        pa.cb_diag = pl.quad != 0;
+        pa.qlay = pl.quad != 0;
         pa.xflag = pl.quad ? reinterpret_cast<int*>(static_cast<unsigned char*>(workspace) + pl.xflag_off) : nullptr;
         pa.dx = pl.quad ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + pl.dx_off) : nullptr;
 
@@ -506,7 +525,7 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
                                    stream, wa);
             }
             wa.nitems = wa.nwhole + wa.ntail * nseg;
-            hipLaunchKernelGGL(k == 0 ? walk : pl.walk_left, dim3((unsigned)wa.nitems), dim3(pl.quad ? 512 / kQuadPW : kWalkThreads),
+            hipLaunchKernelGGL(k == 0 ? walk : pl.walk_left, dim3((unsigned)wa.nitems), dim3(pl.quad ? 128 * pl.quad / kQuadPW : kWalkThreads),
                                pl.lds_bytes, stream, wa);
         }
     }

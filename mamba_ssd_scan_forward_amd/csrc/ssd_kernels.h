@@ -55,6 +55,10 @@ struct PrepArgs {
                       // 8]; written by the C B^T role (bf16 only)
     int ct_perm;      // C fragments in the K order of a 32 x 32 accumulator's rows (below)
     int cb_diag;      // compute and store only the diagonal tiles (i, i)
+    int qlay;         // (with ct_perm and cb_diag) each 32-row block's fragments together
+                      // in the cb array instead: [nslots, G, 8, N/16 + N/16 + 2, 64 lanes, 8]
+                      // (B^T fragments (n tile, K-step), C fragments, the diagonal tile's two
+                      // K-steps), so that a block's shared operands are one run of memory
     int* xflag;       // optional: [nslots, H], whether the chunk has a 32-row block whose
                       // cumsum falls by more than 100 (log2 units) from its first row to its last
     float* dx;        // optional: [nslots, H, Qp], 2^(cs[last row of the row's 32-row block] - cs[row])
@@ -325,11 +329,12 @@ __global__ void __launch_bounds__(kPrepThreads, 2) ssd_prep_kernel(PrepArgs a) {
                     const int nt = nf / 32;
                     T* bto = static_cast<T*>(second ? a.bt2 : a.bt) + (int64_t)(k * a.G + g) * (a.N / 32) * 16 * 512;
                     T* cto = static_cast<T*>(second ? a.ct2 : a.ct) + (int64_t)(k * a.G + g) * 8 * (a.N / 16) * 512;
+                    T* qo = static_cast<T*>(a.cb) + ((int64_t)(k * a.G + g) * 8 + j) * (a.N / 8 + 2) * 512;
                     frag v;
 #pragma unroll
                     for (int q = 0; q < 8; ++q)
                         v[q] = Bs[(32 * j + 16 * ks + 8 * (ln >> 5) + q) * SS + 32 * sub + (ln & 31)];
-                    *reinterpret_cast<frag*>(bto + ((nt * 8 + j) * 2 + ks) * 512 + ln * 8) = v;
+                    *reinterpret_cast<frag*>((a.qlay ? qo + (2 * nt + ks) * 512 : bto + ((nt * 8 + j) * 2 + ks) * 512) + ln * 8) = v;
                     frag w;
                     if (a.ct_perm) {
                         // element q of lane (lr, lg) is column 16 ks + 8 (q / 4) + 4 lg + q % 4:
@@ -343,7 +348,8 @@ __global__ void __launch_bounds__(kPrepThreads, 2) ssd_prep_kernel(PrepArgs a) {
                     } else {
                         w = E::lds8(Cs + (32 * j + (ln & 31)) * SS + 32 * sub + 16 * ks + 8 * (ln >> 5));
                     }
-                    *reinterpret_cast<frag*>(cto + (j * (a.N / 16) + nf / 16 + ks) * 512 + ln * 8) = w;
+                    *reinterpret_cast<frag*>((a.qlay ? qo + (a.N / 16 + nf / 16 + ks) * 512 : cto + (j * (a.N / 16) + nf / 16 + ks) * 512) +
+                                             ln * 8) = w;
                 }
             }
         }
@@ -364,7 +370,8 @@ __global__ void __launch_bounds__(kPrepThreads, 2) ssd_prep_kernel(PrepArgs a) {
     for (int u = 0; u < MAXT; ++u) {
         const int t = tt[u];
         if (t >= a.ntile) break;
-        T* out = static_cast<T*>(a.cb) + ((int64_t)(k * a.G + g) * a.ntile + t) * 1024;
+        T* out = a.qlay ? static_cast<T*>(a.cb) + (((int64_t)(k * a.G + g) * 8 + ti[u]) * (a.N / 8 + 2) + a.N / 8) * 512
+                        : static_cast<T*>(a.cb) + ((int64_t)(k * a.G + g) * a.ntile + t) * 1024;
         if (ti[u] == tj[u]) {
             // diagonal tiles carry the causal mask: (C B^T)_{ls} = 0 for s > l
 #pragma unroll

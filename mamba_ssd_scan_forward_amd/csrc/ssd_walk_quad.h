@@ -43,16 +43,16 @@ namespace ssd {
 // its Y tile on the way to global memory [32][32 PW + 8].  The slots are separate
 // arrays, so that the compiler can tell a slot being filled (by direct-to-LDS loads)
 // from the slot being read.
-template <int NP, int PW> struct QuadLds {
+template <int NP, int PW, int HQ> struct QuadLds {
     static constexpr int nsh = NP / 8 + 2;
     static constexpr int bt = 0;
     static constexpr int ct = NP / 16 * 1024;
     static constexpr int cb = NP / 8 * 1024;
     static constexpr int x = nsh * 1024;
-    static constexpr int cs = x + 4 * 32 * 64 * 2;
-    static constexpr int slot = cs + 4 * 64 * 4;
+    static constexpr int cs = x + HQ * 32 * 64 * 2;
+    static constexpr int slot = cs + HQ * 64 * 4;
     static constexpr int nslot = 4;
-    static constexpr int nwave = 8 / PW;
+    static constexpr int nwave = 2 * HQ / PW;
     static constexpr int ystride = 32 * PW + 8;
     static constexpr int ybytes = nwave * 32 * ystride * 2;
     static_assert(nslot * slot + ybytes <= 160 * 1024, "LDS");
@@ -263,21 +263,20 @@ __device__ __forceinline__ void quad_exact_block(f32x16 (&hacc)[NT][PW], f32x16 
 
 // The walk of one work item (sequence s, group g, quad qd) over the LDS ring r0..r3 and
 // the Y staging area ystage.  EXACT: whether a block of very steep decay may come.
-template <int NP, int PW, bool EXACT>
+template <int NP, int PW, int HQ, bool EXACT>
 __device__ __forceinline__ void quad_walk(const WalkArgs& a, unsigned char* ring0, unsigned char* ring1,
                                           unsigned char* ring2, unsigned char* ring3, __bf16* ystage, int s, int g,
                                           int qd) {
     typedef Elem<__bf16> E;
     typedef bf16x8 frag;
-    typedef QuadLds<NP, PW> L;
+    typedef QuadLds<NP, PW, HQ> L;
     typedef LdsMat<__bf16, 64> XL;
     constexpr int NT = NP / 32;            // n tiles of the state
-    constexpr int NKK = NP / 16;           // K-steps over n
     constexpr int WPH = 2 / PW;            // waves per head
-    constexpr int NW = 4 * WPH;            // waves per workgroup
+    constexpr int NW = HQ * WPH;           // waves per workgroup
     constexpr int XQ = 4 / WPH;            // 1 KB pieces of its head's X rows loaded by one wave
     constexpr int D = 3;                   // blocks in flight ahead of the one computed
-    constexpr int LPS = 2 * ((NP / 16 + NW - 1) / NW) + 1 + XQ + 1;   // vector memory loads per step (per wave)
+    constexpr int LPS = (L::nsh + NW - 1) / NW + XQ + 1;   // vector memory loads per step (per wave)
     constexpr int SPS = 2 * PW;            // vector memory stores per step
     constexpr int YS = L::ystride;
     static_assert(L::nslot >= D + 1, "ring");
@@ -295,7 +294,7 @@ __device__ __forceinline__ void quad_walk(const WalkArgs& a, unsigned char* ring
     const int ps0 = (wave % WPH) * PW;     // first p sub-tile of this wave
     const int H = a.H, G = a.G, hpg = H / G;
 
-    const int hl = 4 * qd + hw;
+    const int hl = HQ * qd + hw;
     const bool valid = hl < hpg;
     const int h = g * hpg + (valid ? hl : hpg - 1);
 
@@ -315,8 +314,6 @@ __device__ __forceinline__ void quad_walk(const WalkArgs& a, unsigned char* ring
     const int nb = 8 * nchunks;   // 32-row blocks (a ragged chunk is walked in full)
 
     const __bf16* X = static_cast<const __bf16*>(a.X);
-    const __bf16* BTg = static_cast<const __bf16*>(a.bt);
-    const __bf16* CTg = static_cast<const __bf16*>(a.ct);
     const __bf16* CBg = static_cast<const __bf16*>(a.cb);
     __bf16* Y = static_cast<__bf16*>(a.Y);
     const int XH = a.xh, xhi = h / (H / XH);   // X row of this head
@@ -324,27 +321,23 @@ __device__ __forceinline__ void quad_walk(const WalkArgs& a, unsigned char* ring
 
     // ---- block min(b, nb - 1)'s share of this wave, global memory -> LDS slot b % 4
     //      (LPS loads; a block past the end loads the last one, into a slot nobody
-    //      reads).  The shared fragments come through one descriptor over the workspace
-    //      from the C B^T tiles to the end of the C fragments (the workspace holds them
-    //      in that order, within 2 GiB): this wave's B^T fragments (n tile f / 2, K-step
-    //      f % 2), C fragments (K-step f) and diagonal-tile K-step, f = wave + NW i
-    //      (a wave past the last fragment loads the last one again, to the same place,
-    //      with the same bytes: every wave issues the same loads).  The wave's part of
-    //      each offset is in the vector offset, the block's in the scalar offset.
+    //      reads).  The block's shared operands -- N/16 B^T fragments (n tile f / 2,
+    //      K-step f % 2), N/16 C fragments (K-step f) and the diagonal C B^T tile's two
+    //      K-steps, 1 KB each -- are one run of memory, in the slot's order (prep kernel);
+    //      wave w loads pieces w + NW i (a wave past the last piece loads the last one
+    //      again, to the same place, with the same bytes: every wave issues the same
+    //      loads).  The wave's part of each offset is in the vector offset, the block's in
+    //      the scalar offset.
     const rsrc_t wsr = make_rsrc(CBg, 0xFFFFFFFFu);
-    const uint32_t bt_rel = (uint32_t)(reinterpret_cast<const char*>(BTg) - reinterpret_cast<const char*>(CBg));
-    const uint32_t ct_rel = (uint32_t)(reinterpret_cast<const char*>(CTg) - reinterpret_cast<const char*>(CBg));
-    constexpr int NF = (NKK + NW - 1) / NW;   // B^T (and C) fragments per wave
-    uint32_t vbt[NF], vct[NF];
-    int fbt[NF];
+    constexpr int NSH = L::nsh;                 // shared 1 KB pieces of a block
+    constexpr int NI = (NSH + NW - 1) / NW;     // of them loaded by one wave
+    int pk[NI];
+    uint32_t pv[NI];
 #pragma unroll
-    for (int i = 0; i < NF; ++i) {
-        fbt[i] = wave + NW * i < NKK ? wave + NW * i : NKK - 1;
-        vbt[i] = opaque(16u * lane + bt_rel + (uint32_t)(((fbt[i] >> 1) * 16 + (fbt[i] & 1)) * 1024));
-        vct[i] = opaque(16u * lane + ct_rel + (uint32_t)(fbt[i] * 1024));
+    for (int i = 0; i < NI; ++i) {
+        pk[i] = min(wave + NW * i, NSH - 1);
+        pv[i] = opaque(16u * lane + (uint32_t)(pk[i] * 1024));
     }
-    const int fcb = wave < 1 ? wave : 1;
-    const uint32_t vcb = opaque(16u * lane + (uint32_t)(fcb * 1024));
     // X: lane i of each 1 KB piece fills 16-byte unit i % 8 of row 8 q + i / 8, which
     // holds column unit (i % 8) ^ swz(row); swz depends on row % 4 = (i / 8) % 4 only
     const uint32_t xlane = opaque((uint32_t)(((lane >> 3) * XH + xhi) * 64 + 8 * ((lane & 7) ^ XL::swz(lane >> 3))) * 2);
@@ -358,15 +351,9 @@ __device__ __forceinline__ void quad_walk(const WalkArgs& a, unsigned char* ring
         const int c = b >> 3, j = b & 7;
         const int sl = slot0 + c;
         unsigned char* sb = ring(kc);
-        const uint32_t unit = (uint32_t)(sl * G + g);
-        const uint32_t sfr = unit * (uint32_t)split_bt_bytes(NP);
+        const uint32_t sq = ((uint32_t)(sl * G + g) * 8 + j) * (uint32_t)(NSH * 1024);
 #pragma unroll
-        for (int i = 0; i < NF; ++i)
-            load_lds16(wsr, sb + L::bt + fbt[i] * 1024, vbt[i], sfr + (uint32_t)(2 * j * 1024));
-#pragma unroll
-        for (int i = 0; i < NF; ++i)
-            load_lds16(wsr, sb + L::ct + fbt[i] * 1024, vct[i], sfr + (uint32_t)(j * NKK * 1024));
-        load_lds16(wsr, sb + L::cb + fcb * 1024, vcb, unit * (uint32_t)(a.ntile * 2048) + (uint32_t)(j * (j + 3) * 1024));
+        for (int i = 0; i < NI; ++i) load_lds16(wsr, sb + pk[i] * 1024, pv[i], sq);
         // X rows 8 q .. 8 q + 7 of the block (this wave's share of q; rows past the
         // chunk's end read as zeros: buffer range)
         const int64_t rowc = row0 + (int64_t)c * 256;
@@ -628,17 +615,17 @@ __device__ __forceinline__ void quad_walk(const WalkArgs& a, unsigned char* ring
 // The steep instance of the walk, not inlined: the common one keeps the kernel's registers
 // (this one reaches the LDS ring through pointers, which costs it the overlap of its loads
 // with the walk; it only runs where the decay is far beyond Mamba-2's parameter ranges).
-template <int NP, int PW>
+template <int NP, int PW, int HQ>
 __device__ __noinline__ void quad_walk_steep(WalkArgs a, unsigned char* r0, unsigned char* r1, unsigned char* r2,
                                              unsigned char* r3, __bf16* ys, int s, int g, int qd) {
-    quad_walk<NP, PW, true>(a, r0, r1, r2, r3, ys, s, g, qd);
+    quad_walk<NP, PW, HQ, true>(a, r0, r1, r2, r3, ys, s, g, qd);
 }
 
-template <int NP, int PW>
-__global__ void __launch_bounds__(512 / PW, 2 / PW) ssd_walk_quad_kernel(WalkArgs a) {
-    typedef QuadLds<NP, PW> L;
+template <int NP, int PW, int HQ>
+__global__ void __launch_bounds__(128 * HQ / PW, 2 / PW) ssd_walk_quad_kernel(WalkArgs a) {
+    typedef QuadLds<NP, PW, HQ> L;
     constexpr int WPH = 2 / PW;            // waves per head
-    constexpr int NW = 4 * WPH;            // waves per workgroup
+    constexpr int NW = HQ * WPH;           // waves per workgroup
     __shared__ __align__(16) unsigned char ring0[L::slot], ring1[L::slot], ring2[L::slot], ring3[L::slot];
     __shared__ __align__(16) __bf16 ystage[L::ybytes / 2];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -682,7 +669,7 @@ __global__ void __launch_bounds__(512 / PW, 2 / PW) ssd_walk_quad_kernel(WalkArg
     // written by the prep kernel's cumsum role; each wave votes into the Y staging area,
     // unused until the walk starts)
     {
-        const int hl = 4 * qd + hw;
+        const int hl = HQ * qd + hw;
         const int h = g * hpg + (hl < hpg ? hl : hpg - 1);
         int slot0, nchunks;
         if (!a.seq_offsets) {
@@ -703,11 +690,11 @@ __global__ void __launch_bounds__(512 / PW, 2 / PW) ssd_walk_quad_kernel(WalkArg
         for (int w = 0; w < NW; ++w) steep |= vote[w];
         __syncthreads();
         if (steep) {
-            quad_walk_steep<NP, PW>(a, ring0, ring1, ring2, ring3, ystage, s, g, qd);
+            quad_walk_steep<NP, PW, HQ>(a, ring0, ring1, ring2, ring3, ystage, s, g, qd);
             return;
         }
     }
-    quad_walk<NP, PW, false>(a, ring0, ring1, ring2, ring3, ystage, s, g, qd);
+    quad_walk<NP, PW, HQ, false>(a, ring0, ring1, ring2, ring3, ystage, s, g, qd);
 }
 
 }  // namespace ssd
