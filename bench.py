@@ -9,8 +9,9 @@ on stdout; progress goes to stderr.
 Roofline: the dominant launch is the chunk walk.  Its algorithmic bytes are the
 minimum traffic of the layer: read X, B, C and logA once, write Y and the final state
 once (the per-token figure times the tokens of one launch, plus the states).  Its
-duration is measured here with HIP events around launches of that stage alone on the
-stream it runs on.  HBM traffic measured by counters is read from the committed
+duration is measured here with HIP events on the stream it runs on, one pair around
+each walk launch of a run of whole steps (the launch from the prep's end to its last
+workgroup's, as a kernel trace times it).  HBM traffic measured by counters is read from the committed
 counter summary when it was taken on the current kernel source, else null.
 
 ``--mode copy`` runs only a plain device copy of known size; it is the calibration
@@ -309,8 +310,20 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         stage_ms[k] = e0.elapsed_time(e1) / args.steps
+    # the walk launch's own duration inside whole steps (prep, then walk): an event after
+    # each stage, so the interval covers the walk from the prep's end to its own last
+    # workgroup (what a kernel trace reports per launch; back to back, as above, the tail
+    # of one walk launch overlaps the start of the next)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a_, b_ in ev:
+        stage(1)
+        a_.record(stream)
+        stage(2)
+        b_.record(stream)
+    torch.cuda.synchronize()
+    walk_in_step_ms = statistics.mean(a_.elapsed_time(b_) for a_, b_ in ev)
     log(f"[bench] step {ms_step * 1e3:.1f} us; prep {stage_ms[1] * 1e3:.1f} us; "
-        f"walk {stage_ms[2] * 1e3:.1f} us")
+        f"walk {stage_ms[2] * 1e3:.1f} us back to back, {walk_in_step_ms * 1e3:.1f} us per launch in steps")
 
     # the recurrent decode step (one token per sequence, state updated in place) at the
     # same sequences, heads and sizes; HBM-bound on the float32 state
@@ -379,7 +392,7 @@ def main():
     abytes = algorithmic_bytes(w, es)
     tok_s = tokens / (ms_step * 1e-3)
     peak_mm = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
-    achieved_gbs = abytes / (stage_ms[2] * 1e-3) / 1e9
+    achieved_gbs = abytes / (walk_in_step_ms * 1e-3) / 1e9
 
     traffic = None
     if os.path.exists(COUNTERS_JSON):
@@ -406,7 +419,8 @@ def main():
         "config": dict(workload=name, **w.shape_dict()),
         "tflops_pages": round(fl / (ms_step * 1e-3) / 1e12, 2),
         "mfma_util_pages": round(fl / (ms_step * 1e-3) / 1e12 / peak_mm, 4),
-        "stage_us": {"prep": round(stage_ms[1] * 1e3, 2), "walk": round(stage_ms[2] * 1e3, 2)},
+        "stage_us": {"prep": round(stage_ms[1] * 1e3, 2), "walk": round(stage_ms[2] * 1e3, 2),
+                     "walk_per_launch_in_steps": round(walk_in_step_ms * 1e3, 2)},
         "roofline": {
             "kernel": walk_kernel_name(w),
             "bound": "hbm",

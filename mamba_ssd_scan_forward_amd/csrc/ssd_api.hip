@@ -251,10 +251,10 @@ int make_plan(const ssd_problem* p, Plan* pl, bool allow_quad = true) {
             pl->lds_bytes = ssd::SplitLds<128>::bytes;
             pl->summary_lds = ssd::SummaryLds<128>::bytes;
         }
-        // Head dimension 64 with several heads per group: four heads per workgroup share
-        // one load of the group's operands, when the (sequence, group, quad) workgroups
-        // fill at least half of the compute units without segmenting (the quad walker
-        // walks whole sequences).
+        // Head dimension 64 with several heads per group: three or four heads per
+        // workgroup share one load of the group's operands, when the workgroups of four
+        // heads fill at least half of the compute units without segmenting (the quad
+        // walker walks whole sequences).
         const int64_t hpg = p->nheads / p->ngroups;
         const int64_t qitems = p->nseq * p->ngroups * ((hpg + 3) / 4);
         // Three heads per workgroup instead of four: more, smaller workgroups.  One of

@@ -1,12 +1,13 @@
-// ssd_walk_quad.h -- the chunk walker with four heads per workgroup, for bf16 operands,
-// 256-row chunks, head dimension 64 and d_state 64 or 128 (page "Transformers are SSMs"
-// paper summary, sections 6 and 6.2; heads of a group share B and C, section 7.2).
+// ssd_walk_quad.h -- the chunk walker with HQ = 3 or 4 heads per workgroup (the "quad"
+// walker), for bf16 operands, 256-row chunks, head dimension 64 and d_state 64 or 128
+// (page "Transformers are SSMs" paper summary, sections 6 and 6.2; heads of a group share
+// B and C, section 7.2).
 //
-// One workgroup per (sequence, group, quad of heads of the group); each head's 64
-// columns of P are split over 2 / PW wavefronts (PW = 32-wide p sub-tiles per wave), and
-// a wave keeps its part of the head's state h^T (N x 32 PW, float32) in MFMA
-// accumulators for the whole sequence.  (The waves of the last quad of a group whose
-// heads are used up shadow the group's last head and store nothing.)
+// One workgroup per (sequence, group, HQ heads of the group); each head's 64 columns of
+// P are split over 2 / PW wavefronts (PW = 32-wide p sub-tiles per wave), and a wave
+// keeps its part of the head's state h^T (N x 32 PW, float32) in MFMA accumulators for
+// the whole sequence.  (The waves of the last workgroup of a group whose heads are used
+// up shadow the group's last head and store nothing.)
 //
 // The walk goes block by block (32 rows), and each block's output comes from the state
 // at the end of the previous block instead of from the earlier blocks' C B^T tiles:
@@ -24,10 +25,10 @@
 // 2^(cs[l] - cs[s]) (C B^T)_ls on unscaled X instead.  Every other factor is <= 1.
 //
 // The operands the heads of a group share (B^T and C of the block in MFMA fragment
-// order, and the diagonal C B^T tile: written by the prep kernel) are loaded once per
-// workgroup: each wavefront loads a quarter of them, and of its own head's X, into
-// registers four blocks ahead, writes them to a two-slot LDS ring one block ahead, and
-// one barrier per block hands the slot over.  The state accumulator converts to the A
+// order, and the diagonal C B^T tile: one run of memory per block, written by the prep
+// kernel) are loaded once per workgroup: the waves deal the 1 KB pieces among themselves
+// and each loads its share of its own head's X, straight from global memory into a
+// four-slot LDS ring three blocks ahead; one barrier per block hands a slot over.  The state accumulator converts to the A
 // operand of the left factor without moving data between lanes: a lane holds rows
 // 8 (e / 4) + 4 lg + e % 4 of a 32 x 32 accumulator, and the prep kernel writes C's
 // fragments with the contraction index in that order.
@@ -38,9 +39,10 @@
 namespace ssd {
 
 // LDS of the quad walker: a ring of four slots, each with the block's shared fragments
-// (B^T [N/16], C [N/16], diagonal C B^T [2], 1 KB each), the four heads' X rows
-// [4][32][64] (swizzled) and their rows' cumsums and decays to the block's end [4][2][32]; per wave
-// its Y tile on the way to global memory [32][32 PW + 8].  The slots are separate
+// (B^T [N/16], C [N/16], diagonal C B^T [2], 1 KB each, in the order of their run in
+// memory), the HQ heads' X rows [HQ][32][64] (swizzled) and their rows' cumsums and
+// decays to the block's end [HQ][2][32]; per wave its Y tile on the way to global memory
+// [32][32 PW + 8].  The slots are separate
 // arrays, so that the compiler can tell a slot being filled (by direct-to-LDS loads)
 // from the slot being read.
 template <int NP, int PW, int HQ> struct QuadLds {
