@@ -127,6 +127,83 @@ def run_copy_mode(steps):
     print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "launches": steps}))
 
 
+def clocks_mhz(stamps):
+    """Shader clock of each workgroup from its (s_memtime, s_memrealtime) stamps at start
+    and end (the real-time counter runs at 100 MHz)."""
+    import numpy as np
+    t = stamps.reshape(-1, 4).astype(np.float64)
+    return (t[:, 2] - t[:, 0]) / np.maximum(t[:, 3] - t[:, 1], 1.0) * 100.0
+
+
+def measure_machine(walk, stream, dev):
+    """The roofline constants as this chip reaches them (libssd_probe.so): the dense bf16
+    MFMA rate and the clock under it, a 512 MiB device copy, and the clock while the walk
+    kernel runs (a one-wave-per-workgroup sampler on a second stream beside five walk
+    launches, bracketed on the walk's stream by two one-workgroup markers)."""
+    import ctypes
+    import numpy as np
+    import torch
+    import mamba_ssd_scan_forward_amd as ssd
+    probe = ssd.load_probe_library()
+    cus, khz = ctypes.c_int(0), ctypes.c_int(0)
+    if probe.ssd_probe_device(ctypes.byref(cus), ctypes.byref(khz)) != 0:
+        raise RuntimeError("ssd_probe_device failed")
+    sp = stream.cuda_stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # MFMA: two workgroups of four waves per CU
+    blocks, iters = 2 * cus.value, 40000
+    st = torch.zeros(4 * blocks, dtype=torch.int64, device=dev)
+    for rep in range(3):   # (the first launch warms up)
+        e0.record(stream)
+        assert probe.ssd_probe_mfma_bf16(iters, blocks, st.data_ptr(), sp) == 0
+        e1.record(stream)
+        torch.cuda.synchronize()
+    mfma_s = e0.elapsed_time(e1) * 1e-3
+    mfma_tflops = blocks * 4 * 4 * iters * 32768 / mfma_s / 1e12
+    mfma_clk = float(np.mean(clocks_mhz(st.cpu().numpy())))
+    # copy
+    n = 512 << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    # the clock while the walk runs
+    side = torch.cuda.Stream(device=dev)
+    nsamp = 32
+    samp = torch.zeros(4 * nsamp, dtype=torch.int64, device=dev)
+    marks = torch.zeros(8, dtype=torch.int64, device=dev)
+    assert probe.ssd_probe_clock(1, nsamp, samp.data_ptr(), side.cuda_stream) == 0   # (first use of the stream)
+    torch.cuda.synchronize()
+    first = torch.cuda.Event()
+    assert probe.ssd_probe_clock(1, 1, marks.data_ptr(), sp) == 0
+    walk()
+    first.record(stream)
+    for _ in range(4):
+        walk()
+    assert probe.ssd_probe_clock(1, 1, marks.data_ptr() + 32, sp) == 0
+    # the sampler starts when the first walk launch has ended, during the second
+    side.wait_event(first)
+    assert probe.ssd_probe_clock(3000, nsamp, samp.data_ptr(), side.cuda_stream) == 0
+    torch.cuda.synchronize()
+    sv, mv = samp.cpu().numpy(), marks.cpu().numpy()
+    t = sv.reshape(-1, 4)
+    inside = bool(t[:, 1].min() >= mv[3] and t[:, 3].max() <= mv[5])
+    log(f"[bench] clock sampler: starts {(t[:, 1].min() - mv[3]) / 100:.1f} us after the walks' first marker, "
+        f"ends {(mv[5] - t[:, 3].max()) / 100:.1f} us before their last; walks span {(mv[5] - mv[3]) / 100:.1f} us")
+    walk_clk = float(np.mean(clocks_mhz(sv))) if inside else None
+    return {"compute_units": cus.value, "max_clock_mhz": khz.value / 1000.0,
+            "mfma_bf16_tflops": round(mfma_tflops, 1), "mfma_clock_mhz": round(mfma_clk, 0),
+            "hbm_copy_gbs": round(copy_gbs, 1),
+            "walk_clock_mhz": None if walk_clk is None else round(walk_clk, 0),
+            "walk_clock_window_inside_walks": inside}
+
+
 def run_report_mode(args):
     """One JSON line per workload configuration (the measurement table of the layer)."""
     import numpy as np
@@ -229,6 +306,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-machine", action="store_true",
+                    help="skip the machine measurements (MFMA rate, copy bandwidth, clocks)")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy", "report"])
     args = ap.parse_args()
 
@@ -386,6 +465,11 @@ def main():
         log(f"[bench] backward {us:.1f} us")
         del outs, bws
 
+    machine = None
+    if not args.no_machine:
+        machine = measure_machine(lambda: stage(2), stream, dev)
+        log(f"[bench] machine: {machine}")
+
     lens = [w.seqlen] * w.batch if not w.varlen else list(np.diff(inp.seq_offsets))
     tokens = w.batch * w.seqlen
     fl = flops_pages(w, chunk_lengths(w, [int(v) for v in lens]))
@@ -433,6 +517,13 @@ def main():
         },
     }
 
+    if machine is not None:
+        # the same rates against what the chip reaches: the walk's FLOPs per launch over
+        # the measured dense bf16 rate, its clock against the clock under that rate
+        machine["walk_tflops_pages"] = round(fl / (walk_in_step_ms * 1e-3) / 1e12, 1)
+        machine["walk_frac_of_measured_mfma"] = round(machine["walk_tflops_pages"] / machine["mfma_bf16_tflops"], 4)
+        machine["walk_frac_of_measured_copy"] = round(achieved_gbs / machine["hbm_copy_gbs"], 4)
+        result["measured_peaks"] = machine
     if dec is not None:
         result["decode"] = dec
     if bwd is not None:

@@ -96,6 +96,34 @@ def load_library():
     return lib
 
 
+_probe = None
+
+
+def probe_lib_path() -> str:
+    return os.path.join(_HERE, "libssd_probe.so")
+
+
+def load_probe_library():
+    """Load libssd_probe.so (machine measurements, include/ssd_probe.h).  Raises if it has
+    not been built."""
+    global _probe
+    if _probe is not None:
+        return _probe
+    path = probe_lib_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m mamba_ssd_scan_forward_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.ssd_probe_mfma_bf16.argtypes = [i64, ci, vp, vp]
+    lib.ssd_probe_mfma_bf16.restype = ci
+    lib.ssd_probe_clock.argtypes = [i64, ci, vp, vp]
+    lib.ssd_probe_clock.restype = ci
+    lib.ssd_probe_device.argtypes = [ctypes.POINTER(ci), ctypes.POINTER(ci)]
+    lib.ssd_probe_device.restype = ci
+    _probe = lib
+    return lib
+
+
 def ssd_status_string(status: int) -> str:
     return load_library().ssd_status_string(int(status)).decode()
 

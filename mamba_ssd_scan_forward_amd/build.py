@@ -1,4 +1,5 @@
-"""Build ``libssd.so`` (the HIP kernels and the C ABI of ``include/ssd.h``) for gfx950.
+"""Build ``libssd.so`` (the HIP kernels and the C ABI of ``include/ssd.h``) and
+``libssd_probe.so`` (the machine measurements of ``include/ssd_probe.h``) for gfx950.
 
 hipcc cross-compiles without a GPU, so this runs on any host with ROCm installed.
 """
@@ -10,6 +11,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "ssd_api.hip")
 LIB = os.path.join(HERE, "libssd.so")
+PROBE_SRC = os.path.join(HERE, "csrc", "ssd_probe.hip")
+PROBE_LIB = os.path.join(HERE, "libssd_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -22,8 +25,13 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + [SRC, "-o", tmp]
+    compile_one(PROBE_SRC, PROBE_LIB, verbose)
+    return compile_one(SRC, LIB, verbose)
+
+
+def compile_one(src: str, lib: str, verbose: bool = False) -> str:
+    tmp = lib + ".tmp"
+    cmd = [HIPCC] + FLAGS + [src, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -33,8 +41,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -34,6 +34,28 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+PROBE_HEADER = os.path.join(ROOT, "include", "ssd_probe.h")
+
+
+def test_probe_library_exports_every_declared_symbol():
+    """The machine measurements (include/ssd_probe.h) in their own library."""
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(ssd_[a-z_0-9]+)\s*\(", text)))
+    assert names == ["ssd_probe_clock", "ssd_probe_device", "ssd_probe_mfma_bf16"]
+    lib = ssd.load_probe_library()
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_probe_rejects_bad_arguments():
+    lib = ssd.load_probe_library()
+    assert lib.ssd_probe_mfma_bf16(0, 1, 16, None) == -1
+    assert lib.ssd_probe_mfma_bf16(1, 0, 16, None) == -1
+    assert lib.ssd_probe_mfma_bf16(1, 1, None, None) == -1
+    assert lib.ssd_probe_clock(1 << 25, 1, 16, None) == -1
+    assert lib.ssd_probe_clock(1, 1, None, None) == -1
+
+
 def test_abi_and_status_strings():
     assert ssd.ssd_abi_version() == ssd.ABI_VERSION
     for code in (0, -1, -2, -3, -4):
