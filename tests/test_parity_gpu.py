@@ -270,14 +270,16 @@ def test_full_size_config(name):
 
 # Shapes that fill at least half of the chip with (sequence, group, quad of heads)
 # workgroups, so the library walks them three or four heads per workgroup (three where
-# the extra workgroups still fit one round over the compute units, four otherwise and for
-# packed batches): ragged chunks with an initial state (three, the last workgroup of the
+# the extra workgroups still fit one round over the compute units or cost less in all,
+# four otherwise): ragged chunks with an initial state (three, the last workgroup of the
 # group with one head); d_state 64 with groups of five heads (three, a workgroup of two);
 # d_state 64 with groups of 14 heads (four, a workgroup of two); a packed batch with empty
-# and length-1 sequences (four, longest-first dealing); strong decay, where most 32-row
-# blocks take the exact-mask path, with three and with four heads per workgroup.
-@pytest.mark.parametrize("case", ["ragged_init", "state64_partial", "state64_four", "packed", "strong_decay",
-                                  "strong_decay_four"])
+# and length-1 sequences (four, longest-first dealing); the same with groups of three
+# heads (three); groups of two heads (four, two of them shadowing); strong decay, where
+# most 32-row blocks take the exact-mask path, with three and with four heads per
+# workgroup.
+@pytest.mark.parametrize("case", ["ragged_init", "state64_partial", "state64_four", "packed", "packed_three",
+                                  "two_per_group", "strong_decay", "strong_decay_four"])
 def test_quad_walker(case):
     if case == "ragged_init":
         inp = make_inputs(32, 300, 16, 64, 128, 1, "bf16", seed=1300, init_state=True)
@@ -288,6 +290,11 @@ def test_quad_walker(case):
     elif case == "packed":
         lens = [1, 0, 300, 257, 5, 1200, 256, 31, 0, 700, 64, 129, 2, 500, 33, 522]
         inp = make_inputs(1, sum(lens), 80, 64, 128, 8, "bf16", seed=1302, init_state=True, seq_lengths=lens)
+    elif case == "packed_three":
+        lens = [1, 0, 300, 257, 5, 700, 256, 31, 0, 400, 64, 129, 2, 300, 33, 222]
+        inp = make_inputs(1, sum(lens), 24, 64, 128, 8, "bf16", seed=1306, init_state=True, seq_lengths=lens)
+    elif case == "two_per_group":
+        inp = make_inputs(16, 260, 16, 64, 128, 8, "bf16", seed=1307, init_state=True)
     elif case == "strong_decay":
         inp = make_inputs(32, 300, 16, 64, 128, 1, "bf16", seed=1303, init_state=True)
         inp.logA = (inp.logA * 40.0).astype(np.float32)
