@@ -28,10 +28,10 @@
 // order, and the diagonal C B^T tile: one run of memory per block, written by the prep
 // kernel) are loaded once per workgroup: the waves deal the 1 KB pieces among themselves
 // and each loads its share of its own head's X, straight from global memory into a
-// four-slot LDS ring three blocks ahead; one barrier per block hands a slot over.  The state accumulator converts to the A
-// operand of the left factor without moving data between lanes: a lane holds rows
-// 8 (e / 4) + 4 lg + e % 4 of a 32 x 32 accumulator, and the prep kernel writes C's
-// fragments with the contraction index in that order.
+// four-slot LDS ring three blocks ahead; one barrier per block hands a slot over.  The
+// state accumulator converts to the A operand of the left factor without moving data
+// between lanes: a lane holds rows 8 (e / 4) + 4 lg + e % 4 of a 32 x 32 accumulator,
+// and the prep kernel writes C's fragments with the contraction index in that order.
 #pragma once
 
 #include "ssd_walk_split.h"
