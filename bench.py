@@ -140,6 +140,13 @@ def measure_machine(walk, stream, dev):
     MFMA rate and the clock under it, a 512 MiB device copy, and the clock while the walk
     kernel runs (a one-wave-per-workgroup sampler on a second stream beside five walk
     launches, bracketed on the walk's stream by two one-workgroup markers)."""
+    out = measure_peaks(stream, dev)
+    out.update(measure_walk_clock(walk, stream, dev))
+    return out
+
+
+def measure_peaks(stream, dev):
+    """The dense bf16 MFMA rate (and the clock under it) and a 512 MiB device copy."""
     import ctypes
     import numpy as np
     import torch
@@ -173,7 +180,20 @@ def measure_machine(walk, stream, dev):
     torch.cuda.synchronize()
     copy_gbs = 2 * n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
-    # the clock while the walk runs
+    return {"compute_units": cus.value, "max_clock_mhz": khz.value / 1000.0,
+            "mfma_bf16_tflops": round(mfma_tflops, 1), "mfma_clock_mhz": round(mfma_clk, 0),
+            "hbm_copy_gbs": round(copy_gbs, 1)}
+
+
+def measure_walk_clock(walk, stream, dev):
+    """The shader clock while the walk runs: a one-wave-per-workgroup sampler on a second
+    stream, started when the first of five walk launches has ended, its window checked
+    against two one-workgroup markers on the walk's stream."""
+    import numpy as np
+    import torch
+    import mamba_ssd_scan_forward_amd as ssd
+    probe = ssd.load_probe_library()
+    sp = stream.cuda_stream
     side = torch.cuda.Stream(device=dev)
     nsamp = 32
     samp = torch.zeros(4 * nsamp, dtype=torch.int64, device=dev)
@@ -197,10 +217,7 @@ def measure_machine(walk, stream, dev):
     log(f"[bench] clock sampler: starts {(t[:, 1].min() - mv[3]) / 100:.1f} us after the walks' first marker, "
         f"ends {(mv[5] - t[:, 3].max()) / 100:.1f} us before their last; walks span {(mv[5] - mv[3]) / 100:.1f} us")
     walk_clk = float(np.mean(clocks_mhz(sv))) if inside else None
-    return {"compute_units": cus.value, "max_clock_mhz": khz.value / 1000.0,
-            "mfma_bf16_tflops": round(mfma_tflops, 1), "mfma_clock_mhz": round(mfma_clk, 0),
-            "hbm_copy_gbs": round(copy_gbs, 1),
-            "walk_clock_mhz": None if walk_clk is None else round(walk_clk, 0),
+    return {"walk_clock_mhz": None if walk_clk is None else round(walk_clk, 0),
             "walk_clock_window_inside_walks": inside}
 
 
@@ -214,6 +231,7 @@ def run_report_mode(args):
 
     names = [args.workload] if args.workload else list(CONFIGS)
     dev = torch.device("cuda", 0)
+    measured = measure_peaks(torch.cuda.current_stream(dev), dev)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     steps = max(args.steps, 1)
     for name in names:
@@ -290,6 +308,13 @@ def run_report_mode(args):
             "frac_roofline": round(t_roof / cold_us, 4),
             "frac_roofline_warm": round(t_roof / warm_us, 4),
         }
+        # the same against the rates this chip reaches (bf16 MFMA and a device copy)
+        mm = measured["mfma_bf16_tflops"] if w.dtype == "bf16" else peak
+        t_meas = max(fp / (mm * 1e12), abytes / (measured["hbm_copy_gbs"] * 1e9)) * 1e6
+        line["measured_peaks"] = measured
+        line["frac_mfma_measured"] = round(fp / (cold_us * 1e-6) / 1e12 / mm, 4)
+        line["roofline_us_measured"] = round(t_meas, 2)
+        line["frac_roofline_measured"] = round(t_meas / cold_us, 4)
         if w.varlen:
             line["seq_lengths"] = lens
         print(json.dumps(line), flush=True)
