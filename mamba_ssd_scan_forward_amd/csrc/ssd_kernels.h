@@ -173,14 +173,16 @@ __global__ void __launch_bounds__(kPrepThreads, 2) ssd_prep_kernel(PrepArgs a) {
     // (the wavefront index is uniform: in a scalar register, so are the tile coordinates)
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 31, lg = lane >> 5;
+    // (the C B^T workgroups first: the longer role is dispatched to compute units of its
+    // own before the cumsum workgroups double up)
     int bid = blockIdx.x;
-    const bool cs_role = bid < a.cs_blocks;
+    const bool cs_role = bid >= a.cb_blocks;
     int k, rest;
     if (cs_role) {
+        bid -= a.cb_blocks;
         k = bid / a.hblocks;
         rest = bid % a.hblocks;
     } else {
-        bid -= a.cs_blocks;
         k = bid / a.G;
         rest = bid % a.G;
     }
