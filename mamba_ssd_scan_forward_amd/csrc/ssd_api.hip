@@ -10,6 +10,7 @@
 #include "ssd_kernels.h"
 #include "ssd_walk_split.h"
 #include "ssd_walk_quad.h"
+#include "ssd_walk_fused.h"
 #include "ssd_backward.h"
 
 namespace {
@@ -49,6 +50,10 @@ struct Plan {
     int quads;        // its workgroups per group
     size_t xflag_off; // its per-(chunk, head) flags of very steep decay
     size_t dx_off;    // its per-row decays to the end of the row's 32-row block
+    int fused;        // compute waves per workgroup of the fused walker (0: not used)
+    int fused_wpg;    // its workgroups per group
+    int64_t fused_items;
+    void (*fused_fn)(ssd::FusedArgs);
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -126,12 +131,70 @@ walk_fn pick_walk_bf16(int PT, int NP, bool cbl) {
 
 // Workspace and launch plan.  `nseq_total` slots: batch mode has batch * ceil(T/Q)
 // chunks; a packed batch has at most ceil(T/Q) + nseq (one ragged chunk per sequence).
-int make_plan(const ssd_problem* p, Plan* pl, bool allow_quad = true) {
+// The fused walker (ssd_walk_fused.h): bf16, head dimension a multiple of 32 from 64,
+// d_state 64 or 128, any chunk length (its 32-row blocks pass the state between them, so
+// the chunking does not change the result).  NW compute waves per workgroup, each holding
+// 32 columns of one head; it takes the NW that needs the fewest rounds of workgroups over
+// the compute units (a packed batch: the fewest workgroups), then leaves the fewest compute
+// waves idle, then the larger NW.  It is used when its workgroups fill at least half the
+// chip: fewer, longer walks are left to the segmented split walker.
+typedef void (*fused_fn_t)(ssd::FusedArgs);
+template <int NP>
+fused_fn_t fused_instance(int nw) {
+    switch (nw) {
+        case 4: return ssd::ssd_walk_fused_kernel<NP, 4>;
+        case 5: return ssd::ssd_walk_fused_kernel<NP, 5>;
+        case 6: return ssd::ssd_walk_fused_kernel<NP, 6>;
+    }
+    return nullptr;
+}
+
+bool plan_fused(const ssd_problem* p, Plan* pl) {
+    pl->fused = 0;
+    const int64_t P = p->headdim, N = p->dstate, H = p->nheads, G = p->ngroups;
+    if (p->dtype != SSD_DTYPE_BF16 || P % 32 != 0 || P < 64 || (N != 64 && N != 128)) return false;
+    // 32-bit byte offsets inside one sequence's rows of X / Y, B / C and logA
+    if (p->batch * p->seqlen * H * P * 2 >= ((int64_t)1 << 31) ||
+        p->batch * p->seqlen * G * N * 2 >= ((int64_t)1 << 31))
+        return false;
+    const int64_t upg = (H / G) * (P / 32);
+    const bool packed = p->nseq != p->batch;
+    int best = 0;
+    int64_t best_cost = 0, best_waste = 0, best_items = 0, best_wpg = 0;
+    for (int nw = 6; nw >= 4; --nw) {
+        const int64_t wpg = (upg + nw - 1) / nw;
+        const int64_t items = p->nseq * G * wpg;
+        const int64_t cost = packed ? items : (items + kComputeUnits - 1) / kComputeUnits;
+        const int64_t waste = items * nw - p->nseq * G * upg;
+        if (!best || cost < best_cost || (cost == best_cost && waste < best_waste)) {
+            best = nw;
+            best_cost = cost;
+            best_waste = waste;
+            best_items = items;
+            best_wpg = wpg;
+        }
+    }
+    if (best_items < kComputeUnits / 2 || best_items > INT32_MAX / 8) return false;
+    pl->fused = best;
+    pl->fused_wpg = (int)best_wpg;
+    pl->fused_items = best_items;
+    pl->fused_fn = N == 64 ? fused_instance<64>(best) : fused_instance<128>(best);
+    return pl->fused_fn != nullptr;
+}
+
+int make_plan(const ssd_problem* p, Plan* pl, bool allow_quad = true, bool allow_fused = true) {
     const int rc = check_problem(p);
     if (rc != SSD_OK) return rc;
     pl->dtype = p->dtype;
     pl->quad = 0;
     pl->quads = 0;
+    pl->fused = 0;
+    if (allow_quad && allow_fused && plan_fused(p, pl)) {
+        pl->npass = 1;
+        pl->nseg = 1;
+        pl->ws_bytes = 256;   // (no workspace is used)
+        return SSD_OK;
+    }
     pl->summary = nullptr;
     pl->walk_left = nullptr;
     pl->walk_pair = nullptr;
@@ -360,7 +423,8 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
                 float* final_state, void* workspace, size_t workspace_bytes, void* hip_stream,
                 int64_t x_heads = 0) {
     Plan pl;
-    int rc = make_plan(p, &pl);
+    // (the fused walker reads one X row per head)
+    int rc = make_plan(p, &pl, true, x_heads == 0 || x_heads == p->nheads);
     if (rc != SSD_OK) return rc;
     if (!X || !logA || !B || !C || !Y || !workspace) return SSD_ERR_INVALID_ARG;
     if (seq_offsets) {
@@ -392,6 +456,35 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
     if (final_state && overlap(Y, nx, final_state, ns)) return SSD_ERR_INVALID_ARG;
     if (workspace_bytes < pl.ws_bytes) return SSD_ERR_WORKSPACE;
 
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (pl.fused) {
+        // one launch, no workspace: stage 1 has nothing to do
+        if (!(stages & 2)) return SSD_OK;
+        ssd::FusedArgs fa;
+        fa.X = static_cast<const __bf16*>(X);
+        fa.logA = logA;
+        fa.B = static_cast<const __bf16*>(B);
+        fa.C = static_cast<const __bf16*>(C);
+        fa.init = init_state;
+        fa.seq_offsets = seq_offsets;
+        fa.Y = static_cast<__bf16*>(Y);
+        fa.final_state = final_state;
+        fa.T = T;
+        fa.H = (int)H;
+        fa.P = (int)P;
+        fa.N = (int)N;
+        fa.G = (int)G;
+        fa.nseq = (int)p->nseq;
+        fa.upg = (int)((H / G) * (P / 32));
+        fa.wpg = pl.fused_wpg;
+        fa.nitems = (int)pl.fused_items;
+        // packed sequences: (sequence, group) units dealt to the XCDs longest first
+        fa.lpt = (seq_offsets && p->nseq <= 64) ? 1 : 0;
+        int64_t grid = pl.fused_items;
+        if (fa.lpt) grid = ((p->nseq * G + 7) / 8) * 8 * pl.fused_wpg;
+        hipLaunchKernelGGL(pl.fused_fn, dim3((unsigned)grid), dim3(64 * (pl.fused + 2)), 0, stream, fa);
+        return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+    }
     walk_fn walk = pl.walk;
     prep_fn prep = p->dtype == SSD_DTYPE_BF16 ? ssd::ssd_prep_kernel<__bf16>
                                               : ssd::ssd_prep_kernel<float>;
@@ -410,7 +503,6 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
         if (rc != SSD_OK) return rc;
     }
 
-    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     // slots actually addressed by this call
     const int64_t nc = (T + pl.Q - 1) / pl.Q;
     const int64_t nslots = seq_offsets ? nc + p->nseq : b * nc;

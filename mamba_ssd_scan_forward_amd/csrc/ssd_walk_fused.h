@@ -1,0 +1,624 @@
+// ssd_walk_fused.h -- the fused walker: the whole SSD forward of a (sequence, group, run of
+// 32-column units of P) in one launch, with no workspace, for bf16 operands, head
+// dimension a multiple of 32 and d_state 64, 128 or 256 (page "Transformers are SSMs"
+// paper summary: the recurrence of sections 2.4 / 5.1, the block decomposition of
+// section 6, heads of a group sharing B and C as in section 7.2, packed sequences as in
+// section 8.3).
+//
+// Block decomposition with 32-row blocks and the state passed between blocks.  With
+// cs[l] the inclusive cumsum of logA inside block j (log2 units), e = cs[31], and the
+// state before the block h = 2^lsig g (g is what the accumulators hold):
+//      Y_l   = 2^(cs_l) C_l h + sum_{s <= l} 2^(cs_l - cs_s) (C_l . B_s) X_s
+//      h_end = 2^e h + sum_s 2^(e - cs_s) B_s^T X_s
+// Taking lsig' = lsig + e (the state's new log scale) both become products with per-row
+// factors and one shared, causally masked tile D = tril(C B^T) of the block:
+//      X~_s  = 2^(e - cs_s - lsig') X_s                         (w_s)
+//      Y_l   = 2^(cs_l - e + lsig') [C_l g + sum_s D_ls X~_s]    (r_l)
+//      g'    = g + sum_s B_s^T X~_s
+// so the decays touch 32 rows of X and of Y per block, never the state itself.  When
+// lsig' would fall below -64 the state is first brought to h 2^e (one pass over the
+// accumulators) and lsig' = 0.  A block whose span cs[0] - e exceeds 100 (beyond any
+// Mamba-2 parameter range) would lose rows of X~ to underflow; it takes the exact form
+// instead: the left factor with 2^(cs_l + lsig), the tile masked per head with
+// 2^(cs_l - cs_s) on unscaled X, the state brought to 2^e h before its update with
+// X~ = 2^(e - cs_s) X (every factor <= 1).
+//
+// Workgroup: NW compute waves and two loader waves.  Compute wave k holds unit u = q NW + k
+// of its group (head u / (P/32), columns 32 (u % (P/32)) .. + 31): the state g^T of that
+// slice (N x 32 float32, N/32 MFMA accumulators of 32 x 32) for the whole sequence.  The
+// X-loader brings each unit's X rows, the BC-loader the group's B and C rows and the
+// heads' logA, all straight from global memory into a ring of four LDS slots, three
+// blocks ahead.  The BC-loader also turns each block into its products one step before
+// it is used: the cumsums, w and r of every head, the renormalisation and steep flags,
+// and the masked tile D in the layout of an MFMA operand (v_mfma_f32_32x32x16_bf16 on B
+// and C rows).  Compute waves issue no loads to LDS, read only LDS, and store Y from
+// registers; one barrier per block hands the ring slot and the products over.
+//
+// Contraction order.  A lane holds accumulator rows 8 (e / 4) + 4 lg + e % 4 of a 32 x 32
+// tile (lg = lane / 32).  The state tile g^T (n x p) therefore enters the left factor
+// Y^T = g C^T as an A operand whose K index k = 8 lg + q is the row
+// sigma(k) = 8 (q / 4) + 4 lg + q % 4; C is read in that order (two 8-byte pieces per
+// K-step).  The same order is used for the rows s of X~ and of the tile D, which is how
+// the BC-loader's accumulator of D^T = B C^T becomes the B operand of Y^T += X~^T D^T
+// without moving data between lanes, and why X is read with 4-row transposing reads.
+#pragma once
+
+#include <type_traits>
+
+#include "ssd_kernels.h"
+
+namespace ssd {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+struct FusedArgs {
+    const __bf16* X;
+    const float* logA;
+    const __bf16* B;
+    const __bf16* C;
+    const float* init;
+    const int32_t* seq_offsets;
+    __bf16* Y;
+    float* final_state;
+    int64_t T;      // tokens per sequence (without seq_offsets)
+    int H, P, N, G, nseq;
+    int upg;        // 32-column units per group: (H / G) (P / 32)
+    int wpg;        // workgroups per group: ceil(upg / NW)
+    int nitems;     // nseq G wpg
+    int lpt;        // packed sequences dealt to XCDs longest first
+};
+
+// LDS of the fused walker.  Ring slot: X [NW][32][32] (unit-major, row-major), B and C
+// [32][N] (16-byte units of a row XOR-swizzled by fused_swz), logA [NHL][32].  Products
+// (two buffers): the masked tile D^T as MFMA B-operand fragments [2][64][8] bf16, per
+// head w [32] (in the sigma order of the K index), r [32], the cumsum [32], the
+// renormalisation factor and the path flag, and the per-head exact tiles of steep blocks
+// [NHL][2][64][8] bf16.  The BC-loader keeps its own copy of each block's logA [NHL][32].
+template <int NP, int NW> struct FusedLds {
+    static constexpr int NHL = NW / 2 + 2;             // heads a workgroup can touch (P >= 64)
+    static constexpr int xbytes = NW * 2048;
+    static constexpr int bcbytes = 32 * NP * 2;
+    static constexpr int labytes = ((NHL + 1) / 2) * 256;
+    static constexpr int nslot = NP == 256 ? 3 : 4;    // blocks in flight: nslot - 1
+    static constexpr int dg = 0;
+    static constexpr int w = 2048;
+    static constexpr int r = w + NHL * 128;
+    static constexpr int cs = r + NHL * 128;
+    static constexpr int f = cs + NHL * 128;
+    static constexpr int fl = f + NHL * 4;
+    static constexpr int st = (fl + NHL * 4 + 15) / 16 * 16;
+    static constexpr int prod = st + NHL * 2048;
+    static constexpr int total = nslot * (xbytes + 2 * bcbytes + 2 * labytes) + 2 * prod;
+    static_assert(total <= 160 * 1024, "LDS");
+};
+
+// Position of 16-byte unit u of B / C row r in LDS (units per row U = N / 8): the unit
+// index XOR 4 (r % (U / 4)) + (r / (U / 4)) % 4, which spreads the rows read together by
+// every access pattern of the walk (8-byte C pieces of 32 rows, transposing reads of 8
+// rows of B, 16-byte rows of B and C for the tile) evenly over the banks.
+template <int NP> __device__ __forceinline__ int fused_swz(int r) {
+    constexpr int U4 = NP / 32;
+    return 4 * (r % U4) + (r / U4) % 4;
+}
+
+// Global memory straight to LDS: lane i's 16 (4) bytes land at dst + 16 i (4 i).
+__device__ __forceinline__ void fused_lds16(rsrc_t r, void* dst, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, (int)voff, (int)soff, 0, 0);
+}
+__device__ __forceinline__ void fused_lds4(rsrc_t r, void* dst, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 4, (int)voff, (int)soff, 0, 0);
+}
+template <int n>
+__device__ __forceinline__ void fused_wait_vm() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+__device__ __forceinline__ bf16x4 tr4(const __bf16* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SSD_LDS bf16x4*)(SSD_LDS __bf16*)p);
+}
+__device__ __forceinline__ bf16x8 cat44(bf16x4 lo, bf16x4 hi) {
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+// DPP row operations (gfx9): lanes whose source lies outside the row, or whose row is
+// masked off, keep `old` (here 0)
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWMASK, 0xF, false));
+}
+// Inclusive sum over the 32 lanes of each half of the wave: shifts by 1, 2, 4, 8 inside
+// each 16-lane row, then lane 15 (47) of the first row of a half added to its second row.
+__device__ __forceinline__ float scan32(float x) {
+    x += dpp_f<0x111>(x);
+    x += dpp_f<0x112>(x);
+    x += dpp_f<0x114>(x);
+    x += dpp_f<0x118>(x);
+    x += dpp_f<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3
+    return x;
+}
+__device__ __forceinline__ float lane_f(float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
+// position of row s (0..31) in the sigma order of the K index (bits 2 and 3 swapped)
+__device__ __forceinline__ int sigma_pos(int s) { return (s & 19) | ((s & 4) << 1) | ((s & 8) >> 1); }
+
+template <int NP, int NW>
+__device__ __forceinline__ void fused_walk(const FusedArgs& a, unsigned char* const (&xs)[4],
+                                           unsigned char* const (&bs)[4], unsigned char* const (&cs_)[4],
+                                           unsigned char* const (&las)[4], unsigned char* const (&las2)[4],
+                                           unsigned char* const (&prod)[2], int s,
+                                           int g, int q) {
+    typedef Elem<__bf16> E;
+    typedef FusedLds<NP, NW> L;
+    constexpr int NT = NP / 32;            // n tiles of the state
+    constexpr int NS = L::nslot;
+    constexpr int D = NS - 1;              // blocks in flight ahead of the one computed
+    constexpr int UPR = NP / 8;            // 16-byte units of a B / C row
+    constexpr int RPL = 64 / UPR;          // rows per 1 KB load
+    constexpr int NBL = NP / 16;           // 1 KB loads of B (and of C) per block
+    constexpr int NHL = L::NHL;
+    constexpr int NPAIR = (NHL + 1) / 2;
+    constexpr int LX = 2 * NW + NPAIR;     // X-loader loads per block
+    constexpr int LB = 2 * NBL + NPAIR;    // BC-loader loads per block
+    static_assert(D * LX < 64 && D * LB < 64, "vmcnt range");
+
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool compute = (wave & 3) != 3 && wave - (wave >> 2) < NW;
+    const int ci = wave - (wave >> 2);     // compute index (compute waves)
+    const bool bcloader = wave == 3;
+    const bool xloader = !compute && !bcloader;
+    const int H = a.H, P = a.P, G = a.G, hpg = H / G, uph = P / 32;
+
+    int64_t row0;
+    int len;
+    if (!a.seq_offsets) {
+        row0 = (int64_t)s * a.T;
+        len = (int)a.T;
+    } else {
+        row0 = a.seq_offsets[s];
+        len = a.seq_offsets[s + 1] - a.seq_offsets[s];
+    }
+    const int nb = (len + 31) / 32;
+    const int u0 = q * NW;                 // first unit of the workgroup
+    const int hfirst = u0 / uph;           // first head (within the group) it touches
+    const int64_t xrow = (int64_t)H * P;   // elements per token row of X / Y
+
+    // ---- per-block product buffers
+    auto pbuf = [&](int t) -> unsigned char* { return prod[t & 1]; };
+
+    // ring and barrier discipline shared by both loaders: blocks 0 .. D-1 in flight before
+    // the first step; step t issues block t + D (past the end: the last block again, so
+    // that every step issues the same loads and the wait counts stay exact), waits for its
+    // own loads of block t + 1, turns block t + 1 into its products and meets the other
+    // waves at the barrier after which block t + 1 is complete and block t's slot is free.
+    auto loader_loop = [&](auto issue, auto products, auto wait_rest) __attribute__((always_inline)) {
+        if (nb > 0) {
+            issue(0, std::integral_constant<int, 0>{});
+            issue(1, std::integral_constant<int, 1>{});
+            if constexpr (D == 3) issue(2, std::integral_constant<int, 2>{});
+            wait_rest();
+            products(0, std::integral_constant<int, 0>{});
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        auto step = [&](int t, auto kc) __attribute__((always_inline)) {
+            constexpr int k = decltype(kc)::value;
+            issue(t + D, std::integral_constant<int, (k + D) % NS>{});
+            wait_rest();
+            if (t + 1 < nb) products(t + 1, std::integral_constant<int, (k + 1) % NS>{});
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_s_barrier();
+        };
+        for (int t = 0; t < nb; t += NS) {
+            step(t, std::integral_constant<int, 0>{});
+            if (t + 1 < nb) step(t + 1, std::integral_constant<int, 1>{});
+            if (t + 2 < nb) step(t + 2, std::integral_constant<int, 2>{});
+            if constexpr (NS == 4)
+                if (t + 3 < nb) step(t + 3, std::integral_constant<int, 3>{});
+        }
+        fused_wait_vm<0>();
+        __builtin_amdgcn_s_barrier();
+    };
+
+    if (xloader) {
+        // ------------------------------------------------------------ X loader: every unit's
+        // X rows and the heads' logA; per head the block's cumsum, the row factors w and r,
+        // the renormalisation factor and the path flag
+        const rsrc_t xr = make_rsrc(a.X + row0 * xrow, (uint32_t)((int64_t)len * xrow * 2));
+        const rsrc_t lar = make_rsrc(a.logA + row0 * H, (uint32_t)((int64_t)len * H * 4));
+        uint32_t xl[NW];
+#pragma unroll
+        for (int k = 0; k < NW; ++k) {
+            const int u = min(u0 + k, a.upg - 1);
+            const int h = g * hpg + u / uph, c0 = 32 * (u % uph);
+            xl[k] = (uint32_t)(((lane >> 2) * xrow + (int64_t)h * P + c0 + 8 * (lane & 3)) * 2);
+        }
+        // logA: lanes 0..31 head 2 p, lanes 32..63 head 2 p + 1 (clamped to the group)
+        uint32_t ll[NPAIR];
+#pragma unroll
+        for (int p = 0; p < NPAIR; ++p) {
+            const int hl = min(hfirst + 2 * p + lg, hpg - 1);
+            ll[p] = (uint32_t)((lr * H + g * hpg + hl) * 4);
+        }
+        const uint32_t rs16 = (uint32_t)(16 * xrow * 2), rb32 = (uint32_t)(32 * xrow * 2), lab32 = (uint32_t)(32 * H * 4);
+        auto issue = [&](int b, auto kc) __attribute__((always_inline)) {
+            constexpr int k = decltype(kc)::value;
+            b = min(b, nb - 1);
+#pragma unroll
+            for (int u = 0; u < NW; ++u) {
+                fused_lds16(xr, xs[k] + u * 2048, opaque(xl[u]), (uint32_t)b * rb32);
+                fused_lds16(xr, xs[k] + u * 2048 + 1024, opaque(xl[u]) + rs16, (uint32_t)b * rb32);
+            }
+#pragma unroll
+            for (int p = 0; p < NPAIR; ++p) fused_lds4(lar, las[k] + 256 * p, opaque(ll[p]), (uint32_t)b * lab32);
+        };
+        float lsig[NPAIR];
+#pragma unroll
+        for (int p = 0; p < NPAIR; ++p) lsig[p] = 0.f;
+        auto products = [&](int b, auto kc) __attribute__((always_inline)) {
+            constexpr int k = decltype(kc)::value;
+            unsigned char* pb = pbuf(b);
+            const float* la = reinterpret_cast<const float*>(las[k]);
+#pragma unroll
+            for (int p = 0; p < NPAIR; ++p) {
+                const int jh = 2 * p + lg;
+                // inclusive cumsum over the 32 rows of each half (log2 units)
+                const float c = scan32(la[64 * p + lane] * kLog2e);
+                const float e = lg ? lane_f(c, 63) : lane_f(c, 31);
+                const float c0 = lg ? lane_f(c, 32) : lane_f(c, 0);
+                // path: 2 = exact form (span over 100), 1 = renormalise first, 0 = plain
+                const bool steep = c0 - e > 100.f;
+                const float ls = lsig[p];
+                const bool renorm = steep || ls + e < -64.f;
+                const float lnew = renorm ? 0.f : ls + e;
+                const float w = fast_exp2(e - c - lnew);
+                const float r = fast_exp2(steep ? c + ls : c - e + lnew);
+                const float f = fast_exp2(ls + e);
+                lsig[p] = lnew;
+                if (jh < NHL) {
+                    reinterpret_cast<float*>(pb + L::w)[32 * jh + sigma_pos(lr)] = w;
+                    reinterpret_cast<float*>(pb + L::r)[32 * jh + lr] = r;
+                    reinterpret_cast<float*>(pb + L::cs)[32 * jh + lr] = c;
+                    if (lr == 0) {
+                        reinterpret_cast<float*>(pb + L::f)[jh] = f;
+                        reinterpret_cast<int*>(pb + L::fl)[jh] = steep ? 2 : renorm ? 1 : 0;
+                    }
+                }
+            }
+        };
+        loader_loop(issue, products, [&]() __attribute__((always_inline)) { fused_wait_vm<(D - 1) * LX>(); });
+        // the heads' final log scales for the compute waves' final states
+#pragma unroll
+        for (int p = 0; p < NPAIR; ++p)
+            if (2 * p + lg < NHL && lr == 0) reinterpret_cast<float*>(pbuf(0) + L::f)[2 * p + lg] = lsig[p];
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        return;
+    }
+
+    if (bcloader) {
+        // ------------------------------------------------------------ BC loader: the group's
+        // B and C rows; per block the causally masked tile D^T = B C^T as MFMA fragments
+        const rsrc_t br = make_rsrc(a.B + row0 * G * NP + g * NP, (uint32_t)((int64_t)len * G * NP * 2));
+        const rsrc_t cr = make_rsrc(a.C + row0 * G * NP + g * NP, (uint32_t)((int64_t)len * G * NP * 2));
+        // lane i of load k fills position i % UPR of row k RPL + i / UPR
+        const int brow = lane / UPR, bpos = lane % UPR;
+        uint32_t bl[NBL];
+#pragma unroll
+        for (int k = 0; k < NBL; ++k) {
+            const int r = k * RPL + brow;
+            bl[k] = (uint32_t)((r * G * NP + 8 * (bpos ^ fused_swz<NP>(r))) * 2);
+        }
+        // its own copy of the heads' logA, for the exact tiles of steep blocks
+        const rsrc_t lar = make_rsrc(a.logA + row0 * H, (uint32_t)((int64_t)len * H * 4));
+        uint32_t ll[NPAIR];
+#pragma unroll
+        for (int p = 0; p < NPAIR; ++p) {
+            const int hl = min(hfirst + 2 * p + lg, hpg - 1);
+            ll[p] = (uint32_t)((lr * H + g * hpg + hl) * 4);
+        }
+        const uint32_t bcb32 = (uint32_t)(32 * G * NP * 2), lab32 = (uint32_t)(32 * H * 4);
+        auto issue = [&](int b, auto kc) __attribute__((always_inline)) {
+            constexpr int k = decltype(kc)::value;
+            b = min(b, nb - 1);
+#pragma unroll
+            for (int i = 0; i < NBL; ++i) fused_lds16(br, bs[k] + 1024 * i, opaque(bl[i]), (uint32_t)b * bcb32);
+#pragma unroll
+            for (int i = 0; i < NBL; ++i) fused_lds16(cr, cs_[k] + 1024 * i, opaque(bl[i]), (uint32_t)b * bcb32);
+#pragma unroll
+            for (int p = 0; p < NPAIR; ++p) fused_lds4(lar, las2[k] + 256 * p, opaque(ll[p]), (uint32_t)b * lab32);
+        };
+        auto products = [&](int b, auto kc) __attribute__((always_inline)) {
+            constexpr int k = decltype(kc)::value;
+            unsigned char* pb = pbuf(b);
+            // D^T = B C^T (s x l) on MFMA, rows of both from the slot, two accumulator chains
+            const __bf16* bsl = reinterpret_cast<const __bf16*>(bs[k]);
+            const __bf16* csl = reinterpret_cast<const __bf16*>(cs_[k]);
+            f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < NP / 16; kk += 2) {
+                const int o0 = lr * NP + 8 * ((2 * kk + lg) ^ fused_swz<NP>(lr));
+                const int o1 = lr * NP + 8 * ((2 * kk + 2 + lg) ^ fused_swz<NP>(lr));
+                acc0 = E::mma(acc0, E::lds8(bsl + o0), E::lds8(csl + o0));
+                acc1 = E::mma(acc1, E::lds8(bsl + o1), E::lds8(csl + o1));
+            }
+            // causal mask (s <= l) and the fragments (K-step ks = elements 8 ks .. 8 ks + 7)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                bf16x8 d;
+#pragma unroll
+                for (int q8 = 0; q8 < 8; ++q8) {
+                    const int e8 = 8 * ks + q8;
+                    const int srow = 8 * (e8 >> 2) + 4 * lg + (e8 & 3);
+                    d[q8] = (__bf16)(srow <= lr ? acc0[e8] + acc1[e8] : 0.f);
+                }
+                *reinterpret_cast<bf16x8*>(pb + L::dg + 1024 * ks + 16 * lane) = d;
+            }
+            // exact tiles of the heads whose block spans more than 100 (the X-loader's test
+            // on the same cumsum): D'^T[s][l] = D^T[s][l] 2^(cs_l - cs_s)
+            const float* la = reinterpret_cast<const float*>(las2[k]);
+#pragma unroll
+            for (int p = 0; p < NPAIR; ++p) {
+                const float c = scan32(la[64 * p + lane] * kLog2e);
+                const float e = lg ? lane_f(c, 63) : lane_f(c, 31);
+                const float c0 = lg ? lane_f(c, 32) : lane_f(c, 0);
+                const bool steep_lo = lane_f(c, 0) - lane_f(c, 31) > 100.f;
+                const bool steep_hi = lane_f(c, 32) - lane_f(c, 63) > 100.f;
+                if (steep_lo || steep_hi) {
+                    (void)e;
+                    (void)c0;
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int jh = 2 * p + hh;
+                        if (jh >= NHL || !(hh ? steep_hi : steep_lo)) continue;
+                        // lane (lg, lr) needs cs at l = lr and at its rows s of this head
+                        const float cl = __shfl(c, 32 * hh + lr);
+#pragma unroll
+                        for (int ks = 0; ks < 2; ++ks) {
+                            bf16x8 t8;
+#pragma unroll
+                            for (int q8 = 0; q8 < 8; ++q8) {
+                                const int e8 = 8 * ks + q8;
+                                const int srow = 8 * (e8 >> 2) + 4 * lg + (e8 & 3);
+                                const float csr = __shfl(c, 32 * hh + srow);
+                                t8[q8] = (__bf16)(srow <= lr ? (acc0[e8] + acc1[e8]) * fast_exp2(cl - csr) : 0.f);
+                            }
+                            *reinterpret_cast<bf16x8*>(pb + L::st + 2048 * jh + 1024 * ks + 16 * lane) = t8;
+                        }
+                    }
+                }
+            }
+        };
+        loader_loop(issue, products, [&]() __attribute__((always_inline)) { fused_wait_vm<(D - 1) * LB>(); });
+        __builtin_amdgcn_s_barrier();
+        return;
+    }
+
+    // ---------------------------------------------------------------- compute waves
+    const int u = u0 + ci;
+    const bool valid = u < a.upg;
+    const int uc = valid ? u : a.upg - 1;
+    const int hl = uc / uph;                      // head within the group
+    const int h = g * hpg + hl;
+    const int c0 = 32 * (uc % uph);               // first column of P
+    const int jh = hl - hfirst;                   // local head index
+    const int64_t state_base = ((int64_t)s * H + h) * (int64_t)P * NP;
+
+    f32x16 gs[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) gs[nt] = f32x16{};
+    if (a.init) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 iv = *reinterpret_cast<const f32x4*>(a.init + state_base + (int64_t)(c0 + lr) * NP + 32 * nt +
+                                                                  8 * q4 + 4 * lg);
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) gs[nt][4 * q4 + e4] = iv[e4];
+            }
+    }
+    const rsrc_t yr = make_rsrc(a.Y + row0 * xrow, valid ? (uint32_t)((int64_t)len * xrow * 2) : 0u);
+    const uint32_t ylane = (uint32_t)((lr * xrow + (int64_t)h * P + c0 + 8 * lg) * 2);
+    const uint32_t yb32 = (uint32_t)(32 * xrow * 2);
+    // LDS addresses (byte offsets inside a slot).  With the swizzle of B / C rows the unit
+    // position of n tile nt is 4 (nt ^ a) + (m ^ b) for per-lane a, b: one base per n tile
+    // and one per 16-byte unit inside it.
+    const int xa0 = ci * 2048 + 64 * (4 * lg + ((lane & 15) >> 2)) + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    int cnt[NT], cm[4];   // C pieces of row lr: n tile part, unit part (m = 2 kk + j)
+    int bnt[NT], bm[2][2];   // B^T transposing reads: n tile part, (K-step, 4-row half) part
+    {
+        const int sa = fused_swz<NP>(lr);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) cnt[nt] = 2 * lr * NP + 8 * lg + 16 * ((4 * nt) ^ (sa & ~3));
+#pragma unroll
+        for (int m = 0; m < 4; ++m) cm[m] = 16 * (m ^ (sa & 3));
+        const int rb = 4 * lg + ((lane & 15) >> 2);   // row of the transposing read, K-step 0, half 0
+        const int v = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) bnt[nt] = 2 * rb * NP + 8 * (lane & 1) + 16 * ((4 * nt) ^ (fused_swz<NP>(rb) & ~3));
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) bm[ks][j] = 16 * (v ^ (fused_swz<NP>(16 * ks + 8 * j + rb) & 3));
+    }
+    // (rows 16 ks + 8 j + rb have rb's part 4 (r % U4) of the swizzle, U4 dividing 8; only the
+    // low two bits, (r / U4) % 4, change with ks and j)
+    auto ldsb = [&](const unsigned char* base, int off) __attribute__((always_inline)) -> bf16x4 {
+        return tr4(reinterpret_cast<const __bf16*>(base + off));
+    };
+
+    __builtin_amdgcn_s_barrier();
+    auto step = [&](int t, auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
+        const unsigned char* pb = pbuf(t);
+        const __bf16* xsl = reinterpret_cast<const __bf16*>(xs[k]);
+        const unsigned char* bsl = bs[k];
+        const unsigned char* csl = cs_[k];
+        // X of the block (K-step ks: rows 16 ks + sigma(8 lg + q))
+        bf16x8 xf[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            xf[ks] = cat44(tr4(xsl + (xa0 + 1024 * ks) / 2), tr4(xsl + (xa0 + 1024 * ks + 512) / 2));
+        const f32x4* wp = reinterpret_cast<const f32x4*>(pb + L::w + 128 * jh + 32 * lg);
+        const f32x4 w00 = wp[0], w01 = wp[1], w10 = wp[4], w11 = wp[5];
+        const float rl = reinterpret_cast<const float*>(pb + L::r)[32 * jh + lr];
+        const int flag = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int*>(pb + L::fl)[jh]);
+        const float f = reinterpret_cast<const float*>(pb + L::f)[jh];
+        const float ws[2][8] = {{w00[0], w00[1], w00[2], w00[3], w01[0], w01[1], w01[2], w01[3]},
+                                {w10[0], w10[1], w10[2], w10[3], w11[0], w11[1], w11[2], w11[3]}};
+        bf16x8 xt[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int q8 = 0; q8 < 8; ++q8) xt[ks][q8] = (__bf16)((float)xf[ks][q8] * ws[ks][q8]);
+        // one n tile: the left factor's two K-steps on the state before its update, then the
+        // state update (SCALE: the exact form's decay of the state between the two)
+        auto ntile = [&](f32x16& acc, int nt, bool scale) __attribute__((always_inline)) {
+            bf16x8 cf[2], bt[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(csl + cnt[nt] + cm[2 * kk]);
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(csl + cnt[nt] + cm[2 * kk + 1]);
+                cf[kk] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+                bt[kk] = cat44(ldsb(bsl, bnt[nt] + bm[kk][0] + 32 * NP * kk),
+                               ldsb(bsl, bnt[nt] + bm[kk][1] + 32 * NP * kk + 16 * NP));
+            }
+            bf16x8 hb[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int q8 = 0; q8 < 8; ++q8) hb[kk][q8] = (__bf16)gs[nt][8 * kk + q8];
+            acc = E::mma(acc, hb[0], cf[0]);
+            acc = E::mma(acc, hb[1], cf[1]);
+            if (scale) gs[nt] *= f;
+            gs[nt] = E::mma(gs[nt], bt[0], xt[0]);
+            gs[nt] = E::mma(gs[nt], bt[1], xt[1]);
+        };
+        f32x16 acc = f32x16{};
+        if (flag != 2) {
+            if (flag == 1) {
+                // (a branch, not a select: as a select every block would pay the pass)
+                asm volatile("");
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) gs[nt] *= f;
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) ntile(acc, nt, false);
+            const bf16x8 d0 = *reinterpret_cast<const bf16x8*>(pb + L::dg + 16 * lane);
+            const bf16x8 d1 = *reinterpret_cast<const bf16x8*>(pb + L::dg + 1024 + 16 * lane);
+            acc = E::mma(acc, xt[0], d0);
+            acc = E::mma(acc, xt[1], d1);
+            acc *= rl;
+        } else {
+            // exact form (steep block): left factor of the unscaled state, the per-head
+            // masked tile on unscaled X, the state brought to 2^e h before its update
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) ntile(acc, nt, true);
+            acc *= rl;
+            const unsigned char* stp = pb + L::st + 2048 * jh;
+            const bf16x8 d0 = *reinterpret_cast<const bf16x8*>(stp + 16 * lane);
+            const bf16x8 d1 = *reinterpret_cast<const bf16x8*>(stp + 1024 + 16 * lane);
+            acc = E::mma(acc, xf[0], d0);
+            acc = E::mma(acc, xf[1], d1);
+        }
+        // Y^T (p x l) -> bf16 pairs; lanes l and l + 32 trade pieces so that each holds 8
+        // consecutive columns of row l twice (columns 16 j + 8 lg .. + 7, j = 0, 1)
+        uint32_t pk[8];
+#pragma unroll
+        for (int j8 = 0; j8 < 8; ++j8) {
+            const bf16x2 v = {(__bf16)acc[2 * j8], (__bf16)acc[2 * j8 + 1]};
+            pk[j8] = __builtin_bit_cast(uint32_t, v);
+        }
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int j2 = 0; j2 < 2; ++j2) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(pk[4 * hf + j2], pk[4 * hf + 2 + j2], false, false);
+                pk[4 * hf + j2] = sw[0];
+                pk[4 * hf + 2 + j2] = sw[1];
+            }
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{pk[0], pk[1], pk[2], pk[3]}, yr, (int)ylane, (int)((uint32_t)t * yb32), 0);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{pk[4], pk[5], pk[6], pk[7]}, yr, (int)(ylane + 32u),
+                                               (int)((uint32_t)t * yb32), 0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+    };
+    for (int t = 0; t < nb; t += NS) {
+        step(t, std::integral_constant<int, 0>{});
+        if (t + 1 < nb) step(t + 1, std::integral_constant<int, 1>{});
+        if (t + 2 < nb) step(t + 2, std::integral_constant<int, 2>{});
+        if constexpr (NS == 4)
+            if (t + 3 < nb) step(t + 3, std::integral_constant<int, 3>{});
+    }
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_s_barrier();
+    if (a.final_state && valid) {
+        const float fs = fast_exp2(reinterpret_cast<const float*>(pbuf(0) + L::f)[jh]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 o = {gs[nt][4 * q4] * fs, gs[nt][4 * q4 + 1] * fs, gs[nt][4 * q4 + 2] * fs,
+                                 gs[nt][4 * q4 + 3] * fs};
+                *reinterpret_cast<f32x4*>(a.final_state + state_base + (int64_t)(c0 + lr) * NP + 32 * nt + 8 * q4 +
+                                          4 * lg) = o;
+            }
+    }
+}
+
+template <int NP, int NW>
+__global__ void __launch_bounds__(64 * (NW + 2), 1) ssd_walk_fused_kernel(FusedArgs a) {
+    typedef FusedLds<NP, NW> L;
+    constexpr int NS = L::nslot;
+    __shared__ __align__(16) unsigned char x0[L::xbytes], x1[L::xbytes], x2[L::xbytes], x3[NS == 4 ? L::xbytes : 16];
+    __shared__ __align__(16) unsigned char b0[L::bcbytes], b1[L::bcbytes], b2[L::bcbytes], b3[NS == 4 ? L::bcbytes : 16];
+    __shared__ __align__(16) unsigned char c0[L::bcbytes], c1[L::bcbytes], c2[L::bcbytes], c3[NS == 4 ? L::bcbytes : 16];
+    __shared__ __align__(16) unsigned char l0[L::labytes], l1[L::labytes], l2[L::labytes], l3[NS == 4 ? L::labytes : 16];
+    __shared__ __align__(16) unsigned char m0[L::labytes], m1[L::labytes], m2[L::labytes], m3[NS == 4 ? L::labytes : 16];
+    __shared__ __align__(16) unsigned char p0[L::prod], p1[L::prod];
+    unsigned char* const xs[4] = {x0, x1, x2, x3};
+    unsigned char* const bs[4] = {b0, b1, b2, b3};
+    unsigned char* const cs[4] = {c0, c1, c2, c3};
+    unsigned char* const las[4] = {l0, l1, l2, l3};
+    unsigned char* const las2[4] = {m0, m1, m2, m3};
+    unsigned char* const prod[2] = {p0, p1};
+
+    const int lane = threadIdx.x & 63;
+    const int G = a.G, wpg = a.wpg;
+    int s, g, q;
+    if (a.lpt) {
+        // packed sequences: the (sequence, group) units are dealt to the XCDs
+        // round-robin, longest sequence first
+        const int bid = blockIdx.x;
+        const int xcd = bid % 8, slot = bid / 8;
+        const int un = (slot / wpg) * 8 + xcd;
+        q = slot % wpg;
+        const int r = un / G;
+        g = un % G;
+        if (r >= a.nseq) return;
+        const int* off = a.seq_offsets;
+        bool mine = false;
+        if (lane < a.nseq) {
+            const int Ln = off[lane + 1] - off[lane];
+            int rank = 0;
+            for (int v = 0; v < a.nseq; ++v) {
+                const int Lv = off[v + 1] - off[v];
+                rank += (Lv > Ln) || (Lv == Ln && v < lane);
+            }
+            mine = rank == r;
+        }
+        s = __builtin_ctzll(__ballot(mine));
+    } else {
+        const int item = xcd_remap(blockIdx.x, gridDim.x);
+        if (item >= a.nitems) return;
+        q = item % wpg;
+        const int sg = item / wpg;
+        g = sg % G;
+        s = sg / G;
+    }
+    fused_walk<NP, NW>(a, xs, bs, cs, las, las2, prod, s, g, q);
+}
+
+}  // namespace ssd
