@@ -102,19 +102,24 @@ template <int NP> __device__ __forceinline__ int fused_swz(int r) {
 }
 
 // Global memory straight to LDS: lane i's 16 (4) bytes land at dst + 16 i (4 i).
-__device__ __forceinline__ void fused_lds16(rsrc_t r, void* dst, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, (int)voff, (int)soff, 0, 0);
+// (LDS addresses are kept in address space 3 throughout: a generic pointer converted at
+// each use would cost a null test per load)
+typedef SSD_LDS unsigned char* lds_ptr;
+__device__ __forceinline__ void fused_lds16(rsrc_t r, lds_ptr dst, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (SSD_LDS void*)dst, 16, (int)voff, (int)soff, 0, 0);
 }
-__device__ __forceinline__ void fused_lds4(rsrc_t r, void* dst, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 4, (int)voff, (int)soff, 0, 0);
+__device__ __forceinline__ void fused_lds4(rsrc_t r, lds_ptr dst, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (SSD_LDS void*)dst, 4, (int)voff, (int)soff, 0, 0);
 }
+template <typename T> __device__ __forceinline__ T ldsv(lds_ptr p) { return *reinterpret_cast<SSD_LDS const T*>(p); }
+template <typename T> __device__ __forceinline__ void ldsw(lds_ptr p, T v) { *reinterpret_cast<SSD_LDS T*>(p) = v; }
 template <int n>
 __device__ __forceinline__ void fused_wait_vm() {
     static_assert(n >= 0 && n < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
-__device__ __forceinline__ bf16x4 tr4(const __bf16* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SSD_LDS bf16x4*)(SSD_LDS __bf16*)p);
+__device__ __forceinline__ bf16x4 tr4(lds_ptr p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SSD_LDS bf16x4*)p);
 }
 __device__ __forceinline__ bf16x8 cat44(bf16x4 lo, bf16x4 hi) {
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -143,11 +148,29 @@ __device__ __forceinline__ float lane_f(float x, int l) {
 __device__ __forceinline__ int sigma_pos(int s) { return (s & 19) | ((s & 4) << 1) | ((s & 8) >> 1); }
 
 template <int NP, int NW>
-__device__ __forceinline__ void fused_walk(const FusedArgs& a, unsigned char* const (&xs)[4],
-                                           unsigned char* const (&bs)[4], unsigned char* const (&cs_)[4],
-                                           unsigned char* const (&las)[4], unsigned char* const (&las2)[4],
-                                           unsigned char* const (&prod)[2], int s,
+__device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
                                            int g, int q) {
+    typedef FusedLds<NP, NW> LL;
+    constexpr int NSL = LL::nslot;
+    // ring slots and product buffers: separate arrays, so that the compiler can tell the
+    // slot a direct-to-LDS load is filling from the slot being read; selected by constant
+    // index (a constant table of LDS addresses cannot be emitted)
+    __shared__ __align__(16) unsigned char x0[LL::xbytes], x1[LL::xbytes], x2[LL::xbytes], x3[NSL == 4 ? LL::xbytes : 16];
+    __shared__ __align__(16) unsigned char b0[LL::bcbytes], b1[LL::bcbytes], b2[LL::bcbytes], b3[NSL == 4 ? LL::bcbytes : 16];
+    __shared__ __align__(16) unsigned char c0_[LL::bcbytes], c1_[LL::bcbytes], c2_[LL::bcbytes], c3_[NSL == 4 ? LL::bcbytes : 16];
+    __shared__ __align__(16) unsigned char l0[LL::labytes], l1[LL::labytes], l2[LL::labytes], l3[NSL == 4 ? LL::labytes : 16];
+    __shared__ __align__(16) unsigned char m0[LL::labytes], m1[LL::labytes], m2[LL::labytes], m3[NSL == 4 ? LL::labytes : 16];
+    __shared__ __align__(16) unsigned char p0[LL::prod], p1[LL::prod];
+    auto pick = [](int k, unsigned char* a0, unsigned char* a1, unsigned char* a2, unsigned char* a3)
+                    __attribute__((always_inline)) -> lds_ptr {
+        return k == 0 ? (lds_ptr)a0 : k == 1 ? (lds_ptr)a1 : k == 2 ? (lds_ptr)a2 : (lds_ptr)a3;
+    };
+    auto XS = [&](int k) __attribute__((always_inline)) { return pick(k, x0, x1, x2, x3); };
+    auto BS = [&](int k) __attribute__((always_inline)) { return pick(k, b0, b1, b2, b3); };
+    auto CS = [&](int k) __attribute__((always_inline)) { return pick(k, c0_, c1_, c2_, c3_); };
+    auto LA = [&](int k) __attribute__((always_inline)) { return pick(k, l0, l1, l2, l3); };
+    auto LA2 = [&](int k) __attribute__((always_inline)) { return pick(k, m0, m1, m2, m3); };
+
     typedef Elem<__bf16> E;
     typedef FusedLds<NP, NW> L;
     constexpr int NT = NP / 32;            // n tiles of the state
@@ -185,7 +208,7 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, unsigned char* co
     const int64_t xrow = (int64_t)H * P;   // elements per token row of X / Y
 
     // ---- per-block product buffers
-    auto pbuf = [&](int t) -> unsigned char* { return prod[t & 1]; };
+    auto pbuf = [&](int t) __attribute__((always_inline)) -> lds_ptr { return (t & 1) ? (lds_ptr)p1 : (lds_ptr)p0; };
 
     // ring and barrier discipline shared by both loaders: blocks 0 .. D-1 in flight before
     // the first step; step t issues block t + D (past the end: the last block again, so
@@ -247,24 +270,24 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, unsigned char* co
             b = min(b, nb - 1);
 #pragma unroll
             for (int u = 0; u < NW; ++u) {
-                fused_lds16(xr, xs[k] + u * 2048, opaque(xl[u]), (uint32_t)b * rb32);
-                fused_lds16(xr, xs[k] + u * 2048 + 1024, opaque(xl[u]) + rs16, (uint32_t)b * rb32);
+                fused_lds16(xr, XS(k) + u * 2048, opaque(xl[u]), (uint32_t)b * rb32);
+                fused_lds16(xr, XS(k) + u * 2048 + 1024, opaque(xl[u]) + rs16, (uint32_t)b * rb32);
             }
 #pragma unroll
-            for (int p = 0; p < NPAIR; ++p) fused_lds4(lar, las[k] + 256 * p, opaque(ll[p]), (uint32_t)b * lab32);
+            for (int p = 0; p < NPAIR; ++p) fused_lds4(lar, LA(k) + 256 * p, opaque(ll[p]), (uint32_t)b * lab32);
         };
         float lsig[NPAIR];
 #pragma unroll
         for (int p = 0; p < NPAIR; ++p) lsig[p] = 0.f;
         auto products = [&](int b, auto kc) __attribute__((always_inline)) {
             constexpr int k = decltype(kc)::value;
-            unsigned char* pb = pbuf(b);
-            const float* la = reinterpret_cast<const float*>(las[k]);
+            lds_ptr pb = pbuf(b);
+            const lds_ptr la = LA(k);
 #pragma unroll
             for (int p = 0; p < NPAIR; ++p) {
                 const int jh = 2 * p + lg;
                 // inclusive cumsum over the 32 rows of each half (log2 units)
-                const float c = scan32(la[64 * p + lane] * kLog2e);
+                const float c = scan32(ldsv<float>(la + 4 * (64 * p + lane)) * kLog2e);
                 const float e = lg ? lane_f(c, 63) : lane_f(c, 31);
                 const float c0 = lg ? lane_f(c, 32) : lane_f(c, 0);
                 // path: 2 = exact form (span over 100), 1 = renormalise first, 0 = plain
@@ -277,12 +300,12 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, unsigned char* co
                 const float f = fast_exp2(ls + e);
                 lsig[p] = lnew;
                 if (jh < NHL) {
-                    reinterpret_cast<float*>(pb + L::w)[32 * jh + sigma_pos(lr)] = w;
-                    reinterpret_cast<float*>(pb + L::r)[32 * jh + lr] = r;
-                    reinterpret_cast<float*>(pb + L::cs)[32 * jh + lr] = c;
+                    ldsw<float>(pb + L::w + 4 * (32 * jh + sigma_pos(lr)), w);
+                    ldsw<float>(pb + L::r + 4 * (32 * jh + lr), r);
+                    ldsw<float>(pb + L::cs + 4 * (32 * jh + lr), c);
                     if (lr == 0) {
-                        reinterpret_cast<float*>(pb + L::f)[jh] = f;
-                        reinterpret_cast<int*>(pb + L::fl)[jh] = steep ? 2 : renorm ? 1 : 0;
+                        ldsw<float>(pb + L::f + 4 * jh, f);
+                        ldsw<int>(pb + L::fl + 4 * jh, steep ? 2 : renorm ? 1 : 0);
                     }
                 }
             }
@@ -291,7 +314,7 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, unsigned char* co
         // the heads' final log scales for the compute waves' final states
 #pragma unroll
         for (int p = 0; p < NPAIR; ++p)
-            if (2 * p + lg < NHL && lr == 0) reinterpret_cast<float*>(pbuf(0) + L::f)[2 * p + lg] = lsig[p];
+            if (2 * p + lg < NHL && lr == 0) ldsw<float>(pbuf(0) + L::f + 4 * (2 * p + lg), lsig[p]);
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_s_barrier();
         return;
@@ -323,25 +346,31 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, unsigned char* co
             constexpr int k = decltype(kc)::value;
             b = min(b, nb - 1);
 #pragma unroll
-            for (int i = 0; i < NBL; ++i) fused_lds16(br, bs[k] + 1024 * i, opaque(bl[i]), (uint32_t)b * bcb32);
+            for (int i = 0; i < NBL; ++i) fused_lds16(br, BS(k) + 1024 * i, opaque(bl[i]), (uint32_t)b * bcb32);
 #pragma unroll
-            for (int i = 0; i < NBL; ++i) fused_lds16(cr, cs_[k] + 1024 * i, opaque(bl[i]), (uint32_t)b * bcb32);
+            for (int i = 0; i < NBL; ++i) fused_lds16(cr, CS(k) + 1024 * i, opaque(bl[i]), (uint32_t)b * bcb32);
 #pragma unroll
-            for (int p = 0; p < NPAIR; ++p) fused_lds4(lar, las2[k] + 256 * p, opaque(ll[p]), (uint32_t)b * lab32);
+            for (int p = 0; p < NPAIR; ++p) fused_lds4(lar, LA2(k) + 256 * p, opaque(ll[p]), (uint32_t)b * lab32);
         };
         auto products = [&](int b, auto kc) __attribute__((always_inline)) {
             constexpr int k = decltype(kc)::value;
-            unsigned char* pb = pbuf(b);
-            // D^T = B C^T (s x l) on MFMA, rows of both from the slot, two accumulator chains
-            const __bf16* bsl = reinterpret_cast<const __bf16*>(bs[k]);
-            const __bf16* csl = reinterpret_cast<const __bf16*>(cs_[k]);
+            lds_ptr pb = pbuf(b);
+            // D^T = B C^T (s x l) on MFMA, rows of both from the slot, two accumulator chains;
+            // every fragment is read before the first product (one LDS round trip, not one per
+            // K-step)
+            const lds_ptr bsl = BS(k), csl = CS(k);
+            bf16x8 bfr[NP / 16], cfr[NP / 16];
+#pragma unroll
+            for (int kk = 0; kk < NP / 16; ++kk) {
+                const int o = 2 * (lr * NP + 8 * ((2 * kk + lg) ^ fused_swz<NP>(lr)));
+                bfr[kk] = ldsv<bf16x8>(bsl + o);
+                cfr[kk] = ldsv<bf16x8>(csl + o);
+            }
             f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
             for (int kk = 0; kk < NP / 16; kk += 2) {
-                const int o0 = lr * NP + 8 * ((2 * kk + lg) ^ fused_swz<NP>(lr));
-                const int o1 = lr * NP + 8 * ((2 * kk + 2 + lg) ^ fused_swz<NP>(lr));
-                acc0 = E::mma(acc0, E::lds8(bsl + o0), E::lds8(csl + o0));
-                acc1 = E::mma(acc1, E::lds8(bsl + o1), E::lds8(csl + o1));
+                acc0 = E::mma(acc0, bfr[kk], cfr[kk]);
+                acc1 = E::mma(acc1, bfr[kk + 1], cfr[kk + 1]);
             }
             // causal mask (s <= l) and the fragments (K-step ks = elements 8 ks .. 8 ks + 7)
 #pragma unroll
@@ -353,14 +382,14 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, unsigned char* co
                     const int srow = 8 * (e8 >> 2) + 4 * lg + (e8 & 3);
                     d[q8] = (__bf16)(srow <= lr ? acc0[e8] + acc1[e8] : 0.f);
                 }
-                *reinterpret_cast<bf16x8*>(pb + L::dg + 1024 * ks + 16 * lane) = d;
+                ldsw<bf16x8>(pb + L::dg + 1024 * ks + 16 * lane, d);
             }
             // exact tiles of the heads whose block spans more than 100 (the X-loader's test
             // on the same cumsum): D'^T[s][l] = D^T[s][l] 2^(cs_l - cs_s)
-            const float* la = reinterpret_cast<const float*>(las2[k]);
+            const lds_ptr la = LA2(k);
 #pragma unroll
             for (int p = 0; p < NPAIR; ++p) {
-                const float c = scan32(la[64 * p + lane] * kLog2e);
+                const float c = scan32(ldsv<float>(la + 4 * (64 * p + lane)) * kLog2e);
                 const float e = lg ? lane_f(c, 63) : lane_f(c, 31);
                 const float c0 = lg ? lane_f(c, 32) : lane_f(c, 0);
                 const bool steep_lo = lane_f(c, 0) - lane_f(c, 31) > 100.f;
@@ -384,7 +413,7 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, unsigned char* co
                                 const float csr = __shfl(c, 32 * hh + srow);
                                 t8[q8] = (__bf16)(srow <= lr ? (acc0[e8] + acc1[e8]) * fast_exp2(cl - csr) : 0.f);
                             }
-                            *reinterpret_cast<bf16x8*>(pb + L::st + 2048 * jh + 1024 * ks + 16 * lane) = t8;
+                            ldsw<bf16x8>(pb + L::st + 2048 * jh + 1024 * ks + 16 * lane, t8);
                         }
                     }
                 }
@@ -445,27 +474,23 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, unsigned char* co
     }
     // (rows 16 ks + 8 j + rb have rb's part 4 (r % U4) of the swizzle, U4 dividing 8; only the
     // low two bits, (r / U4) % 4, change with ks and j)
-    auto ldsb = [&](const unsigned char* base, int off) __attribute__((always_inline)) -> bf16x4 {
-        return tr4(reinterpret_cast<const __bf16*>(base + off));
-    };
+    auto ldsb = [&](lds_ptr base, int off) __attribute__((always_inline)) -> bf16x4 { return tr4(base + off); };
 
     __builtin_amdgcn_s_barrier();
     auto step = [&](int t, auto kc) __attribute__((always_inline)) {
         constexpr int k = decltype(kc)::value;
-        const unsigned char* pb = pbuf(t);
-        const __bf16* xsl = reinterpret_cast<const __bf16*>(xs[k]);
-        const unsigned char* bsl = bs[k];
-        const unsigned char* csl = cs_[k];
+        const lds_ptr pb = pbuf(t);
+        const lds_ptr xsl = XS(k), bsl = BS(k), csl = CS(k);
         // X of the block (K-step ks: rows 16 ks + sigma(8 lg + q))
         bf16x8 xf[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-            xf[ks] = cat44(tr4(xsl + (xa0 + 1024 * ks) / 2), tr4(xsl + (xa0 + 1024 * ks + 512) / 2));
-        const f32x4* wp = reinterpret_cast<const f32x4*>(pb + L::w + 128 * jh + 32 * lg);
-        const f32x4 w00 = wp[0], w01 = wp[1], w10 = wp[4], w11 = wp[5];
-        const float rl = reinterpret_cast<const float*>(pb + L::r)[32 * jh + lr];
-        const int flag = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int*>(pb + L::fl)[jh]);
-        const float f = reinterpret_cast<const float*>(pb + L::f)[jh];
+            xf[ks] = cat44(tr4(xsl + xa0 + 1024 * ks), tr4(xsl + xa0 + 1024 * ks + 512));
+        const lds_ptr wp = pb + L::w + 128 * jh + 32 * lg;
+        const f32x4 w00 = ldsv<f32x4>(wp), w01 = ldsv<f32x4>(wp + 16), w10 = ldsv<f32x4>(wp + 64), w11 = ldsv<f32x4>(wp + 80);
+        const float rl = ldsv<float>(pb + L::r + 4 * (32 * jh + lr));
+        const int flag = __builtin_amdgcn_readfirstlane(ldsv<int>(pb + L::fl + 4 * jh));
+        const float f = ldsv<float>(pb + L::f + 4 * jh);
         const float ws[2][8] = {{w00[0], w00[1], w00[2], w00[3], w01[0], w01[1], w01[2], w01[3]},
                                 {w10[0], w10[1], w10[2], w10[3], w11[0], w11[1], w11[2], w11[3]}};
         bf16x8 xt[2];
@@ -479,8 +504,8 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, unsigned char* co
             bf16x8 cf[2], bt[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const u32x2 lo = *reinterpret_cast<const u32x2*>(csl + cnt[nt] + cm[2 * kk]);
-                const u32x2 hi = *reinterpret_cast<const u32x2*>(csl + cnt[nt] + cm[2 * kk + 1]);
+                const u32x2 lo = ldsv<u32x2>(csl + cnt[nt] + cm[2 * kk]);
+                const u32x2 hi = ldsv<u32x2>(csl + cnt[nt] + cm[2 * kk + 1]);
                 cf[kk] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
                 bt[kk] = cat44(ldsb(bsl, bnt[nt] + bm[kk][0] + 32 * NP * kk),
                                ldsb(bsl, bnt[nt] + bm[kk][1] + 32 * NP * kk + 16 * NP));
@@ -506,8 +531,8 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, unsigned char* co
             }
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) ntile(acc, nt, false);
-            const bf16x8 d0 = *reinterpret_cast<const bf16x8*>(pb + L::dg + 16 * lane);
-            const bf16x8 d1 = *reinterpret_cast<const bf16x8*>(pb + L::dg + 1024 + 16 * lane);
+            const bf16x8 d0 = ldsv<bf16x8>(pb + L::dg + 16 * lane);
+            const bf16x8 d1 = ldsv<bf16x8>(pb + L::dg + 1024 + 16 * lane);
             acc = E::mma(acc, xt[0], d0);
             acc = E::mma(acc, xt[1], d1);
             acc *= rl;
@@ -517,9 +542,9 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, unsigned char* co
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) ntile(acc, nt, true);
             acc *= rl;
-            const unsigned char* stp = pb + L::st + 2048 * jh;
-            const bf16x8 d0 = *reinterpret_cast<const bf16x8*>(stp + 16 * lane);
-            const bf16x8 d1 = *reinterpret_cast<const bf16x8*>(stp + 1024 + 16 * lane);
+            const lds_ptr stp = pb + L::st + 2048 * jh;
+            const bf16x8 d0 = ldsv<bf16x8>(stp + 16 * lane);
+            const bf16x8 d1 = ldsv<bf16x8>(stp + 1024 + 16 * lane);
             acc = E::mma(acc, xf[0], d0);
             acc = E::mma(acc, xf[1], d1);
         }
@@ -555,7 +580,7 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, unsigned char* co
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_s_barrier();
     if (a.final_state && valid) {
-        const float fs = fast_exp2(reinterpret_cast<const float*>(pbuf(0) + L::f)[jh]);
+        const float fs = fast_exp2(ldsv<float>(pbuf(0) + L::f + 4 * jh));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -570,21 +595,6 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, unsigned char* co
 
 template <int NP, int NW>
 __global__ void __launch_bounds__(64 * (NW + 2), 1) ssd_walk_fused_kernel(FusedArgs a) {
-    typedef FusedLds<NP, NW> L;
-    constexpr int NS = L::nslot;
-    __shared__ __align__(16) unsigned char x0[L::xbytes], x1[L::xbytes], x2[L::xbytes], x3[NS == 4 ? L::xbytes : 16];
-    __shared__ __align__(16) unsigned char b0[L::bcbytes], b1[L::bcbytes], b2[L::bcbytes], b3[NS == 4 ? L::bcbytes : 16];
-    __shared__ __align__(16) unsigned char c0[L::bcbytes], c1[L::bcbytes], c2[L::bcbytes], c3[NS == 4 ? L::bcbytes : 16];
-    __shared__ __align__(16) unsigned char l0[L::labytes], l1[L::labytes], l2[L::labytes], l3[NS == 4 ? L::labytes : 16];
-    __shared__ __align__(16) unsigned char m0[L::labytes], m1[L::labytes], m2[L::labytes], m3[NS == 4 ? L::labytes : 16];
-    __shared__ __align__(16) unsigned char p0[L::prod], p1[L::prod];
-    unsigned char* const xs[4] = {x0, x1, x2, x3};
-    unsigned char* const bs[4] = {b0, b1, b2, b3};
-    unsigned char* const cs[4] = {c0, c1, c2, c3};
-    unsigned char* const las[4] = {l0, l1, l2, l3};
-    unsigned char* const las2[4] = {m0, m1, m2, m3};
-    unsigned char* const prod[2] = {p0, p1};
-
     const int lane = threadIdx.x & 63;
     const int G = a.G, wpg = a.wpg;
     int s, g, q;
@@ -618,7 +628,7 @@ __global__ void __launch_bounds__(64 * (NW + 2), 1) ssd_walk_fused_kernel(FusedA
         g = sg % G;
         s = sg / G;
     }
-    fused_walk<NP, NW>(a, xs, bs, cs, las, las2, prod, s, g, q);
+    fused_walk<NP, NW>(a, s, g, q);
 }
 
 }  // namespace ssd
