@@ -2,9 +2,17 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-A step is one whole SSD forward (both launches: chunk cumsum + C B^T tiles, then the
-chunk walk) over one synthetic batch already resident in HBM.  Prints ONE JSON line
-on stdout; progress goes to stderr.
+A step is one whole SSD forward over one synthetic batch already resident in HBM: the
+launches the library plans for the shape (one fused walk for bf16 layer shapes that fill
+the chip; else a prep launch of chunk cumsums and C B^T tiles, then the chunk walk, and a
+summary pass where sequences are split).  Prints ONE JSON line on stdout; progress goes to
+stderr.  The kernels timed are the ones the library reports for the shape
+(``ssd_plan_describe``).
+
+Warm-up runs the requested steps, then more until it has run for at least MIN_WARM_S
+seconds (the chip needs some tens of milliseconds to reach its steady clocks).  Besides
+the warm figure the line carries a cold one: the median of per-step times with a 512 MiB
+buffer read before each step, which evicts the inputs from the last-level cache.
 
 Roofline: the dominant launch is the chunk walk.  Its algorithmic bytes are the
 minimum traffic of the layer: read X, B, C and logA once, write Y and the final state
@@ -19,7 +27,7 @@ program for the FETCH_SIZE / WRITE_SIZE counters.
 
 ``--mode report`` prints one JSON line per workload configuration (all of them, or the
 one ``--workload`` names): the median of per-step HIP-event times with the last-level
-cache flushed before every step (a 512 MiB write) and without, the FLOP rates by the
+cache flushed before every step (a 512 MiB read) and without, the FLOP rates by the
 pages' count and by its causal half, and the fractions of the MFMA peak and of the
 roofline (the parity of each configuration is the full-size tests' business).
 """
@@ -39,6 +47,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 matrix/vector, published
 COUNTERS_JSON = os.path.join(ROOT, "profiles", "walk_cfg1_hbm_counters.json")
+MIN_WARM_S = 0.5               # least wall time of warm-up before the timed steps
 
 
 def log(*a):
@@ -47,7 +56,8 @@ def log(*a):
 
 # the sources of the forward kernels and of their launch plan (the backward pass's files
 # are not among them)
-FORWARD_SOURCES = ("ssd_device.h", "ssd_kernels.h", "ssd_walk_split.h", "ssd_walk_quad.h", "ssd_api.hip")
+FORWARD_SOURCES = ("ssd_device.h", "ssd_kernels.h", "ssd_walk_split.h", "ssd_walk_quad.h", "ssd_walk_fused.h",
+                   "ssd_api.hip")
 
 
 def kernel_source_hash():
@@ -56,27 +66,6 @@ def kernel_source_hash():
         with open(os.path.join(ROOT, "mamba_ssd_scan_forward_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
-
-
-def walk_kernel_name(w):
-    """The walk kernel that the library's planner picks for this workload."""
-    if w.dtype == "bf16" and w.chunk_len == 256 and w.dstate in (64, 128) and w.headdim % 64 == 0:
-        hpg = w.nheads // w.ngroups
-        nseq = w.nseq if w.varlen else w.batch
-        it4 = nseq * w.ngroups * ((hpg + 3) // 4)
-        if w.headdim == 64 and hpg >= 2 and it4 >= 128:
-            hq = 4
-            if hpg >= 3:
-                it3 = nseq * w.ngroups * ((hpg + 2) // 3)
-                if w.varlen:
-                    hq = 3 if 85 * it3 < 100 * it4 else 4
-                else:
-                    hq = 3 if 85 * -(-it3 // 256) < 100 * -(-it4 // 256) else 4
-            return f"ssd_walk_quad_kernel<{w.dstate}, 1, {hq}>"
-        return f"ssd_walk_split_kernel<{w.dstate}, false, false>"
-    if w.dtype == "bf16" and w.chunk_len == 256 and w.dstate == 256 and w.headdim % 64 == 0:
-        return "ssd_walk_split_pair_kernel<128>"
-    return "ssd_walk_kernel"
 
 
 def algorithmic_bytes(w, es):
@@ -114,6 +103,40 @@ def chunk_lengths(w, lens):
         full, rem = divmod(L, w.chunk_len)
         out += [w.chunk_len] * full + ([rem] if rem else [])
     return out
+
+
+def flush_by_reading(buf):
+    """Evict the last-level cache by reading a buffer twice its size: the cache is left
+    holding clean lines, so the next kernel neither hits on its inputs nor pays for
+    writing back a flush buffer's dirty lines."""
+    buf.max()
+
+
+def executed_mfma_flops(plan, w, lens):
+    """FLOPs of the MFMA instructions the fused walker issues (v_mfma_f32_32x32x16_bf16,
+    32768 each): per 32-row block and 32-column unit of a head, 8 for the left factor, 8
+    for the state update and 2 for the diagonal block (N = 128; N/16 each of the first two
+    in general); per block and workgroup N/16 for the tile C B^T.  None for other walks."""
+    walk = plan.get("walk", "")
+    if not walk.startswith("ssd_walk_fused_kernel<"):
+        return None
+    nw = int(walk.split("<")[1].split(",")[1].strip(" >"))
+    ks = w.dstate // 16
+    units = (w.nheads // w.ngroups) * (w.headdim // 32)
+    wpg = -(-units // nw)
+    blocks = sum(-(-int(L) // 32) for L in lens)
+    per_unit = 2 * ks + 2
+    mfmas = blocks * w.ngroups * (units * per_unit + wpg * ks)
+    return mfmas * 32768
+
+
+PAGES_CONTEXT = {
+    "vs_mamba_selective_scan": "2-8x faster (paper summary page, section 9.3, Fig. 10 left; state size 64)",
+    "vs_flashattention2": "on par at sequence length 2K (news page) / faster from 2K (paper summary page), "
+                          "about 6x faster at 16K",
+    "state_size_sweep": "SSD slows little as the state grows, the selective scan linearly (Fig. 10 right)",
+    "hardware": "A100 80GB PCIe per the paper summary page's appendix; absolute times are not given",
+}
 
 
 def run_copy_mode(steps):
@@ -267,7 +290,7 @@ def run_report_mode(args):
                    for _ in range(steps)]
             for i, (a, b) in enumerate(evs):
                 if cold:
-                    flush.fill_(i & 0xFF)
+                    flush_by_reading(flush)
                 a.record(stream)
                 step()
                 b.record(stream)
@@ -290,8 +313,9 @@ def run_report_mode(args):
         line = {
             "workload": name, "config": w.shape_dict(), "chunk_len": w.chunk_len,
             "time_us": round(cold_us, 2), "time_us_warm": round(warm_us, 2),
-            "timing": f"median of {steps} HIP-event-timed steps; 'time_us' with a 512 MiB write "
-                      f"before each step, 'time_us_warm' back to back",
+            "timing": f"median of {steps} HIP-event-timed steps; 'time_us' with a 512 MiB buffer read "
+                      f"before each step (evicts the inputs from the 256 MB last-level cache and leaves "
+                      f"it holding clean lines), 'time_us_warm' back to back",
             "tokens_per_s": round(tokens / (cold_us * 1e-6), 1),
             "tokens_per_s_warm": round(tokens / (warm_us * 1e-6), 1),
             "gflop_pages": round(fp / 1e9, 3), "gflop_causal": round(fc / 1e9, 3),
@@ -392,9 +416,21 @@ def main():
         if rc != 0:
             raise ssd.SsdError(rc, f"ssd_forward_stage({k})")
 
+    plan = ssd.ssd_plan_describe(prob)
+    log(f"[bench] plan {plan}")
+    # warm-up: the requested steps, then more until the chip has run for MIN_WARM_S (it
+    # takes a few hundred steps, some tens of milliseconds, to reach its steady clocks)
+    t0 = time.perf_counter()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    warm_steps = args.warmup
+    while time.perf_counter() - t0 < MIN_WARM_S:
+        for _ in range(50):
+            step()
+        torch.cuda.synchronize()
+        warm_steps += 50
+    warm_s = time.perf_counter() - t0
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -403,6 +439,20 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
+
+    # cold: each step after a 512 MiB read that evicts the inputs from the last-level cache
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush.fill_(1)
+    n_cold = max(5, min(args.steps, 30))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_cold)]
+    for a_, b_ in evs:
+        flush_by_reading(flush)
+        a_.record(stream)
+        step()
+        b_.record(stream)
+    torch.cuda.synchronize()
+    cold_ms = statistics.median(a_.elapsed_time(b_) for a_, b_ in evs)
+    del flush
 
     # each launch alone, on the same stream, same events
     stage_ms = {}
@@ -428,7 +478,8 @@ def main():
         b_.record(stream)
     torch.cuda.synchronize()
     walk_in_step_ms = statistics.mean(a_.elapsed_time(b_) for a_, b_ in ev)
-    log(f"[bench] step {ms_step * 1e3:.1f} us; prep {stage_ms[1] * 1e3:.1f} us; "
+    log(f"[bench] step {ms_step * 1e3:.1f} us warm ({warm_steps} warm-up steps, {warm_s:.2f} s), "
+        f"{cold_ms * 1e3:.1f} us cold; prep {stage_ms[1] * 1e3:.1f} us; "
         f"walk {stage_ms[2] * 1e3:.1f} us back to back, {walk_in_step_ms * 1e3:.1f} us per launch in steps")
 
     # the recurrent decode step (one token per sequence, state updated in place) at the
@@ -497,13 +548,16 @@ def main():
         machine = measure_machine(lambda: stage(2), stream, dev)
         log(f"[bench] machine: {machine}")
 
-    lens = [w.seqlen] * w.batch if not w.varlen else list(np.diff(inp.seq_offsets))
+    lens = [w.seqlen] * w.batch if not w.varlen else [int(v) for v in np.diff(inp.seq_offsets)]
     tokens = w.batch * w.seqlen
-    fl = flops_pages(w, chunk_lengths(w, [int(v) for v in lens]))
+    cl = chunk_lengths(w, lens)
+    fl, fc = flops_pages(w, cl), flops_causal(w, cl)
+    fx = executed_mfma_flops(plan, w, lens)
     abytes = algorithmic_bytes(w, es)
     tok_s = tokens / (ms_step * 1e-3)
     peak_mm = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
     achieved_gbs = abytes / (walk_in_step_ms * 1e-3) / 1e9
+    t_roof_ms = max(fl / (peak_mm * 1e12), abytes / (HBM_PEAK_GBS * 1e9)) * 1e3
 
     traffic = None
     if os.path.exists(COUNTERS_JSON):
@@ -528,12 +582,24 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded: X~N(0,1), B,C~N(0,1/N), logA=-U[.001,.1]*U[1,16])",
         "config": dict(workload=name, **w.shape_dict()),
+        "warmup_run": {"steps": warm_steps, "seconds": round(warm_s, 3), "min_seconds": MIN_WARM_S,
+                       "note": "the requested warm-up steps, then more until the chip had run for min_seconds"},
+        "cold": {"ms_per_step": round(cold_ms, 5), "tokens_per_s": round(tokens / (cold_ms * 1e-3), 1),
+                 "steps": n_cold, "timing": "median of per-step HIP-event times, a 512 MiB buffer read "
+                                            "before each step (inputs evicted from the 256 MB last-level cache)"},
         "tflops_pages": round(fl / (ms_step * 1e-3) / 1e12, 2),
+        "tflops_causal": round(fc / (ms_step * 1e-3) / 1e12, 2),
         "mfma_util_pages": round(fl / (ms_step * 1e-3) / 1e12 / peak_mm, 4),
+        "mfma_util_causal": round(fc / (ms_step * 1e-3) / 1e12 / peak_mm, 4),
+        "mfma_util_executed": None if fx is None else round(fx / (ms_step * 1e-3) / 1e12 / peak_mm, 4),
+        "mfma_util_note": "pages: the block decomposition's products as the pages count them (dense QxQ "
+                          "diagonal blocks, the figure the 0.40 target is stated in); causal: their lower "
+                          "halves; executed: the MFMA instructions the kernel issues",
+        "plan": plan,
         "stage_us": {"prep": round(stage_ms[1] * 1e3, 2), "walk": round(stage_ms[2] * 1e3, 2),
                      "walk_per_launch_in_steps": round(walk_in_step_ms * 1e3, 2)},
         "roofline": {
-            "kernel": walk_kernel_name(w),
+            "kernel": plan["walk"],
             "bound": "hbm",
             "achieved": round(achieved_gbs, 1),
             "peak": HBM_PEAK_GBS,
@@ -541,7 +607,10 @@ def main():
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "algorithmic_bytes": abytes,
+            "step_frac": round(t_roof_ms / ms_step, 4),
+            "step_frac_cold": round(t_roof_ms / cold_ms, 4),
         },
+        "pages_context": PAGES_CONTEXT,
     }
 
     if machine is not None:
@@ -560,22 +629,29 @@ def main():
         import oracle
         x64 = [np.asarray(a, dtype=np.float64) for a in (inp.X, inp.logA, inp.B, inp.C)]
         i64 = None if inp.init is None else inp.init.astype(np.float64)
-        oracle.recurrence(*[a[:, :64] for a in x64], None if i64 is None else i64, None)  # warm
+        # every core this process may run on (sched_getaffinity), no more than the OpenMP
+        # thread limit of the environment when one is set
+        affinity = len(os.sched_getaffinity(0))
+        nthr = min(affinity, oracle.threads()) if os.environ.get("OMP_NUM_THREADS") else affinity
+        oracle.recurrence(*[a[:, :64] for a in x64], None if i64 is None else i64, None, nthreads=nthr)  # warm
+        # whole passes over the workload until about 10 s of CPU work have run
         times = []
-        for _ in range(3):
+        while len(times) < 3 or (sum(times) < 10.0 and len(times) < 200):
             t0 = time.perf_counter()
-            oracle.recurrence(*x64, i64, inp.seq_offsets)
+            oracle.recurrence(*x64, i64, inp.seq_offsets, nthreads=nthr)
             times.append(time.perf_counter() - t0)
         t = statistics.median(times)
         result["cpu_baseline"] = {
             "value": round(tokens / t, 1),
             "unit": "tokens/s",
-            "cores": oracle.threads(),
+            "cores": nthr,
+            "affinity_cores": affinity,
             "kind": "oracle",
             "sample": f"whole workload ({tokens} tokens, all {w.nheads} heads), float64 "
-                      f"recurrence, median of 3 runs ({t:.2f}s each)",
+                      f"recurrence on {nthr} threads, median of {len(times)} passes ({t:.2f}s each, "
+                      f"{sum(times):.1f}s in all)",
         }
-        log(f"[bench] oracle {t:.2f}s on {oracle.threads()} threads")
+        log(f"[bench] oracle {t:.2f}s on {nthr} threads ({affinity} cores in the affinity mask)")
     print(json.dumps(result), flush=True)
 
 

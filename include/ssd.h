@@ -113,7 +113,8 @@ int ssd_forward(const ssd_problem* p, const void* X, const float* logA, const vo
 
 /* One of the two launches that make up ssd_forward, with the same arguments and checks.
  *   stage 1: chunk cumsum of logA and the C B^T tiles of every chunk, written to the
- *            workspace (page section 6.1 and Listing 1 step 1 inputs);
+ *            workspace (page section 6.1 and Listing 1 step 1 inputs); nothing, for the
+ *            plans whose walk forms these itself (ssd_plan_describe: prep=none);
  *   stage 2: the chunk walk: outputs, chunk states and state passing (section 6.1 and
  *            6.2), reading the workspace that a stage-1 call with the same problem and
  *            inputs left there.
@@ -180,6 +181,14 @@ const char* ssd_status_string(int status);
 
 /* ABI revision of this header; bumped on any incompatible change. */
 int ssd_abi_version(void);
+
+/* The kernels ssd_forward launches for problem p, as text for logs and benchmarks:
+ * "walk=<kernel>;prep=<kernel or none>;summary=<kernel or none>", for example
+ * "walk=ssd_walk_fused_kernel<128, 5>;prep=none;summary=none".  Writes at most len
+ * bytes, NUL-terminated, to buf (host memory).  Returns SSD_OK, the status of
+ * ssd_check_problem for an invalid or unsupported problem, or SSD_ERR_INVALID_ARG for a
+ * NULL buf or len 0.  No device work. */
+int ssd_plan_describe(const ssd_problem* p, char* buf, size_t len);
 
 #define SSD_ABI_VERSION 1
 

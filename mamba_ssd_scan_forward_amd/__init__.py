@@ -25,7 +25,7 @@ __all__ = [
     "SSD_DTYPE_F32", "SSD_DTYPE_BF16", "SsdProblem", "SsdError", "lib_path", "load_library",
     "ssd_check_problem", "ssd_workspace_bytes", "ssd_forward", "ssd_forward_stage",
     "ssd_decode_step", "ssd_backward_workspace_bytes", "ssd_backward", "ssd_status_string",
-    "ssd_abi_version", "forward", "decode_step", "backward", "problem_for",
+    "ssd_abi_version", "ssd_plan_describe", "forward", "decode_step", "backward", "problem_for",
 ]
 
 SSD_OK = 0
@@ -88,6 +88,8 @@ def load_library():
     lib.ssd_backward.restype = ctypes.c_int
     lib.ssd_status_string.argtypes = [ctypes.c_int]
     lib.ssd_status_string.restype = ctypes.c_char_p
+    lib.ssd_plan_describe.argtypes = [pp, ctypes.c_char_p, sz]
+    lib.ssd_plan_describe.restype = ctypes.c_int
     lib.ssd_abi_version.argtypes = []
     lib.ssd_abi_version.restype = ctypes.c_int
     if lib.ssd_abi_version() != ABI_VERSION:
@@ -130,6 +132,16 @@ def ssd_status_string(status: int) -> str:
 
 def ssd_abi_version() -> int:
     return int(load_library().ssd_abi_version())
+
+
+def ssd_plan_describe(problem: SsdProblem) -> dict:
+    """The kernels ssd_forward launches for this problem: {"walk": ..., "prep": ...,
+    "summary": ...} ("none" where a launch is not made)."""
+    buf = ctypes.create_string_buffer(256)
+    rc = load_library().ssd_plan_describe(ctypes.byref(problem), buf, len(buf))
+    if rc != SSD_OK:
+        raise SsdError(rc, "ssd_plan_describe")
+    return dict(kv.split("=", 1) for kv in buf.value.decode().split(";"))
 
 
 def ssd_check_problem(problem: SsdProblem) -> int:

@@ -5,6 +5,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <cstdio>
 
 #include "ssd.h"
 #include "ssd_kernels.h"
@@ -404,6 +405,34 @@ int ssd_check_problem(const ssd_problem* p) {
     if (!p) return SSD_ERR_INVALID_ARG;
     Plan pl;
     return make_plan(p, &pl);
+}
+
+int ssd_plan_describe(const ssd_problem* p, char* buf, size_t len) {
+    if (!buf || len == 0) return SSD_ERR_INVALID_ARG;
+    buf[0] = 0;
+    if (!p) return SSD_ERR_INVALID_ARG;
+    Plan pl;
+    const int rc = make_plan(p, &pl);
+    if (rc != SSD_OK) return rc;
+    char walk[96];
+    const char* prep = p->dtype == SSD_DTYPE_BF16 ? "ssd_prep_kernel<bf16>" : "ssd_prep_kernel<float>";
+    const char* summary = "none";
+    if (pl.fused) {
+        snprintf(walk, sizeof walk, "ssd_walk_fused_kernel<%d, %d>", (int)p->dstate, pl.fused);
+        prep = "none";
+    } else if (pl.quad) {
+        snprintf(walk, sizeof walk, "ssd_walk_quad_kernel<%d, 1, %d>", (int)p->dstate, pl.quad);
+    } else if (pl.npass == 2) {
+        snprintf(walk, sizeof walk, "ssd_walk_split_pair_kernel<128>+ssd_add_kernel<bf16>");
+    } else if (pl.split) {
+        snprintf(walk, sizeof walk, "ssd_walk_split_kernel<%d, false, false>", (int)p->dstate);
+        if (pl.nseg > 1) summary = p->dstate == 64 ? "ssd_walk_split_kernel<64, true, false>"
+                                                    : "ssd_walk_split_kernel<128, true, false>";
+    } else {
+        snprintf(walk, sizeof walk, "ssd_walk_kernel");
+    }
+    snprintf(buf, len, "walk=%s;prep=%s;summary=%s", walk, prep, summary);
+    return SSD_OK;
 }
 
 size_t ssd_workspace_bytes(const ssd_problem* p) {

@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["ssd_abi_version", "ssd_backward", "ssd_backward_workspace_bytes",
                                            "ssd_check_problem", "ssd_decode_step", "ssd_forward",
-                                           "ssd_forward_stage", "ssd_status_string", "ssd_workspace_bytes"])
+                                           "ssd_forward_stage", "ssd_plan_describe", "ssd_status_string",
+                                           "ssd_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -264,3 +265,17 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ssd, "lib_path", lambda: str(tmp_path / "libssd.so"))
     with pytest.raises(ImportError):
         ssd.load_library()
+
+
+def test_plan_describe_names_the_kernels():
+    # the planner is host logic: the kernels a shape gets are known without a device
+    bf16, f32 = ssd.SSD_DTYPE_BF16, ssd.SSD_DTYPE_F32
+    layer = ssd.problem_for(8, 2048, 80, 64, 128, 1, 256, 8, bf16)
+    assert ssd.ssd_plan_describe(layer) == {"walk": "ssd_walk_fused_kernel<128, 5>", "prep": "none",
+                                            "summary": "none"}
+    small = ssd.problem_for(1, 256, 4, 64, 64, 1, 256, 1, f32)
+    d = ssd.ssd_plan_describe(small)
+    assert d["walk"] != "none" and "fused" not in d["walk"] and d["prep"] != "none"
+    bad = ssd.problem_for(1, 256, 4, 64, 64, 3, 256, 1, bf16)     # heads not a multiple of groups
+    with pytest.raises(ssd.SsdError):
+        ssd.ssd_plan_describe(bad)
