@@ -48,7 +48,9 @@ typedef enum ssd_status {
     SSD_ERR_INVALID_ARG = -1,  /* null/misaligned/aliased pointer, bad dimension      */
     SSD_ERR_UNSUPPORTED = -2,  /* dtype, chunk_len, headdim or dstate outside support */
     SSD_ERR_WORKSPACE = -3,    /* workspace smaller than ssd_workspace_bytes()        */
-    SSD_ERR_HIP = -4           /* a HIP runtime call or kernel launch failed          */
+    SSD_ERR_HIP = -4,          /* a HIP runtime call or kernel launch failed          */
+    SSD_ERR_TOO_LARGE = -5     /* ssd_forward_noalloc: the problem needs more scratch
+                                  than SSD_NOALLOC_SCRATCH_BYTES                      */
 } ssd_status;
 
 typedef enum ssd_dtype {
@@ -189,6 +191,24 @@ int ssd_abi_version(void);
  * ssd_check_problem for an invalid or unsupported problem, or SSD_ERR_INVALID_ARG for a
  * NULL buf or len 0.  No device work. */
 int ssd_plan_describe(const ssd_problem* p, char* buf, size_t len);
+
+/* ssd_forward for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same arguments, checks
+ * and results as ssd_forward, without the workspace: the kernels that need scratch use a
+ * fixed array of SSD_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs
+ * on until the process ends.  The call allocates nothing (no hipMalloc or allocating
+ * library routine).  Its first call on a device looks up that device's array address; the
+ * stream (NULL = the default stream) must belong to the current device.
+ * All calls on one device share its array, and a call leaves its contents behind: calls
+ * whose work overlaps on one device (on different streams, or from several threads) race
+ * and give wrong results; calls ordered on one stream are safe.  Nothing in the array has
+ * to start at zero.
+ * Returns SSD_ERR_TOO_LARGE, before any device work, when ssd_workspace_bytes(p) exceeds
+ * SSD_NOALLOC_SCRATCH_BYTES, else what ssd_forward returns. */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int ssd_forward_noalloc(const ssd_problem* p, const void* X, const float* logA, const void* B,
+                        const void* C, const float* init_state, const int32_t* seq_offsets,
+                        void* Y, float* final_state, void* hip_stream);
 
 #define SSD_ABI_VERSION 1
 

@@ -25,7 +25,8 @@ __all__ = [
     "SSD_DTYPE_F32", "SSD_DTYPE_BF16", "SsdProblem", "SsdError", "lib_path", "load_library",
     "ssd_check_problem", "ssd_workspace_bytes", "ssd_forward", "ssd_forward_stage",
     "ssd_decode_step", "ssd_backward_workspace_bytes", "ssd_backward", "ssd_status_string",
-    "ssd_abi_version", "ssd_plan_describe", "forward", "decode_step", "backward", "problem_for",
+    "ssd_abi_version", "ssd_plan_describe", "ssd_forward_noalloc", "SSD_NOALLOC_SCRATCH_BYTES",
+    "SSD_ERR_TOO_LARGE", "forward", "decode_step", "backward", "problem_for",
 ]
 
 SSD_OK = 0
@@ -33,6 +34,8 @@ SSD_ERR_INVALID_ARG = -1
 SSD_ERR_UNSUPPORTED = -2
 SSD_ERR_WORKSPACE = -3
 SSD_ERR_HIP = -4
+SSD_ERR_TOO_LARGE = -5
+SSD_NOALLOC_SCRATCH_BYTES = 64 << 20
 SSD_DTYPE_F32 = 0
 SSD_DTYPE_BF16 = 1
 ABI_VERSION = 1
@@ -88,6 +91,8 @@ def load_library():
     lib.ssd_backward.restype = ctypes.c_int
     lib.ssd_status_string.argtypes = [ctypes.c_int]
     lib.ssd_status_string.restype = ctypes.c_char_p
+    lib.ssd_forward_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ssd_forward_noalloc.restype = ctypes.c_int
     lib.ssd_plan_describe.argtypes = [pp, ctypes.c_char_p, sz]
     lib.ssd_plan_describe.restype = ctypes.c_int
     lib.ssd_abi_version.argtypes = []
@@ -159,6 +164,15 @@ def ssd_forward(problem: SsdProblem, X, logA, B, C, init_state, seq_offsets, Y, 
     return int(load_library().ssd_forward(ctypes.byref(problem), X, logA, B, C, init_state,
                                           seq_offsets, Y, final_state, workspace,
                                           int(workspace_bytes), hip_stream))
+
+
+def ssd_forward_noalloc(problem: SsdProblem, X, logA, B, C, init_state, seq_offsets, Y, final_state,
+                        hip_stream) -> int:
+    """Direct call of the no-allocation entry point (its scratch is the library's own
+    per-device array of SSD_NOALLOC_SCRATCH_BYTES).  Pointer arguments are integers
+    (device addresses) or None; returns the ssd_status code."""
+    return int(load_library().ssd_forward_noalloc(ctypes.byref(problem), X, logA, B, C, init_state,
+                                                  seq_offsets, Y, final_state, hip_stream))
 
 
 def ssd_forward_stage(stage: int, problem: SsdProblem, X, logA, B, C, init_state, seq_offsets, Y,

@@ -6,6 +6,7 @@
 #include <cstdint>
 #include <cstring>
 #include <cstdio>
+#include <mutex>
 
 #include "ssd.h"
 #include "ssd_kernels.h"
@@ -397,6 +398,7 @@ const char* ssd_status_string(int status) {
         case SSD_ERR_UNSUPPORTED: return "unsupported problem (dtype, chunk_len, headdim or dstate)";
         case SSD_ERR_WORKSPACE: return "workspace too small";
         case SSD_ERR_HIP: return "HIP runtime error";
+        case SSD_ERR_TOO_LARGE: return "problem needs more scratch than the no-allocation entry point holds";
         default: return "unknown status";
     }
 }
@@ -670,6 +672,57 @@ int ssd_forward(const ssd_problem* p, const void* X, const float* logA, const vo
                 float* final_state, void* workspace, size_t workspace_bytes, void* hip_stream) {
     return run_forward(3, p, X, logA, B, C, init_state, seq_offsets, Y, final_state, workspace,
                        workspace_bytes, hip_stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The scratch of ssd_forward_noalloc: one array per device, loaded with the code object.
+// In host code its name is a host-side stand-in; only the address that
+// hipGetSymbolAddress returns on a device is a device address.
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_addr[kMaxDevices] = {};
+
+// the current device's scratch address, looked up on the first call on that device
+int scratch_for_current_device(hipStream_t stream, void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return SSD_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return SSD_ERR_UNSUPPORTED;
+    if (stream) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return SSD_ERR_HIP;
+        if (sdev != dev) return SSD_ERR_INVALID_ARG;
+    }
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_addr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SSD_ERR_HIP;
+        scratch_addr[dev] = ptr;
+    }
+    *out = scratch_addr[dev];
+    return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_forward_noalloc(const ssd_problem* p, const void* X, const float* logA, const void* B,
+                        const void* C, const float* init_state, const int32_t* seq_offsets,
+                        void* Y, float* final_state, void* hip_stream) {
+    Plan pl;
+    const int rc = make_plan(p, &pl);
+    if (rc != SSD_OK) return rc;
+    if (pl.ws_bytes > SSD_NOALLOC_SCRATCH_BYTES) return SSD_ERR_TOO_LARGE;
+    void* ws = nullptr;
+    const int src = scratch_for_current_device(static_cast<hipStream_t>(hip_stream), &ws);
+    if (src != SSD_OK) return src;
+    return run_forward(3, p, X, logA, B, C, init_state, seq_offsets, Y, final_state, ws,
+                       SSD_NOALLOC_SCRATCH_BYTES, hip_stream);
 }
 
 int ssd_decode_step(const ssd_problem* p, const void* x, const float* logA, const void* B,

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["ssd_abi_version", "ssd_backward", "ssd_backward_workspace_bytes",
-                                           "ssd_check_problem", "ssd_decode_step", "ssd_forward",
+                                           "ssd_check_problem", "ssd_decode_step", "ssd_forward", "ssd_forward_noalloc",
                                            "ssd_forward_stage", "ssd_plan_describe", "ssd_status_string",
                                            "ssd_workspace_bytes"])
 
@@ -279,3 +279,12 @@ def test_plan_describe_names_the_kernels():
     bad = ssd.problem_for(1, 256, 4, 64, 64, 3, 256, 1, bf16)     # heads not a multiple of groups
     with pytest.raises(ssd.SsdError):
         ssd.ssd_plan_describe(bad)
+
+
+def test_noalloc_rejects_a_problem_beyond_its_scratch_before_device_work():
+    # the size check comes before any HIP call, so fake addresses are never touched
+    prob = ssd.problem_for(4, 4096, 32, 64, 256, 1, 256, 4, ssd.SSD_DTYPE_BF16)
+    assert ssd.ssd_workspace_bytes(prob) > ssd.SSD_NOALLOC_SCRATCH_BYTES
+    rc = ssd.ssd_forward_noalloc(prob, 1 * GB, 2 * GB, 3 * GB, 4 * GB, None, None, 6 * GB, None, None)
+    assert rc == ssd.SSD_ERR_TOO_LARGE
+    assert "scratch" in ssd.ssd_status_string(rc)
