@@ -11,7 +11,6 @@
 #include "ssd.h"
 #include "ssd_kernels.h"
 #include "ssd_walk_split.h"
-#include "ssd_walk_quad.h"
 #include "ssd_walk_fused.h"
 #include "ssd_backward.h"
 
@@ -20,12 +19,6 @@ namespace {
 constexpr int kLdsMax = 160 * 1024;   // LDS per workgroup on gfx950
 constexpr int kWalkThreads = 512;
 constexpr int kComputeUnits = 256;     // MI355X: 8 XCDs x 32 CUs
-// the quad walker's 32-wide p sub-tiles per wavefront: 1 = two wavefronts per head, two
-// per SIMD (2 = one wavefront per head)
-#ifndef SSD_QUAD_PW
-#define SSD_QUAD_PW 1
-#endif
-constexpr int kQuadPW = SSD_QUAD_PW;
 
 typedef void (*walk_fn_t)(ssd::WalkArgs);
 
@@ -48,10 +41,6 @@ struct Plan {
     walk_fn_t walk_left;   // the second pass of a two-pass d_state (left factors only)
     void (*walk_pair)(ssd::WalkArgs, ssd::WalkArgs);   // both passes in one launch
     walk_fn_t summary;   // the segment-summary instance (nseg > 1)
-    int quad;         // heads per workgroup of the quad walker (3 or 4; 0: not used)
-    int quads;        // its workgroups per group
-    size_t xflag_off; // its per-(chunk, head) flags of very steep decay
-    size_t dx_off;    // its per-row decays to the end of the row's 32-row block
     int fused;        // compute waves per workgroup of the fused walker (0: not used)
     int fused_wpg;    // its workgroups per group
     int64_t fused_items;
@@ -184,14 +173,12 @@ bool plan_fused(const ssd_problem* p, Plan* pl) {
     return pl->fused_fn != nullptr;
 }
 
-int make_plan(const ssd_problem* p, Plan* pl, bool allow_quad = true, bool allow_fused = true) {
+int make_plan(const ssd_problem* p, Plan* pl, bool allow_fused = true) {
     const int rc = check_problem(p);
     if (rc != SSD_OK) return rc;
     pl->dtype = p->dtype;
-    pl->quad = 0;
-    pl->quads = 0;
     pl->fused = 0;
-    if (allow_quad && allow_fused && plan_fused(p, pl)) {
+    if (allow_fused && plan_fused(p, pl)) {
         pl->npass = 1;
         pl->nseg = 1;
         pl->ws_bytes = 256;   // (no workspace is used)
@@ -209,7 +196,7 @@ int make_plan(const ssd_problem* p, Plan* pl, bool allow_quad = true, bool allow
     if (p->dtype == SSD_DTYPE_BF16 && p->chunk_len == 256 && p->dstate == 256 && p->headdim % 64 == 0) {
         ssd_problem q = *p;
         q.dstate = 128;
-        const int qrc = make_plan(&q, pl, false);
+        const int qrc = make_plan(&q, pl, false);   // (the split walker's plan for each half)
         if (qrc != SSD_OK) return qrc;
         pl->npass = 2;
         pl->walk_left = ssd::ssd_walk_split_kernel<128, false, true>;
@@ -316,47 +303,6 @@ int make_plan(const ssd_problem* p, Plan* pl, bool allow_quad = true, bool allow
             pl->lds_bytes = ssd::SplitLds<128>::bytes;
             pl->summary_lds = ssd::SummaryLds<128>::bytes;
         }
-        // Head dimension 64 with several heads per group: three or four heads per
-        // workgroup share one load of the group's operands, when the workgroups of four
-        // heads fill at least half of the compute units without segmenting (the quad
-        // walker walks whole sequences).
-        const int64_t hpg = p->nheads / p->ngroups;
-        const int64_t qitems = p->nseq * p->ngroups * ((hpg + 3) / 4);
-        // Three heads per workgroup instead of four: more, smaller workgroups.  One of
-        // three heads walks a block in about 0.85 of the time of one of four (measured at
-        // d_state 128); it is taken when that shortens the estimated walk: the rounds of
-        // workgroups over the compute units for sequences of one length, the total work
-        // for packed sequences.
-        int hq = 4;
-        if (hpg >= 3) {
-            const int64_t it3 = p->nseq * p->ngroups * ((hpg + 2) / 3);
-            const int64_t cost4 = p->nseq == p->batch ? 100 * ((qitems + kComputeUnits - 1) / kComputeUnits) : 100 * qitems;
-            const int64_t cost3 = p->nseq == p->batch ? 85 * ((it3 + kComputeUnits - 1) / kComputeUnits) : 85 * it3;
-            if (cost3 < cost4) hq = 3;
-        }
-        const int64_t nq = (hpg + hq - 1) / hq;
-        // (its loads address the workspace from the C B^T tiles to the end of the C
-        // fragments, and the cumsum, with 32-bit offsets)
-        const bool small_ws = pl->seg_off - pl->cb_off < ((size_t)1 << 31) && pl->ws_bytes + cs_bytes < ((size_t)1 << 31);
-        // (its prep writes each block's B^T, C and diagonal C B^T fragments together, over
-        // the C B^T, B^T and C arrays: [nslots, G, 8, N/8 + 2 KB])
-        const bool fits = (size_t)pl->nslots * p->ngroups * 8 * (N / 8 + 2) * 1024 <= pl->seg_off - pl->cb_off;
-        if (allow_quad && P == 64 && hpg >= 2 && qitems >= kComputeUnits / 2 && small_ws && fits) {
-            pl->quad = hq;
-            pl->quads = (int)nq;
-            pl->nitems = p->nseq * p->ngroups * nq;
-            pl->nseg = 1;
-            pl->nsplit = 1;
-            pl->ntail = 0;
-            if (hq == 3)
-                pl->walk = N == 64 ? ssd::ssd_walk_quad_kernel<64, kQuadPW, 3> : ssd::ssd_walk_quad_kernel<128, kQuadPW, 3>;
-            else
-                pl->walk = N == 64 ? ssd::ssd_walk_quad_kernel<64, kQuadPW, 4> : ssd::ssd_walk_quad_kernel<128, kQuadPW, 4>;
-            pl->xflag_off = pl->ws_bytes;
-            pl->dx_off = align_up(pl->xflag_off + (size_t)pl->nslots * p->nheads * sizeof(int), 256);
-            pl->ws_bytes = align_up(pl->dx_off + cs_bytes, 256);
-            pl->lds_bytes = 0;   // static LDS
-        }
     }
     return SSD_OK;
 }
@@ -422,8 +368,6 @@ int ssd_plan_describe(const ssd_problem* p, char* buf, size_t len) {
     if (pl.fused) {
         snprintf(walk, sizeof walk, "ssd_walk_fused_kernel<%d, %d>", (int)p->dstate, pl.fused);
         prep = "none";
-    } else if (pl.quad) {
-        snprintf(walk, sizeof walk, "ssd_walk_quad_kernel<%d, 1, %d>", (int)p->dstate, pl.quad);
     } else if (pl.npass == 2) {
         snprintf(walk, sizeof walk, "ssd_walk_split_pair_kernel<128>+ssd_add_kernel<bf16>");
     } else if (pl.split) {
@@ -454,8 +398,7 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
                 float* final_state, void* workspace, size_t workspace_bytes, void* hip_stream,
                 int64_t x_heads = 0) {
     Plan pl;
-    // (the fused walker reads one X row per head)
-    int rc = make_plan(p, &pl, true, x_heads == 0 || x_heads == p->nheads);
+    int rc = make_plan(p, &pl);
     if (rc != SSD_OK) return rc;
     if (!X || !logA || !B || !C || !Y || !workspace) return SSD_ERR_INVALID_ARG;
     if (seq_offsets) {
@@ -505,6 +448,7 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
         fa.P = (int)P;
         fa.N = (int)N;
         fa.G = (int)G;
+        fa.xh = (int)x_heads;
         fa.nseq = (int)p->nseq;
         fa.upg = (int)((H / G) * (P / 32));
         fa.wpg = pl.fused_wpg;
@@ -519,8 +463,7 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
     walk_fn walk = pl.walk;
     prep_fn prep = p->dtype == SSD_DTYPE_BF16 ? ssd::ssd_prep_kernel<__bf16>
                                               : ssd::ssd_prep_kernel<float>;
-    // (the quad walker's LDS is static: no dynamic LDS to allow)
-    rc = pl.quad ? SSD_OK : ensure_lds_limit(reinterpret_cast<const void*>(walk));
+    rc = ensure_lds_limit(reinterpret_cast<const void*>(walk));
     if (rc != SSD_OK) return rc;
     if (pl.npass == 2) {
         rc = ensure_lds_limit(reinterpret_cast<const void*>(pl.walk_left));
@@ -571,12 +514,6 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
         // one prep serves both passes: it walks every column for the tiles anyway
         pa.bt2 = (pl.npass == 2 && k == 0) ? static_cast<unsigned char*>(workspace) + pl.pass_ws + pl.bt_off : nullptr;
         pa.ct2 = (pl.npass == 2 && k == 0) ? static_cast<unsigned char*>(workspace) + pl.pass_ws + pl.ct_off : nullptr;
-        // the quad walker takes C in its accumulator-row K order and only diagonal tiles
-        pa.ct_perm = pl.quad != 0;
-        pa.cb_diag = pl.quad != 0;
-        pa.qlay = pl.quad != 0;
-        pa.xflag = pl.quad ? reinterpret_cast<int*>(static_cast<unsigned char*>(workspace) + pl.xflag_off) : nullptr;
-        pa.dx = pl.quad ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + pl.dx_off) : nullptr;
 
         ssd::WalkArgs& wa = *pwa;
         wa.X = X;
@@ -618,9 +555,6 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
         wa.lpt = (pl.split && seq_offsets && p->nseq <= 64 && (p->nseq * G) % 8 == 0) ? 1 : 0;
         wa.seg_state = reinterpret_cast<float*>(ws + pl.seg_off);
         wa.seg_decay = reinterpret_cast<float*>(ws + pl.segd_off);
-        wa.quads = pl.quads;
-        wa.xflag = pa.xflag;
-        wa.dx = pa.dx;
     };
     const int64_t prep_blocks = nslots * ((H + ssd::kPrepHeads - 1) / ssd::kPrepHeads) + nslots * G;
     if (prep_blocks > INT32_MAX) return SSD_ERR_UNSUPPORTED;
@@ -648,7 +582,7 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
                                    stream, wa);
             }
             wa.nitems = wa.nwhole + wa.ntail * nseg;
-            hipLaunchKernelGGL(k == 0 ? walk : pl.walk_left, dim3((unsigned)wa.nitems), dim3(pl.quad ? 128 * pl.quad / kQuadPW : kWalkThreads),
+            hipLaunchKernelGGL(k == 0 ? walk : pl.walk_left, dim3((unsigned)wa.nitems), dim3(kWalkThreads),
                                pl.lds_bytes, stream, wa);
         }
     }

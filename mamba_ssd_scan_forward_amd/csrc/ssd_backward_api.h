@@ -24,14 +24,9 @@ int make_bwd_plan(const ssd_problem* p, BwdPlan* bp) {
     bp->p2.ngroups = p->nheads;
     rc = check_problem(&bp->p2);
     if (rc != SSD_OK) return rc;
-    // (the dB and dC passes read X per group: sized for the plans with and without the
-    // fused walker, which reads it per head)
-    Plan a, b, c;
-    if (make_plan(&bp->p1, &a) != SSD_OK || make_plan(&bp->p2, &b) != SSD_OK ||
-        make_plan(&bp->p2, &c, true, false) != SSD_OK)
-        return SSD_ERR_UNSUPPORTED;
+    Plan a, b;
+    if (make_plan(&bp->p1, &a) != SSD_OK || make_plan(&bp->p2, &b) != SSD_OK) return SSD_ERR_UNSUPPORTED;
     bp->fws_bytes = a.ws_bytes > b.ws_bytes ? a.ws_bytes : b.ws_bytes;
-    if (c.ws_bytes > bp->fws_bytes) bp->fws_bytes = c.ws_bytes;
     const size_t es = p->dtype == SSD_DTYPE_BF16 ? 2 : 4;
     const size_t rows = (size_t)(p->batch * p->seqlen), H = (size_t)p->nheads, P = (size_t)p->headdim,
                  N = (size_t)p->dstate, G = (size_t)p->ngroups, ns = (size_t)p->nseq;

@@ -53,15 +53,6 @@ struct PrepArgs {
                       // order, [nslots, G, N/32, 8, 2, 64 lanes, 8], and
     void* ct;         // C in MFMA B-operand fragment order, [nslots, G, 8, N/16, 64 lanes,
                       // 8]; written by the C B^T role (bf16 only)
-    int ct_perm;      // C fragments in the K order of a 32 x 32 accumulator's rows (below)
-    int cb_diag;      // compute and store only the diagonal tiles (i, i)
-    int qlay;         // (with ct_perm and cb_diag) each 32-row block's fragments together
-                      // in the cb array instead: [nslots, G, 8, N/16 + N/16 + 2, 64 lanes, 8]
-                      // (B^T fragments (n tile, K-step), C fragments, the diagonal tile's two
-                      // K-steps), so that a block's shared operands are one run of memory
-    int* xflag;       // optional: [nslots, H], whether the chunk has a 32-row block whose
-                      // cumsum falls by more than 100 (log2 units) from its first row to its last
-    float* dx;        // optional: [nslots, H, Qp], 2^(cs[last row of the row's 32-row block] - cs[row])
 };
 
 struct WalkArgs {
@@ -84,9 +75,6 @@ struct WalkArgs {
     int lpt;            // packed sequences: (sequence, group) units dealt to XCDs longest first
     int xh;             // X rows per token: H (one per head), or fewer, shared by H / xh heads
     int ldn, ns0;       // init / final state rows hold ldn values; this call's are [ns0, ns0 + N)
-    int quads;          // quad walker: workgroups (quads of heads) per group
-    const int* xflag;   // quad walker: [nslots, H] chunks with a block of very steep decay
-    const float* dx;    // quad walker: [nslots, H, 256] decay of each row to its 32-row block's end
     int64_t T;
     int H, P, N, G, Q, Qp, ntile, nseq, ptiles, nitems, qb;
     int cb_lds;                                    // stage off-diagonal C B^T tiles in LDS
@@ -222,21 +210,6 @@ __global__ void __launch_bounds__(kPrepThreads, 2) ssd_prep_kernel(PrepArgs a) {
             const f32x4 o = {(excl + v[0]) * kLog2e, (excl + v[1]) * kLog2e, (excl + v[2]) * kLog2e,
                              (excl + v[3]) * kLog2e};
             if (4 * lane < a.Qp) *reinterpret_cast<f32x4*>(a.cs + ((int64_t)k * a.H + h0 + hh) * a.Qp + 4 * lane) = o;
-            if (a.dx) {
-                // the decay of each row to the end of its 32-row block (lane 8 j + 7 holds
-                // that row of block j)
-                const float eb = __shfl(o[3], (lane & ~7) + 7, 64);
-                const f32x4 d = {fast_exp2(eb - o[0]), fast_exp2(eb - o[1]), fast_exp2(eb - o[2]), fast_exp2(eb - o[3])};
-                if (4 * lane < a.Qp) *reinterpret_cast<f32x4*>(a.dx + ((int64_t)k * a.H + h0 + hh) * a.Qp + 4 * lane) = d;
-            }
-            if (a.xflag) {
-                // block j's rows are lanes 8 j .. 8 j + 7: first row o[0] of lane 8 j, last
-                // row o[3] of lane 8 j + 7 (the same stored values the walker compares)
-                const float last = __shfl(o[3], (lane & ~7) + 7, 64);
-                const bool steep = (lane & 7) == 0 && 4 * lane < a.Qp && o[0] - last > 100.f;
-                const int any = __ballot(steep) != 0;   // (every lane votes)
-                if (lane == 0) a.xflag[(int64_t)k * a.H + h0 + hh] = any;
-            }
         }
         return;
     }
@@ -261,12 +234,6 @@ __global__ void __launch_bounds__(kPrepThreads, 2) ssd_prep_kernel(PrepArgs a) {
     int ti[MAXT], tj[MAXT], tt[MAXT];
 #pragma unroll
     for (int u = 0; u < MAXT; ++u) {
-        if (a.cb_diag) {
-            // diagonal tiles only: wavefront w takes tile (w, w), slot w (w + 3) / 2
-            ti[u] = tj[u] = wave;
-            tt[u] = u == 0 ? wave * (wave + 3) / 2 : a.ntile;
-            continue;
-        }
         const int t = wave + kPrepWaves * u;
         int i = 0;
         while ((i + 1) * (i + 2) / 2 <= t) ++i;
@@ -331,27 +298,13 @@ __global__ void __launch_bounds__(kPrepThreads, 2) ssd_prep_kernel(PrepArgs a) {
                     const int nt = nf / 32;
                     T* bto = static_cast<T*>(second ? a.bt2 : a.bt) + (int64_t)(k * a.G + g) * (a.N / 32) * 16 * 512;
                     T* cto = static_cast<T*>(second ? a.ct2 : a.ct) + (int64_t)(k * a.G + g) * 8 * (a.N / 16) * 512;
-                    T* qo = static_cast<T*>(a.cb) + ((int64_t)(k * a.G + g) * 8 + j) * (a.N / 8 + 2) * 512;
                     frag v;
 #pragma unroll
                     for (int q = 0; q < 8; ++q)
                         v[q] = Bs[(32 * j + 16 * ks + 8 * (ln >> 5) + q) * SS + 32 * sub + (ln & 31)];
-                    *reinterpret_cast<frag*>((a.qlay ? qo + (2 * nt + ks) * 512 : bto + ((nt * 8 + j) * 2 + ks) * 512) + ln * 8) = v;
-                    frag w;
-                    if (a.ct_perm) {
-                        // element q of lane (lr, lg) is column 16 ks + 8 (q / 4) + 4 lg + q % 4:
-                        // the order in which a lane holds the rows of a 32 x 32 accumulator
-                        // (rows 8 (e / 4) + 4 lg + e % 4), so that an accumulator converts to
-                        // an A operand without moving data between lanes
-                        const T* cr = Cs + (32 * j + (ln & 31)) * SS + 32 * sub + 16 * ks + 4 * (ln >> 5);
-                        const bf16x4 lo = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(cr));
-                        const bf16x4 hi = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(cr + 8));
-                        w = frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    } else {
-                        w = E::lds8(Cs + (32 * j + (ln & 31)) * SS + 32 * sub + 16 * ks + 8 * (ln >> 5));
-                    }
-                    *reinterpret_cast<frag*>((a.qlay ? qo + (a.N / 16 + nf / 16 + ks) * 512 : cto + (j * (a.N / 16) + nf / 16 + ks) * 512) +
-                                             ln * 8) = w;
+                    *reinterpret_cast<frag*>(bto + ((nt * 8 + j) * 2 + ks) * 512 + ln * 8) = v;
+                    const frag w = E::lds8(Cs + (32 * j + (ln & 31)) * SS + 32 * sub + 16 * ks + 8 * (ln >> 5));
+                    *reinterpret_cast<frag*>(cto + (j * (a.N / 16) + nf / 16 + ks) * 512 + ln * 8) = w;
                 }
             }
         }
@@ -372,8 +325,7 @@ __global__ void __launch_bounds__(kPrepThreads, 2) ssd_prep_kernel(PrepArgs a) {
     for (int u = 0; u < MAXT; ++u) {
         const int t = tt[u];
         if (t >= a.ntile) break;
-        T* out = a.qlay ? static_cast<T*>(a.cb) + (((int64_t)(k * a.G + g) * 8 + ti[u]) * (a.N / 8 + 2) + a.N / 8) * 512
-                        : static_cast<T*>(a.cb) + ((int64_t)(k * a.G + g) * a.ntile + t) * 1024;
+        T* out = static_cast<T*>(a.cb) + ((int64_t)(k * a.G + g) * a.ntile + t) * 1024;
         if (ti[u] == tj[u]) {
             // diagonal tiles carry the causal mask: (C B^T)_{ls} = 0 for s > l
 #pragma unroll

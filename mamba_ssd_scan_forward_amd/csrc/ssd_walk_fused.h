@@ -62,6 +62,7 @@ struct FusedArgs {
     float* final_state;
     int64_t T;      // tokens per sequence (without seq_offsets)
     int H, P, N, G, nseq;
+    int xh;         // X rows per token: H (one per head), or fewer, each shared by a run of H / xh heads
     int upg;        // 32-column units per group: (H / G) (P / 32)
     int wpg;        // workgroups per group: ceil(upg / NW)
     int nitems;     // nseq G wpg
@@ -248,14 +249,16 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
         // ------------------------------------------------------------ X loader: every unit's
         // X rows and the heads' logA; per head the block's cumsum, the row factors w and r,
         // the renormalisation factor and the path flag
-        const rsrc_t xr = make_rsrc(a.X + row0 * xrow, (uint32_t)((int64_t)len * xrow * 2));
+        const int64_t xrx = (int64_t)a.xh * P;   // elements per token row of X
+        const int hrep = H / a.xh;
+        const rsrc_t xr = make_rsrc(a.X + row0 * xrx, (uint32_t)((int64_t)len * xrx * 2));
         const rsrc_t lar = make_rsrc(a.logA + row0 * H, (uint32_t)((int64_t)len * H * 4));
         uint32_t xl[NW];
 #pragma unroll
         for (int k = 0; k < NW; ++k) {
             const int u = min(u0 + k, a.upg - 1);
             const int h = g * hpg + u / uph, c0 = 32 * (u % uph);
-            xl[k] = (uint32_t)(((lane >> 2) * xrow + (int64_t)h * P + c0 + 8 * (lane & 3)) * 2);
+            xl[k] = (uint32_t)(((lane >> 2) * xrx + (int64_t)(h / hrep) * P + c0 + 8 * (lane & 3)) * 2);
         }
         // logA: lanes 0..31 head 2 p, lanes 32..63 head 2 p + 1 (clamped to the group)
         uint32_t ll[NPAIR];
@@ -264,7 +267,7 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
             const int hl = min(hfirst + 2 * p + lg, hpg - 1);
             ll[p] = (uint32_t)((lr * H + g * hpg + hl) * 4);
         }
-        const uint32_t rs16 = (uint32_t)(16 * xrow * 2), rb32 = (uint32_t)(32 * xrow * 2), lab32 = (uint32_t)(32 * H * 4);
+        const uint32_t rs16 = (uint32_t)(16 * xrx * 2), rb32 = (uint32_t)(32 * xrx * 2), lab32 = (uint32_t)(32 * H * 4);
         auto issue = [&](int b, auto kc) __attribute__((always_inline)) {
             constexpr int k = decltype(kc)::value;
             b = min(b, nb - 1);

@@ -56,10 +56,20 @@ def rel_err(out, ref):
     return float(np.max(np.abs(out - ref))) / max(den, 1e-30)
 
 
+def plan_of(inp, Q):
+    """The kernels the library plans for this input (host logic, no device work)."""
+    import mamba_ssd_scan_forward_amd as ssd
+    b, T, H, P = inp.X.shape
+    G, N = inp.B.shape[2], inp.B.shape[3]
+    nseq = b if inp.seq_offsets is None else len(inp.seq_offsets) - 1
+    dt = ssd.SSD_DTYPE_BF16 if inp.dtype == "bf16" else ssd.SSD_DTYPE_F32
+    return ssd.ssd_plan_describe(ssd.problem_for(b, T, H, P, N, G, Q, nseq, dt))
+
+
 def check(inp, Q, label=""):
     print(f"[parity] {label} X{tuple(inp.X.shape)} G={inp.B.shape[2]} N={inp.B.shape[3]} "
-          f"Q={Q} {inp.dtype} init={inp.init is not None} varlen={inp.seq_offsets is not None}",
-          flush=True)
+          f"Q={Q} {inp.dtype} init={inp.init is not None} varlen={inp.seq_offsets is not None} "
+          f"walk={plan_of(inp, Q)['walk']}", flush=True)
     Y, F = run_gpu(inp, Q)
     Yr, Fr = oracle.recurrence(inp.X, inp.logA, inp.B, inp.C, inp.init, inp.seq_offsets)
     ey, ef = rel_err(Y, Yr), rel_err(F, Fr)
@@ -268,19 +278,16 @@ def test_full_size_config(name):
     assert ey <= TOL[w.dtype] and ef <= TOL[w.dtype], (ey, ef)
 
 
-# Shapes that fill at least half of the chip with (sequence, group, quad of heads)
-# workgroups, so the library walks them three or four heads per workgroup (three where
-# the extra workgroups still fit one round over the compute units or cost less in all,
-# four otherwise): ragged chunks with an initial state (three, the last workgroup of the
-# group with one head); d_state 64 with groups of five heads (three, a workgroup of two);
-# d_state 64 with groups of 14 heads (four, a workgroup of two); a packed batch with empty
-# and length-1 sequences (four, longest-first dealing); the same with groups of three
-# heads (three); groups of two heads (four, two of them shadowing); strong decay, where
-# most 32-row blocks take the exact-mask path, with three and with four heads per
-# workgroup.
+# Shapes whose (sequence, group, NW units of 32 head columns) workgroups fill at least
+# half of the chip, so the library walks them on the fused walker with the heads of a
+# group sharing one load of B and C: ragged chunks with an initial state; d_state 64 with
+# groups of five heads and of 14 heads (a group's last workgroup partly idle); a packed
+# batch with empty and length-1 sequences (longest-first dealing); the same with groups of
+# three heads; groups of two heads; strong decay, where most 32-row blocks take the
+# exact-mask path, at two head counts.
 @pytest.mark.parametrize("case", ["ragged_init", "state64_partial", "state64_four", "packed", "packed_three",
                                   "two_per_group", "strong_decay", "strong_decay_four"])
-def test_quad_walker(case):
+def test_group_shared_walker(case):
     if case == "ragged_init":
         inp = make_inputs(32, 300, 16, 64, 128, 1, "bf16", seed=1300, init_state=True)
     elif case == "state64_partial":
@@ -301,4 +308,5 @@ def test_quad_walker(case):
     else:
         inp = make_inputs(64, 300, 14, 64, 128, 1, "bf16", seed=1305, init_state=True)
         inp.logA = (inp.logA * 40.0).astype(np.float32)
+    assert plan_of(inp, 256)["walk"].startswith("ssd_walk_fused_kernel"), plan_of(inp, 256)
     check(inp, 256, case)
