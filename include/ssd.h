@@ -107,7 +107,8 @@ size_t ssd_workspace_bytes(const ssd_problem* p);
  *   final_state  [nseq, H, P, N]   float32 (out)  state after the last token, or NULL to skip
  *   workspace    >= ssd_workspace_bytes(p) bytes of device scratch, 256-byte aligned
  *   hip_stream   hipStream_t to enqueue on (NULL = the default stream)
- * Y and final_state must not overlap any input or each other.
+ * Y and final_state must not overlap any input or each other; the workspace (written by
+ * the call) must overlap no input and no output.
  * Returns SSD_OK or an ssd_status error code (see the enum). */
 int ssd_forward(const ssd_problem* p, const void* X, const float* logA, const void* B,
                 const void* C, const float* init_state, const int32_t* seq_offsets, void* Y,
@@ -169,7 +170,8 @@ size_t ssd_backward_workspace_bytes(const ssd_problem* p);
  *   dinit        [nseq, H, P, N]  float32 (out)  or NULL to skip (defined with or
  *                                                without init_state)
  *   workspace    >= ssd_backward_workspace_bytes(p) bytes, 256-byte aligned
- * The outputs must not overlap any input, the workspace or each other.  Supported
+ * The outputs must not overlap any input, the workspace or each other, and the workspace
+ * overlaps no input.  Supported
  * problems: those of ssd_forward whose transposed problem (head dimension and state
  * size swapped) is supported too.  Returns SSD_OK or an ssd_status error code. */
 int ssd_backward(const ssd_problem* p, const void* X, const float* logA, const void* B, const void* C,

@@ -45,5 +45,28 @@ def compile_one(src: str, lib: str, verbose: bool = False) -> str:
     return lib
 
 
+HOST_CHECK_SRC = os.path.join(HERE, "csrc", "host_check.cpp")
+HOST_CHECK = os.path.join(HERE, "_build", "host_check")
+# host code under AddressSanitizer and UndefinedBehaviorSanitizer (each -fsanitize= for the
+# host pass only: the device code is built as usual and never run by the check)
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g", "-O1"]
+
+
+def build_host_check(verbose: bool = False) -> str:
+    """The host-code check: ssd_api.hip and host_check.cpp linked into one program."""
+    os.makedirs(os.path.dirname(HOST_CHECK), exist_ok=True)
+    flags = [f for f in FLAGS if f not in ("-shared", "-fPIC", "-O3")]
+    tmp = HOST_CHECK + ".tmp"
+    cmd = [HIPCC] + flags + SANITIZE + [SRC, HOST_CHECK_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}{res.stderr}")
+    os.replace(tmp, HOST_CHECK)
+    return HOST_CHECK
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -57,7 +57,9 @@ int check_problem(const ssd_problem* p) {
     if (p->nheads % p->ngroups != 0) return SSD_ERR_INVALID_ARG;
     if (p->nseq < 1) return SSD_ERR_INVALID_ARG;
     // int32 indexing limits of the kernels (token rows, element offsets use int64)
-    if (p->batch * p->seqlen > (int64_t)1 << 30 || p->nheads > (1 << 20) || p->nseq > (1 << 24))
+    // (each factor is bounded before the product, which then cannot overflow)
+    if (p->batch > (int64_t)1 << 30 || p->seqlen > (int64_t)1 << 30 || p->batch * p->seqlen > (int64_t)1 << 30 ||
+        p->nheads > (1 << 20) || p->nseq > (1 << 24))
         return SSD_ERR_UNSUPPORTED;
     if (p->dtype != SSD_DTYPE_F32 && p->dtype != SSD_DTYPE_BF16) return SSD_ERR_UNSUPPORTED;
     const int64_t Q = p->chunk_len;
@@ -375,7 +377,11 @@ int ssd_plan_describe(const ssd_problem* p, char* buf, size_t len) {
         if (pl.nseg > 1) summary = p->dstate == 64 ? "ssd_walk_split_kernel<64, true, false>"
                                                     : "ssd_walk_split_kernel<128, true, false>";
     } else {
-        snprintf(walk, sizeof walk, "ssd_walk_kernel");
+        // the general walker: element type, P tile, padded d_state, C B^T tiles in LDS, and
+        // the rows of B staged at once (fewer than the padded chunk: B goes in stages)
+        snprintf(walk, sizeof walk, "ssd_walk_kernel<%s, %d, %d, %s> qb=%d/%d",
+                 p->dtype == SSD_DTYPE_BF16 ? "bf16" : "float", pl.PT, pl.NP, pl.cb_lds ? "true" : "false", pl.qb,
+                 pl.Qp);
     }
     snprintf(buf, len, "walk=%s;prep=%s;summary=%s", walk, prep, summary);
     return SSD_OK;
@@ -428,6 +434,9 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
         if (final_state && overlap(final_state, ns, ins[i], nin[i])) return SSD_ERR_INVALID_ARG;
     }
     if (final_state && overlap(Y, nx, final_state, ns)) return SSD_ERR_INVALID_ARG;
+    // the workspace is written too (by the prep, read back by the walk): it overlaps no input
+    for (int i = 0; i < 6; ++i)
+        if (overlap(workspace, workspace_bytes, ins[i], nin[i])) return SSD_ERR_INVALID_ARG;
     if (workspace_bytes < pl.ws_bytes) return SSD_ERR_WORKSPACE;
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
@@ -669,7 +678,8 @@ int ssd_decode_step(const ssd_problem* p, const void* x, const float* logA, cons
     if (p->dtype != SSD_DTYPE_F32 && p->dtype != SSD_DTYPE_BF16) return SSD_ERR_UNSUPPORTED;
     if (p->headdim % 16 != 0 || p->headdim > 256 || p->dstate % 16 != 0 || p->dstate > 256)
         return SSD_ERR_UNSUPPORTED;
-    if (p->batch * p->nheads > INT32_MAX) return SSD_ERR_UNSUPPORTED;
+    // (each factor is bounded before the product, which then cannot overflow)
+    if (p->batch > INT32_MAX || p->nheads > INT32_MAX || p->batch * p->nheads > INT32_MAX) return SSD_ERR_UNSUPPORTED;
     if (!x || !logA || !B || !C || !state || !y) return SSD_ERR_INVALID_ARG;
     const void* ptrs[] = {x, logA, B, C, state, y};
     for (const void* q : ptrs)

@@ -104,6 +104,9 @@ int ssd_backward(const ssd_problem* p, const void* X, const float* logA, const v
         for (int j = i + 1; j < 5; ++j)
             if (overlap(outs[i], nout[i], outs[j], nout[j])) return SSD_ERR_INVALID_ARG;
     }
+    // the workspace is written too: it overlaps no input
+    for (int j = 0; j < 10; ++j)
+        if (overlap(workspace, workspace_bytes, ins[j], nin[j])) return SSD_ERR_INVALID_ARG;
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     unsigned char* ws = static_cast<unsigned char*>(workspace);

@@ -359,22 +359,30 @@ __global__ void __launch_bounds__(256) ssd_add_kernel(T* y, const T* z, int64_t 
 // One recurrent step of every (sequence, head): h <- a h + x B^T, y = h C (page "Transformers
 // are SSMs" paper summary, section 2.4 with A_t = a_t I; the recurrent mode of section 3,
 // one token at a time from a state the forward pass returned).  One 256-thread workgroup
-// per (sequence, head) streams the P x N state once: each thread owns 4 consecutive
-// state entries of a row per pass, the N/4 threads of a row reduce y[p] with lane
-// shuffles.  The state goes from HBM to registers and back, nothing is staged.
+// per (sequence, head) streams the P x N state once: each of the first N/4 threads of a
+// row owns 4 consecutive state entries of that row per pass, and a row's threads (N/4
+// rounded up to a power of two, so that a row is a run of lanes inside one wavefront and
+// the rows of a pass tile the workgroup exactly) reduce y[p] with lane shuffles.  The
+// state goes from HBM to registers and back, nothing is staged.
 template <typename T>
 __global__ void __launch_bounds__(256) ssd_decode_kernel(DecodeArgs a) {
     using E = Elem<T>;
     const int bh = blockIdx.x;
     const int b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
     const int tid = threadIdx.x;
-    const int tpr = a.N / 4;                 // threads per state row (4 .. 64)
+    const int nq = a.N / 4;                  // threads of a row that hold state (4 .. 64)
+    int tpr = 4;                             // threads per state row: nq rounded up to a
+    while (tpr < nq) tpr <<= 1;              // power of two (4 .. 64)
     const int rpp = 256 / tpr;               // rows per pass
     const int j = tid % tpr, rsub = tid / tpr;
-    const T* Bv = static_cast<const T*>(a.B) + ((int64_t)b * a.G + g) * a.N + 4 * j;
-    const T* Cv = static_cast<const T*>(a.C) + ((int64_t)b * a.G + g) * a.N + 4 * j;
-    const float b0 = E::to_f(Bv[0]), b1 = E::to_f(Bv[1]), b2 = E::to_f(Bv[2]), b3 = E::to_f(Bv[3]);
-    const float c0 = E::to_f(Cv[0]), c1 = E::to_f(Cv[1]), c2 = E::to_f(Cv[2]), c3 = E::to_f(Cv[3]);
+    const bool holds = j < nq;
+    float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f, c0 = 0.f, c1 = 0.f, c2 = 0.f, c3 = 0.f;
+    if (holds) {
+        const T* Bv = static_cast<const T*>(a.B) + ((int64_t)b * a.G + g) * a.N + 4 * j;
+        const T* Cv = static_cast<const T*>(a.C) + ((int64_t)b * a.G + g) * a.N + 4 * j;
+        b0 = E::to_f(Bv[0]), b1 = E::to_f(Bv[1]), b2 = E::to_f(Bv[2]), b3 = E::to_f(Bv[3]);
+        c0 = E::to_f(Cv[0]), c1 = E::to_f(Cv[1]), c2 = E::to_f(Cv[2]), c3 = E::to_f(Cv[3]);
+    }
     const float da = fast_exp2(a.logA[(int64_t)b * a.H + h] * kLog2e);
     const T* xv = static_cast<const T*>(a.x) + ((int64_t)b * a.H + h) * a.P;
     T* yv = static_cast<T*>(a.y) + ((int64_t)b * a.H + h) * a.P;
@@ -382,7 +390,7 @@ __global__ void __launch_bounds__(256) ssd_decode_kernel(DecodeArgs a) {
     for (int p0 = 0; p0 < a.P; p0 += rpp) {
         const int p = p0 + rsub;
         float part = 0.f;
-        if (p < a.P) {
+        if (p < a.P && holds) {
             f32x4* s4 = reinterpret_cast<f32x4*>(st + (int64_t)p * a.N + 4 * j);
             const float xp = E::to_f(xv[p]);
             f32x4 v = *s4;

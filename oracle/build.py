@@ -21,5 +21,22 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+CHECK_SRC = os.path.join(HERE, "sanitize_check.c")
+CHECK = os.path.join(HERE, "_build", "sanitize_check")
+
+
+def build_sanitize_check(verbose: bool = False) -> str:
+    """The oracle under AddressSanitizer and UndefinedBehaviorSanitizer, driven by
+    sanitize_check.c."""
+    os.makedirs(os.path.dirname(CHECK), exist_ok=True)
+    cmd = ["gcc", "-O1", "-g", "-fopenmp", "-std=c11", "-Wall", "-Wextra", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", SRC, CHECK_SRC, "-o", CHECK + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(CHECK + ".tmp", CHECK)
+    return CHECK
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -59,7 +59,7 @@ def test_probe_rejects_bad_arguments():
 
 def test_abi_and_status_strings():
     assert ssd.ssd_abi_version() == ssd.ABI_VERSION
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert ssd.ssd_status_string(code)
     assert ssd.ssd_status_string(12345) == "unknown status"
 
@@ -145,6 +145,18 @@ def test_forward_rejects_nseq_mismatch_without_offsets():
                                      ("final", "Y")])
 def test_forward_rejects_aliased_outputs(out, inp):
     assert call(prob(), off=None, **{out: ADDR[inp]}) == ssd.SSD_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("inp", ["X", "logA", "B", "C", "init", "off"])
+def test_forward_rejects_workspace_overlapping_an_input(inp):
+    # the workspace starts at the input's first byte, or 256 bytes into it (seq_offsets
+    # holds only 8 bytes here: its first byte only)
+    p = prob(batch=1, nseq=1) if inp == "off" else prob()
+    for shift in ((0,) if inp == "off" else (0, 256)):
+        over = {"ws": ADDR[inp] + shift}
+        if inp != "off":
+            over["off"] = None
+        assert call(p, **over) == ssd.SSD_ERR_INVALID_ARG, (inp, shift)
 
 
 def test_forward_rejects_small_workspace():
@@ -251,6 +263,11 @@ def test_backward_needs_final_state_with_dfinal():
 @pytest.mark.parametrize("out,inp", [("dX", "X"), ("dB", "dY"), ("dinit", "init"), ("dC", "bws"), ("dB", "dC")])
 def test_backward_rejects_aliased_outputs(out, inp):
     assert bcall(prob(), off=None, **{out: BADDR[inp]}) == ssd.SSD_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("inp", ["X", "logA", "B", "C", "init", "Yf", "final", "dY", "dF"])
+def test_backward_rejects_workspace_overlapping_an_input(inp):
+    assert bcall(prob(), off=None, bws=BADDR[inp]) == ssd.SSD_ERR_INVALID_ARG
 
 
 def test_backward_rejects_small_workspace_and_misalignment():

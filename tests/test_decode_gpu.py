@@ -54,6 +54,11 @@ def run_step(x, logA, B, C, S, dtype):
     (2, 4, 16, 16, 2, "f32"),
     (2, 6, 48, 256, 3, "f32"),
     (1, 2, 256, 32, 1, "bf16"),
+    # d_state not a power of two: a row's threads are rounded up to one
+    (3, 4, 64, 48, 2, "bf16"),
+    (2, 4, 80, 80, 1, "f32"),
+    (2, 3, 32, 144, 3, "bf16"),
+    (1, 2, 48, 240, 1, "f32"),
 ])
 def test_decode_step_matches_oracle(b, H, P, N, G, dtype):
     x, logA, B, C, S = step_inputs(b, H, P, N, G, dtype, seed=b * 1000 + H + P + N)

@@ -310,3 +310,24 @@ def test_group_shared_walker(case):
         inp.logA = (inp.logA * 40.0).astype(np.float32)
     assert plan_of(inp, 256)["walk"].startswith("ssd_walk_fused_kernel"), plan_of(inp, 256)
     check(inp, 256, case)
+
+
+# The general walker with B staged in parts (fewer B rows than the padded chunk fit in
+# LDS next to the rest): float32 with 256-row chunks at d_state 128, float32 with 128-row
+# chunks at d_state 256, bfloat16 with 256-row chunks at head dimension 48 and d_state 256
+# (C B^T tiles staged in LDS too); ragged last chunks, initial states, and one packed batch.
+@pytest.mark.parametrize("case", ["f32_q256_n128", "f32_q128_n256", "bf16_q256_p48_n256", "f32_q256_n128_packed"])
+def test_general_walker_staged_b(case):
+    if case == "f32_q256_n128":
+        inp, Q = make_inputs(2, 700, 4, 64, 128, 2, "f32", seed=1400, init_state=True), 256
+    elif case == "f32_q128_n256":
+        inp, Q = make_inputs(2, 300, 4, 64, 256, 2, "f32", seed=1401, init_state=True), 128
+    elif case == "bf16_q256_p48_n256":
+        inp, Q = make_inputs(2, 600, 4, 48, 256, 2, "bf16", seed=1402, init_state=True), 256
+    else:
+        lens = [300, 0, 1, 257, 142]
+        inp, Q = make_inputs(1, sum(lens), 4, 64, 128, 2, "f32", seed=1403, init_state=True, seq_lengths=lens), 256
+    walk = plan_of(inp, Q)["walk"]
+    qb, qp = (int(v) for v in walk.split("qb=")[1].split("/"))
+    assert walk.startswith("ssd_walk_kernel<") and qb < qp, walk
+    check(inp, Q, case)
