@@ -149,33 +149,53 @@ __global__ void __launch_bounds__(256) ssd_bwd_group_sum_kernel(const T* in, T* 
 }
 
 // rr[r][h] = dy . y - x . dx over the head's P values.  Each thread takes one 16-byte
-// vector of the flat [rows * H * P] arrays (coalesced), and the partial sums of one
-// (row, head) meet in LDS: a block of 256 vectors spans at most 256 / (P / 8) + 1 of them.
+// vector of the flat [rows * H * P] arrays (coalesced) per window of 256 vectors; the
+// window's partial sums meet in LDS and each (row, head) that starts in the window adds
+// its P / 8 partial sums in column order (those past the window's end recomputed from
+// memory), so rr does not depend on the order in which threads finish.
 template <typename T>
 __global__ void __launch_bounds__(256) ssd_bwd_dot_kernel(const T* dY, const T* Y, const T* X, const T* dX,
                                                           float* rr, int64_t rows, int H, int P) {
     using E = Elem<T>;
     typedef typename E::frag frag;
-    __shared__ float part[257];
+    // each thread's partial sum of 8 columns, then each (row, head) item sums its vectors
+    // in column order: a fixed order, so the result does not depend on thread timing
+    __shared__ float part[256];
     const int vpi = P / 8;                             // vectors per (row, head)
     const int64_t nvec = rows * H * vpi;
     for (int64_t base = (int64_t)blockIdx.x * 256; base < nvec; base += (int64_t)gridDim.x * 256) {
-        const int64_t item0 = base / vpi;
-        const int64_t item_end = min(nvec, base + 256) - 1;
-        const int nitem = (int)(item_end / vpi - item0) + 1;
-        for (int i = threadIdx.x; i < nitem; i += 256) part[i] = 0.f;
-        __syncthreads();
         const int64_t v = base + threadIdx.x;
+        float acc = 0.f;
         if (v < nvec) {
             const int64_t e = v * 8;
             const frag a = E::ldg8(dY + e), b = E::ldg8(Y + e), x = E::ldg8(X + e), d = E::ldg8(dX + e);
-            float acc = 0.f;
 #pragma unroll
             for (int q = 0; q < 8; ++q) acc += E::to_f(a[q]) * E::to_f(b[q]) - E::to_f(x[q]) * E::to_f(d[q]);
-            atomicAdd(&part[v / vpi - item0], acc);
         }
+        part[threadIdx.x] = acc;
         __syncthreads();
-        for (int i = threadIdx.x; i < nitem; i += 256) rr[item0 + i] = part[i];
+        // the items that start in this 256-vector window (an item that starts in the
+        // previous window was summed there: windows are whole items when vpi divides 256,
+        // else an item's vectors past the window are read from the next window's loads)
+        const int64_t first = (base + vpi - 1) / vpi, last = (min(nvec, base + 256) - 1) / vpi;
+        for (int64_t it = first + threadIdx.x; it <= last; it += 256) {
+            float sum = 0.f;
+            for (int k = 0; k < vpi; ++k) {
+                const int64_t w = it * vpi + k;
+                if (w < base + 256) {
+                    sum += part[w - base];
+                } else {
+                    // past the window: recompute from global memory, in the same order
+                    const int64_t e = w * 8;
+                    const frag a = E::ldg8(dY + e), b = E::ldg8(Y + e), x = E::ldg8(X + e), d = E::ldg8(dX + e);
+                    float r = 0.f;
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) r += E::to_f(a[q]) * E::to_f(b[q]) - E::to_f(x[q]) * E::to_f(d[q]);
+                    sum += r;
+                }
+            }
+            rr[it] = sum;
+        }
         __syncthreads();
     }
 }

@@ -90,7 +90,7 @@ def check_backward(inp, Q, label, with_dfinal=True, seed=0):
 
 
 @pytest.mark.parametrize("case", ["layer_shape", "varlen", "f32_general", "bf16_q64", "no_init_no_dfinal",
-                                  "segmented", "headdim128"])
+                                  "segmented", "headdim128", "f32_headdim48"])
 def test_backward_matches_oracle(case):
     if case == "layer_shape":
         inp = make_inputs(2, 600, 4, 64, 128, 2, "bf16", seed=2000, init_state=True)
@@ -113,9 +113,42 @@ def test_backward_matches_oracle(case):
     elif case == "segmented":
         inp = make_inputs(1, 4200, 4, 64, 128, 1, "bf16", seed=2005, init_state=True)
         check_backward(inp, 256, case)
-    else:
+    elif case == "headdim128":
         inp = make_inputs(2, 520, 3, 128, 64, 1, "bf16", seed=2006, init_state=True)
         check_backward(inp, 256, case)
+    else:
+        # P = 48: a (row, head) item of 6 vectors can straddle two 256-vector windows of
+        # the decay-gradient dot product
+        inp = make_inputs(2, 300, 5, 48, 32, 1, "f32", seed=2007, init_state=True)
+        check_backward(inp, 64, case)
+
+
+def test_backward_is_bitwise_repeatable():
+    """Two backward passes on the same inputs give the same bits in every gradient (no
+    atomics and no order that depends on thread timing); the layer shape and a packed
+    batch at P = 48 (items straddling reduction windows)."""
+    import mamba_ssd_scan_forward_amd as ssd
+    torch = _torch()
+    cases = [(make_inputs(2, 600, 4, 64, 128, 2, "bf16", seed=2100, init_state=True), 256),
+             (make_inputs(1, 700, 5, 48, 32, 1, "f32", seed=2101, init_state=True,
+                          seq_lengths=[300, 0, 1, 399]), 64)]
+    for inp, Q in cases:
+        dt = torch.bfloat16 if inp.dtype == "bf16" else torch.float32
+        dev = lambda a, t=dt: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(t).cuda()
+        rng = np.random.default_rng(5)
+        nseq = inp.X.shape[0] if inp.seq_offsets is None else len(inp.seq_offsets) - 1
+        H, P, N = inp.X.shape[2], inp.X.shape[3], inp.B.shape[3]
+        dY = rng.standard_normal(inp.X.shape)
+        dF = (rng.standard_normal((nseq, H, P, N)) * 0.5).astype(np.float32)
+        X, logA, B, C = dev(inp.X), dev(inp.logA, torch.float32), dev(inp.B), dev(inp.C)
+        init = dev(inp.init, torch.float32)
+        off = None if inp.seq_offsets is None else torch.from_numpy(inp.seq_offsets).cuda()
+        print(f"[backward] repeatability X{tuple(inp.X.shape)} {inp.dtype}", flush=True)
+        Y, F = ssd.forward(X, logA, B, C, Q, init, off)
+        runs = [ssd.backward(X, logA, B, C, Q, Y, dev(dY), init, off, F, dev(dF, torch.float32)) for _ in range(3)]
+        torch.cuda.synchronize()
+        for name, a, b, c in zip(["dX", "dlogA", "dB", "dC", "dinit"], *runs):
+            assert torch.equal(a, b) and torch.equal(a, c), name
 
 
 @pytest.mark.parametrize("name,sample", [("cfg1_mamba2_2.7b_bf16", [0, 7]), ("cfg4_varlen32k_bf16", [6, 13])])
