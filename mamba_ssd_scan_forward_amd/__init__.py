@@ -60,6 +60,17 @@ class SsdError(RuntimeError):
         super().__init__(f"{what} failed: {ssd_status_string(status)} ({status})")
 
 
+def _share_hip_runtime():
+    """One HIP runtime per process.  PyTorch for ROCm ships its own libamdhip64 and loads
+    it by path: if a library of ours came first (binding the system runtime of the same
+    soname), the process would hold two runtimes and the one ours uses would find no
+    device.  Loaded after torch, our libraries bind to torch's runtime."""
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+
+
 def lib_path() -> str:
     return os.path.join(_HERE, "libssd.so")
 
@@ -72,6 +83,7 @@ def load_library():
     path = lib_path()
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m mamba_ssd_scan_forward_amd.build`")
+    _share_hip_runtime()
     lib = ctypes.CDLL(path)
     vp, sz = ctypes.c_void_p, ctypes.c_size_t
     pp = ctypes.POINTER(SsdProblem)
@@ -119,6 +131,7 @@ def load_probe_library():
     path = probe_lib_path()
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m mamba_ssd_scan_forward_amd.build`")
+    _share_hip_runtime()
     lib = ctypes.CDLL(path)
     vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.ssd_probe_mfma_bf16.argtypes = [i64, ci, vp, vp]

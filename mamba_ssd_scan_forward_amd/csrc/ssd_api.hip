@@ -466,7 +466,7 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
         fa.lpt = (seq_offsets && p->nseq <= 64) ? 1 : 0;
         int64_t grid = pl.fused_items;
         if (fa.lpt) grid = ((p->nseq * G + 7) / 8) * 8 * pl.fused_wpg;
-        hipLaunchKernelGGL(pl.fused_fn, dim3((unsigned)grid), dim3(64 * (pl.fused + 2)), 0, stream, fa);
+        hipLaunchKernelGGL(pl.fused_fn, dim3((unsigned)grid), dim3(64 * (pl.fused + 3)), 0, stream, fa);
         return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
     }
     walk_fn walk = pl.walk;

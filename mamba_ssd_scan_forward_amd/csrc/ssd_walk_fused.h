@@ -23,16 +23,21 @@
 // 2^(cs_l - cs_s) on unscaled X, the state brought to 2^e h before its update with
 // X~ = 2^(e - cs_s) X (every factor <= 1).
 //
-// Workgroup: NW compute waves and two loader waves.  Compute wave k holds unit u = q NW + k
-// of its group (head u / (P/32), columns 32 (u % (P/32)) .. + 31): the state g^T of that
-// slice (N x 32 float32, N/32 MFMA accumulators of 32 x 32) for the whole sequence.  The
-// X-loader brings each unit's X rows, the BC-loader the group's B and C rows and the
-// heads' logA, all straight from global memory into a ring of four LDS slots, three
-// blocks ahead.  The BC-loader also turns each block into its products one step before
-// it is used: the cumsums, w and r of every head, the renormalisation and steep flags,
-// and the masked tile D in the layout of an MFMA operand (v_mfma_f32_32x32x16_bf16 on B
-// and C rows).  Compute waves issue no loads to LDS, read only LDS, and store Y from
-// registers; one barrier per block hands the ring slot and the products over.
+// Workgroup: NW compute waves, two loader waves and a storer.  Compute wave k holds unit
+// u = q NW + k of its group (head u / (P/32), columns 32 (u % (P/32)) .. + 31): the state
+// g^T of that slice (N x 32 float32, N/32 MFMA accumulators of 32 x 32) for the whole
+// sequence.  The X-loader brings each unit's X rows, the BC-loader the group's B and C
+// rows and the heads' logA, all straight from global memory into a ring of LDS slots,
+// two or three blocks ahead.  The loaders also turn each block into its products one
+// step before it is used: the cumsums, w and r of every head, the renormalisation and
+// steep flags, and the masked tile D in the layout of an MFMA operand
+// (v_mfma_f32_32x32x16_bf16 on B and C rows).  Compute waves issue no global memory
+// instruction at all: they read LDS and write their Y tile to a staging buffer in LDS,
+// from which the storer writes the workgroup's block of Y one block later as whole
+// contiguous row spans (NW units of 64 bytes per row: few, line-sized write requests
+// instead of 32-byte pieces, and no compute wave ever waits behind the loaders' traffic
+// in the vector memory path).  One barrier per block hands the ring slot, the products
+// and the staging buffer over.
 //
 // Contraction order.  A lane holds accumulator rows 8 (e / 4) + 4 lg + e % 4 of a 32 x 32
 // tile (lg = lane / 32).  The state tile g^T (n x p) therefore enters the left factor
@@ -80,7 +85,8 @@ template <int NP, int NW> struct FusedLds {
     static constexpr int xbytes = NW * 2048;
     static constexpr int bcbytes = 32 * NP * 2;
     static constexpr int labytes = ((NHL + 1) / 2) * 256;
-    static constexpr int nslot = NP == 256 ? 3 : 4;    // blocks in flight: nslot - 1
+    // blocks in flight: nslot - 1 (three slots where four would not fit next to the rest)
+    static constexpr int nslot = (NP == 256 || (NP == 128 && NW == 6)) ? 3 : 4;
     static constexpr int dg = 0;
     static constexpr int w = 2048;
     static constexpr int r = w + NHL * 128;
@@ -89,7 +95,10 @@ template <int NP, int NW> struct FusedLds {
     static constexpr int fl = f + NHL * 4;
     static constexpr int st = (fl + NHL * 4 + 15) / 16 * 16;
     static constexpr int prod = st + NHL * 2048;
-    static constexpr int total = nslot * (xbytes + 2 * bcbytes + 2 * labytes) + 2 * prod;
+    // the staging of Y for the storer: [32 rows][NW units x 64 bytes + 16], two buffers
+    static constexpr int ystride = NW * 64 + 16;
+    static constexpr int ybytes = 32 * ystride;
+    static constexpr int total = nslot * (xbytes + 2 * bcbytes + 2 * labytes) + 2 * prod + 2 * ybytes;
     static_assert(total <= 160 * 1024, "LDS");
 };
 
@@ -106,6 +115,8 @@ template <int NP> __device__ __forceinline__ int fused_swz(int r) {
 // (LDS addresses are kept in address space 3 throughout: a generic pointer converted at
 // each use would cost a null test per load)
 typedef SSD_LDS unsigned char* lds_ptr;
+// cache policy of the Y stores: nontemporal (gfx950 "nt"), the kernel never reads Y back
+constexpr int kStreamAux = 2;
 __device__ __forceinline__ void fused_lds16(rsrc_t r, lds_ptr dst, uint32_t voff, uint32_t soff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (SSD_LDS void*)dst, 16, (int)voff, (int)soff, 0, 0);
 }
@@ -162,6 +173,7 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
     __shared__ __align__(16) unsigned char l0[LL::labytes], l1[LL::labytes], l2[LL::labytes], l3[NSL == 4 ? LL::labytes : 16];
     __shared__ __align__(16) unsigned char m0[LL::labytes], m1[LL::labytes], m2[LL::labytes], m3[NSL == 4 ? LL::labytes : 16];
     __shared__ __align__(16) unsigned char p0[LL::prod], p1[LL::prod];
+    __shared__ __align__(16) unsigned char ys0[LL::ybytes], ys1[LL::ybytes];
     auto pick = [](int k, unsigned char* a0, unsigned char* a1, unsigned char* a2, unsigned char* a3)
                     __attribute__((always_inline)) -> lds_ptr {
         return k == 0 ? (lds_ptr)a0 : k == 1 ? (lds_ptr)a1 : k == 2 ? (lds_ptr)a2 : (lds_ptr)a3;
@@ -191,7 +203,8 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
     const bool compute = (wave & 3) != 3 && wave - (wave >> 2) < NW;
     const int ci = wave - (wave >> 2);     // compute index (compute waves)
     const bool bcloader = wave == 3;
-    const bool xloader = !compute && !bcloader;
+    const bool storer = wave == NW + 2;
+    const bool xloader = !compute && !bcloader && !storer;
     const int H = a.H, P = a.P, G = a.G, hpg = H / G, uph = P / 32;
 
     int64_t row0;
@@ -208,8 +221,9 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
     const int hfirst = u0 / uph;           // first head (within the group) it touches
     const int64_t xrow = (int64_t)H * P;   // elements per token row of X / Y
 
-    // ---- per-block product buffers
+    // ---- per-block product buffers and Y staging
     auto pbuf = [&](int t) __attribute__((always_inline)) -> lds_ptr { return (t & 1) ? (lds_ptr)p1 : (lds_ptr)p0; };
+    auto ybuf = [&](int t) __attribute__((always_inline)) -> lds_ptr { return (t & 1) ? (lds_ptr)ys1 : (lds_ptr)ys0; };
 
     // ring and barrier discipline shared by both loaders: blocks 0 .. D-1 in flight before
     // the first step; step t issues block t + D (past the end: the last block again, so
@@ -318,6 +332,47 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
 #pragma unroll
         for (int p = 0; p < NPAIR; ++p)
             if (2 * p + lg < NHL && lr == 0) ldsw<float>(pbuf(0) + L::f + 4 * (2 * p + lg), lsig[p]);
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        return;
+    }
+
+    if (storer) {
+        // ------------------------------------------------------------ storer: once the
+        // barrier after block t has passed, the workgroup's Y rows of block t from the
+        // staging buffer: 32 rows of NW contiguous units (64 bytes each) as 16-byte
+        // pieces, 4 NW per row, 64 pieces per store, streamed past the caches' reuse (the
+        // kernel never reads Y)
+        constexpr int NST = 2 * NW;
+        const rsrc_t yr = make_rsrc(a.Y + row0 * xrow, (uint32_t)((int64_t)len * xrow * 2));
+        uint32_t yo[NST], yl[NST];
+        bool yv[NST];
+#pragma unroll
+        for (int i = 0; i < NST; ++i) {
+            const int pc = 64 * i + lane, row = pc / (4 * NW), piece = pc % (4 * NW);
+            yo[i] = (uint32_t)((row * xrow + (int64_t)g * hpg * P + 32 * u0 + 8 * piece) * 2);
+            yl[i] = (uint32_t)(row * L::ystride + 16 * piece);
+            yv[i] = u0 + piece / 4 < a.upg;   // (units past the group's last are not ours)
+        }
+        const uint32_t yb32 = (uint32_t)(32 * xrow * 2);
+        auto ystore = [&](int t) __attribute__((always_inline)) {
+            const lds_ptr yb = ybuf(t);
+            u32x4 v[NST];
+#pragma unroll
+            for (int i = 0; i < NST; ++i) v[i] = ldsv<u32x4>(yb + yl[i]);
+#pragma unroll
+            for (int i = 0; i < NST; ++i)
+                if (yv[i]) __builtin_amdgcn_raw_buffer_store_b128(v[i], yr, (int)yo[i], (int)((uint32_t)t * yb32), kStreamAux);
+        };
+        // the same barriers as the other waves: the first, one per block, the last two
+        __builtin_amdgcn_s_barrier();
+        for (int t = 0; t < nb; ++t) {
+            if (t > 0) ystore(t - 1);
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_s_barrier();
+        }
+        __builtin_amdgcn_s_barrier();
+        if (nb > 0) ystore(nb - 1);
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_s_barrier();
         return;
@@ -451,9 +506,6 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
                 for (int e4 = 0; e4 < 4; ++e4) gs[nt][4 * q4 + e4] = iv[e4];
             }
     }
-    const rsrc_t yr = make_rsrc(a.Y + row0 * xrow, valid ? (uint32_t)((int64_t)len * xrow * 2) : 0u);
-    const uint32_t ylane = (uint32_t)((lr * xrow + (int64_t)h * P + c0 + 8 * lg) * 2);
-    const uint32_t yb32 = (uint32_t)(32 * xrow * 2);
     // LDS addresses (byte offsets inside a slot).  With the swizzle of B / C rows the unit
     // position of n tile nt is 4 (nt ^ a) + (m ^ b) for per-lane a, b: one base per n tile
     // and one per 16-byte unit inside it.
@@ -501,9 +553,17 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int q8 = 0; q8 < 8; ++q8) xt[ks][q8] = (__bf16)((float)xf[ks][q8] * ws[ks][q8]);
-        // one n tile: the left factor's two K-steps on the state before its update, then the
-        // state update (SCALE: the exact form's decay of the state between the two)
-        auto ntile = [&](f32x16& acc, int nt, bool scale) __attribute__((always_inline)) {
+        // One code path for the three kinds of block; the flag only switches in-place
+        // scalings and the diagonal tile's operands, so the state stays in the same
+        // registers whatever the path (branches of their own around the scalings: as
+        // selects every block would pay them).
+        //   plain (0):        Y = r [C g + D X~],                 g' = g + B^T X~
+        //   renormalise (1):  g <- f g first, then as plain
+        //   exact (2):        Y = r C g + D_exact X,              g' = f g + B^T X~
+        const bool renorm = flag == 1, exact = flag == 2;
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
             bf16x8 cf[2], bt[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
@@ -513,6 +573,11 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
                 bt[kk] = cat44(ldsb(bsl, bnt[nt] + bm[kk][0] + 32 * NP * kk),
                                ldsb(bsl, bnt[nt] + bm[kk][1] + 32 * NP * kk + 16 * NP));
             }
+            if (renorm) {
+                asm volatile("");
+                gs[nt] *= f;
+            }
+            // the left factor's two K-steps on the state before its update
             bf16x8 hb[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
@@ -520,56 +585,41 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
                 for (int q8 = 0; q8 < 8; ++q8) hb[kk][q8] = (__bf16)gs[nt][8 * kk + q8];
             acc = E::mma(acc, hb[0], cf[0]);
             acc = E::mma(acc, hb[1], cf[1]);
-            if (scale) gs[nt] *= f;
+            if (exact) {
+                asm volatile("");
+                gs[nt] *= f;
+            }
             gs[nt] = E::mma(gs[nt], bt[0], xt[0]);
             gs[nt] = E::mma(gs[nt], bt[1], xt[1]);
-        };
-        f32x16 acc = f32x16{};
-        if (flag != 2) {
-            if (flag == 1) {
-                // (a branch, not a select: as a select every block would pay the pass)
-                asm volatile("");
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) gs[nt] *= f;
-            }
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) ntile(acc, nt, false);
-            const bf16x8 d0 = ldsv<bf16x8>(pb + L::dg + 16 * lane);
-            const bf16x8 d1 = ldsv<bf16x8>(pb + L::dg + 1024 + 16 * lane);
-            acc = E::mma(acc, xt[0], d0);
-            acc = E::mma(acc, xt[1], d1);
-            acc *= rl;
-        } else {
-            // exact form (steep block): left factor of the unscaled state, the per-head
-            // masked tile on unscaled X, the state brought to 2^e h before its update
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) ntile(acc, nt, true);
-            acc *= rl;
-            const lds_ptr stp = pb + L::st + 2048 * jh;
-            const bf16x8 d0 = ldsv<bf16x8>(stp + 16 * lane);
-            const bf16x8 d1 = ldsv<bf16x8>(stp + 1024 + 16 * lane);
-            acc = E::mma(acc, xf[0], d0);
-            acc = E::mma(acc, xf[1], d1);
         }
-        // Y^T (p x l) -> bf16 pairs; lanes l and l + 32 trade pieces so that each holds 8
-        // consecutive columns of row l twice (columns 16 j + 8 lg .. + 7, j = 0, 1)
-        uint32_t pk[8];
-#pragma unroll
-        for (int j8 = 0; j8 < 8; ++j8) {
-            const bf16x2 v = {(__bf16)acc[2 * j8], (__bf16)acc[2 * j8 + 1]};
-            pk[j8] = __builtin_bit_cast(uint32_t, v);
+        // the diagonal tile: the shared masked tile on X~, or (exact) this head's tile with
+        // the exact decays on unscaled X, added after the row factor
+        if (exact) {
+            asm volatile("");
+            acc *= rl;
         }
+        const lds_ptr dp = exact ? pb + L::st + 2048 * jh : pb + L::dg;
+        const bf16x8 d0 = ldsv<bf16x8>(dp + 16 * lane);
+        const bf16x8 d1 = ldsv<bf16x8>(dp + 1024 + 16 * lane);
+        bf16x8 xd[2];
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
+        for (int ks = 0; ks < 2; ++ks) xd[ks] = exact ? xf[ks] : xt[ks];
+        acc = E::mma(acc, xd[0], d0);
+        acc = E::mma(acc, xd[1], d1);
+        if (!exact) {
+            asm volatile("");
+            acc *= rl;
+        }
+        // Y^T (p x l) to the staging buffer as bf16 rows: lane (l, lg) holds columns
+        // 8 q + 4 lg .. + 3 of row l, q = 0 .. 3 (the storer writes the block out after the
+        // barrier)
+        const lds_ptr yb = ybuf(t) + lr * L::ystride + ci * 64 + 8 * lg;
 #pragma unroll
-            for (int j2 = 0; j2 < 2; ++j2) {
-                const auto sw = __builtin_amdgcn_permlane32_swap(pk[4 * hf + j2], pk[4 * hf + 2 + j2], false, false);
-                pk[4 * hf + j2] = sw[0];
-                pk[4 * hf + 2 + j2] = sw[1];
-            }
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{pk[0], pk[1], pk[2], pk[3]}, yr, (int)ylane, (int)((uint32_t)t * yb32), 0);
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{pk[4], pk[5], pk[6], pk[7]}, yr, (int)(ylane + 32u),
-                                               (int)((uint32_t)t * yb32), 0);
+        for (int q = 0; q < 4; ++q) {
+            const bf16x2 v0 = {(__bf16)acc[4 * q], (__bf16)acc[4 * q + 1]};
+            const bf16x2 v1 = {(__bf16)acc[4 * q + 2], (__bf16)acc[4 * q + 3]};
+            ldsw<u32x2>(yb + 16 * q, u32x2{__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1)});
+        }
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_s_barrier();
     };
@@ -597,7 +647,7 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
 }
 
 template <int NP, int NW>
-__global__ void __launch_bounds__(64 * (NW + 2), 1) ssd_walk_fused_kernel(FusedArgs a) {
+__global__ void __launch_bounds__(64 * (NW + 3), 1) ssd_walk_fused_kernel(FusedArgs a) {
     const int lane = threadIdx.x & 63;
     const int G = a.G, wpg = a.wpg;
     int s, g, q;

@@ -331,3 +331,23 @@ def test_general_walker_staged_b(case):
     qb, qp = (int(v) for v in walk.split("qb=")[1].split("/"))
     assert walk.startswith("ssd_walk_kernel<") and qb < qp, walk
     check(inp, Q, case)
+
+
+def test_library_loaded_before_the_first_gpu_use():
+    """The library loaded before anything touches the GPU (here: before torch is imported)
+    still runs: the binding makes it share PyTorch's HIP runtime instead of holding a
+    second one that finds no device.  In a fresh process, since the order of loading is
+    what is tested."""
+    import subprocess
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import mamba_ssd_scan_forward_amd as ssd\n"
+            "ssd.load_library()\n"
+            "import torch\n"
+            "from workloads import CONFIGS, workload_inputs\n"
+            "inp = workload_inputs(CONFIGS['cfg0_tiny_f32'])\n"
+            "d = [torch.from_numpy(a).cuda() for a in (inp.X, inp.logA, inp.B, inp.C)]\n"
+            "Y, F = ssd.forward(*d, 64)\n"
+            "torch.cuda.synchronize()\n"
+            "print('ok', float(Y.abs().max()))\n") % os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=100)
+    assert res.returncode == 0 and "ok" in res.stdout, res.stdout + res.stderr
