@@ -74,7 +74,7 @@ struct FusedArgs {
     int lpt;        // packed sequences dealt to XCDs longest first
 };
 
-// LDS of the fused walker.  Ring slot: X [NW][32][32] (unit-major, row-major), B and C
+// LDS of the fused walker.  Ring slot: X [32][NW][32] (the block's rows of the units side by side), B and C
 // [32][N] (16-byte units of a row XOR-swizzled by fused_swz), logA [NHL][32].  Products
 // (two buffers): the masked tile D^T as MFMA B-operand fragments [2][64][8] bf16, per
 // head w [32] (in the sigma order of the K index), r [32], the cumsum [32], the
@@ -267,12 +267,17 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
         const int hrep = H / a.xh;
         const rsrc_t xr = make_rsrc(a.X + row0 * xrx, (uint32_t)((int64_t)len * xrx * 2));
         const rsrc_t lar = make_rsrc(a.logA + row0 * H, (uint32_t)((int64_t)len * H * 4));
-        uint32_t xl[NW];
+        // the slot holds the block's rows of the NW units side by side, [32][NW x 64 bytes],
+        // filled in that order by 2 NW loads of 64 16-byte pieces: lane i of load j takes
+        // piece 64 j + i, row (64 j + i) / 4 NW; with one X row per head the pieces of a
+        // row are one contiguous run of memory (units past the group's last repeat it)
+        uint32_t xl[2 * NW];
 #pragma unroll
-        for (int k = 0; k < NW; ++k) {
-            const int u = min(u0 + k, a.upg - 1);
+        for (int j = 0; j < 2 * NW; ++j) {
+            const int pc = 64 * j + lane, row = pc / (4 * NW), piece = pc % (4 * NW);
+            const int u = min(u0 + piece / 4, a.upg - 1);
             const int h = g * hpg + u / uph, c0 = 32 * (u % uph);
-            xl[k] = (uint32_t)(((lane >> 2) * xrx + (int64_t)(h / hrep) * P + c0 + 8 * (lane & 3)) * 2);
+            xl[j] = (uint32_t)((row * xrx + (int64_t)(h / hrep) * P + c0 + 8 * (piece % 4)) * 2);
         }
         // logA: lanes 0..31 head 2 p, lanes 32..63 head 2 p + 1 (clamped to the group)
         uint32_t ll[NPAIR];
@@ -281,15 +286,12 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
             const int hl = min(hfirst + 2 * p + lg, hpg - 1);
             ll[p] = (uint32_t)((lr * H + g * hpg + hl) * 4);
         }
-        const uint32_t rs16 = (uint32_t)(16 * xrx * 2), rb32 = (uint32_t)(32 * xrx * 2), lab32 = (uint32_t)(32 * H * 4);
+        const uint32_t rb32 = (uint32_t)(32 * xrx * 2), lab32 = (uint32_t)(32 * H * 4);
         auto issue = [&](int b, auto kc) __attribute__((always_inline)) {
             constexpr int k = decltype(kc)::value;
             b = min(b, nb - 1);
 #pragma unroll
-            for (int u = 0; u < NW; ++u) {
-                fused_lds16(xr, XS(k) + u * 2048, opaque(xl[u]), (uint32_t)b * rb32);
-                fused_lds16(xr, XS(k) + u * 2048 + 1024, opaque(xl[u]) + rs16, (uint32_t)b * rb32);
-            }
+            for (int j = 0; j < 2 * NW; ++j) fused_lds16(xr, XS(k) + 1024 * j, opaque(xl[j]), (uint32_t)b * rb32);
 #pragma unroll
             for (int p = 0; p < NPAIR; ++p) fused_lds4(lar, LA(k) + 256 * p, opaque(ll[p]), (uint32_t)b * lab32);
         };
@@ -509,7 +511,8 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
     // LDS addresses (byte offsets inside a slot).  With the swizzle of B / C rows the unit
     // position of n tile nt is 4 (nt ^ a) + (m ^ b) for per-lane a, b: one base per n tile
     // and one per 16-byte unit inside it.
-    const int xa0 = ci * 2048 + 64 * (4 * lg + ((lane & 15) >> 2)) + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    constexpr int XR = NW * 64;   // bytes per row of the X slot
+    const int xa0 = ci * 64 + XR * (4 * lg + ((lane & 15) >> 2)) + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
     int cnt[NT], cm[4];   // C pieces of row lr: n tile part, unit part (m = 2 kk + j)
     int bnt[NT], bm[2][2];   // B^T transposing reads: n tile part, (K-step, 4-row half) part
     {
@@ -540,7 +543,7 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
         bf16x8 xf[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-            xf[ks] = cat44(tr4(xsl + xa0 + 1024 * ks), tr4(xsl + xa0 + 1024 * ks + 512));
+            xf[ks] = cat44(tr4(xsl + xa0 + 16 * XR * ks), tr4(xsl + xa0 + 16 * XR * ks + 8 * XR));
         const lds_ptr wp = pb + L::w + 128 * jh + 32 * lg;
         const f32x4 w00 = ldsv<f32x4>(wp), w01 = ldsv<f32x4>(wp + 16), w10 = ldsv<f32x4>(wp + 64), w11 = ldsv<f32x4>(wp + 80);
         const float rl = ldsv<float>(pb + L::r + 4 * (32 * jh + lr));
