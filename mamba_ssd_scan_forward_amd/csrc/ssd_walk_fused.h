@@ -133,6 +133,28 @@ __device__ __forceinline__ void fused_wait_vm() {
 __device__ __forceinline__ bf16x4 tr4(lds_ptr p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SSD_LDS bf16x4*)p);
 }
+// Eight 16-byte LDS reads in one asm block that also waits for them.  The BC-loader reads
+// its slot's B and C rows this way: with each ring one array, the compiler's bookkeeping of
+// the wave's direct-to-LDS loads could not tell the slot being read from the slots still
+// being filled and would wait for all of them (the loader has waited for this slot
+// itself).  (A load written in asm completes inside its block: the compiler treats the
+// outputs as written when the block ends.)
+__device__ __forceinline__ void lds_read8x16(const uint32_t (&ad)[8], bf16x8 (&r)[8]) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n"
+        "ds_read_b128 %1, %9\n"
+        "ds_read_b128 %2, %10\n"
+        "ds_read_b128 %3, %11\n"
+        "ds_read_b128 %4, %12\n"
+        "ds_read_b128 %5, %13\n"
+        "ds_read_b128 %6, %14\n"
+        "ds_read_b128 %7, %15\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7])
+        : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(lds_ptr p) { return (uint32_t)(uintptr_t)p; }
 __device__ __forceinline__ bf16x8 cat44(bf16x4 lo, bf16x4 hi) {
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
@@ -167,9 +189,10 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
     // ring slots and product buffers: separate arrays, so that the compiler can tell the
     // slot a direct-to-LDS load is filling from the slot being read; selected by constant
     // index (a constant table of LDS addresses cannot be emitted)
+    // (B and C: one array per ring, so that a compute wave reads any slot at an immediate
+    // offset from one per-lane address)
+    __shared__ __align__(16) unsigned char cring[NSL][LL::bcbytes], bring[NSL][LL::bcbytes];
     __shared__ __align__(16) unsigned char x0[LL::xbytes], x1[LL::xbytes], x2[LL::xbytes], x3[NSL == 4 ? LL::xbytes : 16];
-    __shared__ __align__(16) unsigned char b0[LL::bcbytes], b1[LL::bcbytes], b2[LL::bcbytes], b3[NSL == 4 ? LL::bcbytes : 16];
-    __shared__ __align__(16) unsigned char c0_[LL::bcbytes], c1_[LL::bcbytes], c2_[LL::bcbytes], c3_[NSL == 4 ? LL::bcbytes : 16];
     __shared__ __align__(16) unsigned char l0[LL::labytes], l1[LL::labytes], l2[LL::labytes], l3[NSL == 4 ? LL::labytes : 16];
     __shared__ __align__(16) unsigned char m0[LL::labytes], m1[LL::labytes], m2[LL::labytes], m3[NSL == 4 ? LL::labytes : 16];
     __shared__ __align__(16) unsigned char p0[LL::prod], p1[LL::prod];
@@ -179,8 +202,8 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
         return k == 0 ? (lds_ptr)a0 : k == 1 ? (lds_ptr)a1 : k == 2 ? (lds_ptr)a2 : (lds_ptr)a3;
     };
     auto XS = [&](int k) __attribute__((always_inline)) { return pick(k, x0, x1, x2, x3); };
-    auto BS = [&](int k) __attribute__((always_inline)) { return pick(k, b0, b1, b2, b3); };
-    auto CS = [&](int k) __attribute__((always_inline)) { return pick(k, c0_, c1_, c2_, c3_); };
+    auto BS = [&](int k) __attribute__((always_inline)) { return (lds_ptr)bring[k]; };
+    auto CS = [&](int k) __attribute__((always_inline)) { return (lds_ptr)cring[k]; };
     auto LA = [&](int k) __attribute__((always_inline)) { return pick(k, l0, l1, l2, l3); };
     auto LA2 = [&](int k) __attribute__((always_inline)) { return pick(k, m0, m1, m2, m3); };
 
@@ -419,12 +442,32 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
             // every fragment is read before the first product (one LDS round trip, not one per
             // K-step)
             const lds_ptr bsl = BS(k), csl = CS(k);
-            bf16x8 bfr[NP / 16], cfr[NP / 16];
+            constexpr int NK = NP / 16;
+            bf16x8 bfr[NK], cfr[NK];
+            {
+                uint32_t ad[2 * NK];
 #pragma unroll
-            for (int kk = 0; kk < NP / 16; ++kk) {
-                const int o = 2 * (lr * NP + 8 * ((2 * kk + lg) ^ fused_swz<NP>(lr)));
-                bfr[kk] = ldsv<bf16x8>(bsl + o);
-                cfr[kk] = ldsv<bf16x8>(csl + o);
+                for (int kk = 0; kk < NK; ++kk) {
+                    const int o = 2 * (lr * NP + 8 * ((2 * kk + lg) ^ fused_swz<NP>(lr)));
+                    ad[kk] = lds_addr(bsl + o);
+                    ad[NK + kk] = lds_addr(csl + o);
+                }
+                bf16x8 r[2 * NK];
+#pragma unroll
+                for (int c = 0; c < 2 * NK; c += 8) {
+                    uint32_t a8[8];
+                    bf16x8 r8[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) a8[i] = ad[c + i];
+                    lds_read8x16(a8, r8);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) r[c + i] = r8[i];
+                }
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) {
+                    bfr[kk] = r[kk];
+                    cfr[kk] = r[NK + kk];
+                }
             }
             f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
@@ -513,32 +556,37 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
     // and one per 16-byte unit inside it.
     constexpr int XR = NW * 64;   // bytes per row of the X slot
     const int xa0 = ci * 64 + XR * (4 * lg + ((lane & 15) >> 2)) + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
-    int cnt[NT], cm[4];   // C pieces of row lr: n tile part, unit part (m = 2 kk + j)
-    int bnt[NT], bm[2][2];   // B^T transposing reads: n tile part, (K-step, 4-row half) part
+    // Per-lane LDS addresses of every operand read in slot 0, computed once: slot k is
+    // k bcbytes further on, so each read is one register plus an immediate offset.
+    lds_ptr ca[NT][4];      // C pieces of row lr: n tile nt, piece m = 2 kk + j
+    lds_ptr ba[NT][2][2];   // B^T transposing reads: n tile nt, K-step, 4-row half
     {
         const int sa = fused_swz<NP>(lr);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) cnt[nt] = 2 * lr * NP + 8 * lg + 16 * ((4 * nt) ^ (sa & ~3));
-#pragma unroll
-        for (int m = 0; m < 4; ++m) cm[m] = 16 * (m ^ (sa & 3));
         const int rb = 4 * lg + ((lane & 15) >> 2);   // row of the transposing read, K-step 0, half 0
         const int v = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) bnt[nt] = 2 * rb * NP + 8 * (lane & 1) + 16 * ((4 * nt) ^ (fused_swz<NP>(rb) & ~3));
+        for (int nt = 0; nt < NT; ++nt) {
+            const int cnt = 2 * lr * NP + 8 * lg + 16 * ((4 * nt) ^ (sa & ~3));
+            const int bnt = 2 * rb * NP + 8 * (lane & 1) + 16 * ((4 * nt) ^ (fused_swz<NP>(rb) & ~3));
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+            for (int m = 0; m < 4; ++m) ca[nt][m] = CS(0) + cnt + 16 * (m ^ (sa & 3));
 #pragma unroll
-            for (int j = 0; j < 2; ++j) bm[ks][j] = 16 * (v ^ (fused_swz<NP>(16 * ks + 8 * j + rb) & 3));
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    ba[nt][ks][j] = BS(0) + bnt + 16 * (v ^ (fused_swz<NP>(16 * ks + 8 * j + rb) & 3)) + 32 * NP * ks +
+                                    16 * NP * j;
+        }
     }
     // (rows 16 ks + 8 j + rb have rb's part 4 (r % U4) of the swizzle, U4 dividing 8; only the
     // low two bits, (r / U4) % 4, change with ks and j)
-    auto ldsb = [&](lds_ptr base, int off) __attribute__((always_inline)) -> bf16x4 { return tr4(base + off); };
 
     __builtin_amdgcn_s_barrier();
     auto step = [&](int t, auto kc) __attribute__((always_inline)) {
         constexpr int k = decltype(kc)::value;
         const lds_ptr pb = pbuf(t);
-        const lds_ptr xsl = XS(k), bsl = BS(k), csl = CS(k);
+        const lds_ptr xsl = XS(k);
+        constexpr int ko = k * LL::bcbytes;   // slot k of the B and C rings
         // X of the block (K-step ks: rows 16 ks + sigma(8 lg + q))
         bf16x8 xf[2];
 #pragma unroll
@@ -570,11 +618,10 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
             bf16x8 cf[2], bt[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const u32x2 lo = ldsv<u32x2>(csl + cnt[nt] + cm[2 * kk]);
-                const u32x2 hi = ldsv<u32x2>(csl + cnt[nt] + cm[2 * kk + 1]);
+                const u32x2 lo = ldsv<u32x2>(ca[nt][2 * kk] + ko);
+                const u32x2 hi = ldsv<u32x2>(ca[nt][2 * kk + 1] + ko);
                 cf[kk] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-                bt[kk] = cat44(ldsb(bsl, bnt[nt] + bm[kk][0] + 32 * NP * kk),
-                               ldsb(bsl, bnt[nt] + bm[kk][1] + 32 * NP * kk + 16 * NP));
+                bt[kk] = cat44(tr4(ba[nt][kk][0] + ko), tr4(ba[nt][kk][1] + ko));
             }
             if (renorm) {
                 asm volatile("");
