@@ -116,8 +116,11 @@ int ssd_forward(const ssd_problem* p, const void* X, const float* logA, const vo
 
 /* One of the two launches that make up ssd_forward, with the same arguments and checks.
  *   stage 1: chunk cumsum of logA and the C B^T tiles of every chunk, written to the
- *            workspace (page section 6.1 and Listing 1 step 1 inputs); nothing, for the
- *            plans whose walk forms these itself (ssd_plan_describe: prep=none);
+ *            workspace (page section 6.1 and Listing 1 step 1 inputs); for the plans whose
+ *            walk forms these itself (ssd_plan_describe: prep=none), the end state and
+ *            total decay of every segment but the last of a sequence walked in segments,
+ *            and each segment's entry state (section 6.2, Appendix B), or nothing
+ *            (summary=none);
  *   stage 2: the chunk walk: outputs, chunk states and state passing (section 6.1 and
  *            6.2), reading the workspace that a stage-1 call with the same problem and
  *            inputs left there.

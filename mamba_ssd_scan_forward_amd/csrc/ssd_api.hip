@@ -12,6 +12,7 @@
 #include "ssd_kernels.h"
 #include "ssd_walk_split.h"
 #include "ssd_walk_fused.h"
+#include "ssd_walk_segments.h"
 #include "ssd_backward.h"
 
 namespace {
@@ -45,6 +46,11 @@ struct Plan {
     int fused_wpg;    // its workgroups per group
     int64_t fused_items;
     void (*fused_fn)(ssd::FusedArgs);
+    int fseg, fseglen;   // the fused walker's segments per sequence (1: none) and their rows
+    size_t loc_off, dsum_off, sinit_off;   // segment end states, log decays, entry states
+    int sum_wpg;
+    int64_t sum_items;
+    void (*sum_fn)(ssd::SegSumArgs);
 };
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -128,9 +134,10 @@ walk_fn pick_walk_bf16(int PT, int NP, bool cbl) {
 // d_state 64 or 128, any chunk length (its 32-row blocks pass the state between them, so
 // the chunking does not change the result).  NW compute waves per workgroup, each holding
 // 32 columns of one head; it takes the NW that needs the fewest rounds of workgroups over
-// the compute units (a packed batch: the fewest workgroups), then leaves the fewest compute
-// waves idle, then the larger NW.  It is used when its workgroups fill at least half the
-// chip: fewer, longer walks are left to the segmented split walker.
+// the compute units times rows walked (a packed batch: the fewest workgroups), then leaves
+// the fewest compute waves idle, then the larger NW.  Sequences of one length too few to
+// fill the chip are walked in segments (ssd_walk_segments.h).  It is used when its
+// workgroups, segments counted, fill at least half the chip.
 typedef void (*fused_fn_t)(ssd::FusedArgs);
 template <int NP>
 fused_fn_t fused_instance(int nw) {
@@ -144,7 +151,8 @@ fused_fn_t fused_instance(int nw) {
 
 bool plan_fused(const ssd_problem* p, Plan* pl) {
     pl->fused = 0;
-    const int64_t P = p->headdim, N = p->dstate, H = p->nheads, G = p->ngroups;
+    pl->fseg = 1;
+    const int64_t P = p->headdim, N = p->dstate, H = p->nheads, G = p->ngroups, T = p->seqlen;
     if (p->dtype != SSD_DTYPE_BF16 || P % 32 != 0 || P < 64 || (N != 64 && N != 128)) return false;
     // 32-bit byte offsets inside one sequence's rows of X / Y, B / C and logA
     if (p->batch * p->seqlen * H * P * 2 >= ((int64_t)1 << 31) ||
@@ -152,19 +160,42 @@ bool plan_fused(const ssd_problem* p, Plan* pl) {
         return false;
     const int64_t upg = (H / G) * (P / 32);
     const bool packed = p->nseq != p->batch;
-    int best = 0;
+    // Sequences of one length (a batch, or one packed sequence) whose workgroups would not
+    // fill the chip are walked as segments (ssd_walk_segments.h): as many as bring the
+    // workgroups to one per compute unit, of at least 8 blocks (256 rows) each.
+    auto segments = [&](int64_t items, int* nseg, int* seglen) {
+        *nseg = 1;
+        *seglen = (int)T;
+        if (packed || items >= kComputeUnits) return;
+        int64_t k = kComputeUnits / items;
+        if (k > T / 256) k = T / 256;
+        if (k < 2) return;
+        const int64_t sl = ((T + k - 1) / k + 31) / 32 * 32;
+        *nseg = (int)((T + sl - 1) / sl);
+        *seglen = (int)sl;
+    };
+    int best = 0, best_seg = 1, best_sl = 0;
     int64_t best_cost = 0, best_waste = 0, best_items = 0, best_wpg = 0;
-    for (int nw = 6; nw >= 4; --nw) {
+    // (d_state 128 with six compute waves keeps only two blocks in flight: too few to
+    // cover the latency of memory when the inputs are not in the last-level cache)
+    for (int nw = N == 128 ? 5 : 6; nw >= 4; --nw) {
         const int64_t wpg = (upg + nw - 1) / nw;
         const int64_t items = p->nseq * G * wpg;
-        const int64_t cost = packed ? items : (items + kComputeUnits - 1) / kComputeUnits;
+        int nseg, sl;
+        segments(items, &nseg, &sl);
+        const int64_t eff = items * nseg;
+        // rounds of workgroups over the compute units times the rows each walks (a packed
+        // batch: the workgroups)
+        const int64_t cost = packed ? items : (eff + kComputeUnits - 1) / kComputeUnits * sl;
         const int64_t waste = items * nw - p->nseq * G * upg;
         if (!best || cost < best_cost || (cost == best_cost && waste < best_waste)) {
             best = nw;
             best_cost = cost;
             best_waste = waste;
-            best_items = items;
+            best_items = eff;
             best_wpg = wpg;
+            best_seg = nseg;
+            best_sl = sl;
         }
     }
     if (best_items < kComputeUnits / 2 || best_items > INT32_MAX / 8) return false;
@@ -172,6 +203,21 @@ bool plan_fused(const ssd_problem* p, Plan* pl) {
     pl->fused_wpg = (int)best_wpg;
     pl->fused_items = best_items;
     pl->fused_fn = N == 64 ? fused_instance<64>(best) : fused_instance<128>(best);
+    pl->fseg = best_seg;
+    pl->fseglen = best_sl;
+    size_t ws = 256;
+    if (best_seg > 1) {
+        const size_t state = (size_t)(H * P * N) * sizeof(float);
+        pl->loc_off = 0;
+        pl->dsum_off = align_up((size_t)p->nseq * (best_seg - 1) * state, 256);
+        pl->sinit_off = align_up(pl->dsum_off + (size_t)p->nseq * (best_seg - 1) * H * sizeof(float), 256);
+        ws = align_up(pl->sinit_off + (size_t)p->nseq * best_seg * state, 256);
+        pl->sum_wpg = (int)((upg + ssd::kSumUnits - 1) / ssd::kSumUnits);
+        pl->sum_items = p->nseq * (best_seg - 1) * G * pl->sum_wpg;
+        pl->sum_fn = N == 64 ? ssd::ssd_seg_summary_kernel<64> : ssd::ssd_seg_summary_kernel<128>;
+        if (pl->sum_items > INT32_MAX) return false;
+    }
+    pl->ws_bytes = ws;
     return pl->fused_fn != nullptr;
 }
 
@@ -183,7 +229,6 @@ int make_plan(const ssd_problem* p, Plan* pl, bool allow_fused = true) {
     if (allow_fused && plan_fused(p, pl)) {
         pl->npass = 1;
         pl->nseg = 1;
-        pl->ws_bytes = 256;   // (no workspace is used)
         return SSD_OK;
     }
     pl->summary = nullptr;
@@ -370,6 +415,9 @@ int ssd_plan_describe(const ssd_problem* p, char* buf, size_t len) {
     if (pl.fused) {
         snprintf(walk, sizeof walk, "ssd_walk_fused_kernel<%d, %d>", (int)p->dstate, pl.fused);
         prep = "none";
+        if (pl.fseg > 1)
+            summary = p->dstate == 64 ? "ssd_seg_summary_kernel<64>+ssd_seg_combine_kernel"
+                                      : "ssd_seg_summary_kernel<128>+ssd_seg_combine_kernel";
     } else if (pl.npass == 2) {
         snprintf(walk, sizeof walk, "ssd_walk_split_pair_kernel<128>+ssd_add_kernel<bf16>");
     } else if (pl.split) {
@@ -441,15 +489,46 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     if (pl.fused) {
-        // one launch, no workspace: stage 1 has nothing to do
-        if (!(stages & 2)) return SSD_OK;
+        // one launch and no workspace; sequences walked as segments: stage 1 is the
+        // segments' summary and their entry states, stage 2 the walk
+        const bool seg = pl.fseg > 1;
+        unsigned char* ws = static_cast<unsigned char*>(workspace);
+        float* sinit = reinterpret_cast<float*>(ws + pl.sinit_off);
+        if (seg && (stages & 1)) {
+            ssd::SegSumArgs sa;
+            sa.X = static_cast<const __bf16*>(X);
+            sa.logA = logA;
+            sa.B = static_cast<const __bf16*>(B);
+            sa.loc = reinterpret_cast<float*>(ws + pl.loc_off);
+            sa.dsum = reinterpret_cast<float*>(ws + pl.dsum_off);
+            sa.T = T;
+            sa.seglen = pl.fseglen;
+            sa.nseg = pl.fseg;
+            sa.nseq = (int)p->nseq;
+            sa.H = (int)H;
+            sa.P = (int)P;
+            sa.G = (int)G;
+            sa.xh = (int)x_heads;
+            sa.upg = (int)((H / G) * (P / 32));
+            sa.wpg = pl.sum_wpg;
+            sa.nitems = (int)pl.sum_items;
+            hipLaunchKernelGGL(pl.sum_fn, dim3((unsigned)pl.sum_items), dim3(64 * ssd::kSumUnits), 0, stream, sa);
+            const int64_t n4 = p->nseq * H * P * N / 4;
+            const int64_t cblocks = (n4 + 255) / 256 < 8192 ? (n4 + 255) / 256 : 8192;
+            hipLaunchKernelGGL(ssd::ssd_seg_combine_kernel, dim3((unsigned)cblocks), dim3(256), 0, stream,
+                               static_cast<const float*>(sa.loc), static_cast<const float*>(sa.dsum), init_state,
+                               sinit, (int)p->nseq, pl.fseg, (int)H, (int)(P * N));
+        }
+        if (!(stages & 2)) return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
         ssd::FusedArgs fa;
         fa.X = static_cast<const __bf16*>(X);
         fa.logA = logA;
         fa.B = static_cast<const __bf16*>(B);
         fa.C = static_cast<const __bf16*>(C);
-        fa.init = init_state;
-        fa.seq_offsets = seq_offsets;
+        fa.init = seg ? sinit : init_state;
+        // (a segmented plan has sequences of one length: a batch, or one packed sequence
+        // that spans the rows)
+        fa.seq_offsets = seg ? nullptr : seq_offsets;
         fa.Y = static_cast<__bf16*>(Y);
         fa.final_state = final_state;
         fa.T = T;
@@ -458,12 +537,14 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
         fa.N = (int)N;
         fa.G = (int)G;
         fa.xh = (int)x_heads;
-        fa.nseq = (int)p->nseq;
+        fa.nseq = (int)(p->nseq * pl.fseg);
         fa.upg = (int)((H / G) * (P / 32));
         fa.wpg = pl.fused_wpg;
         fa.nitems = (int)pl.fused_items;
+        fa.nseg = pl.fseg;
+        fa.seglen = pl.fseglen;
         // packed sequences: (sequence, group) units dealt to the XCDs longest first
-        fa.lpt = (seq_offsets && p->nseq <= 64) ? 1 : 0;
+        fa.lpt = (!seg && seq_offsets && p->nseq <= 64) ? 1 : 0;
         int64_t grid = pl.fused_items;
         if (fa.lpt) grid = ((p->nseq * G + 7) / 8) * 8 * pl.fused_wpg;
         hipLaunchKernelGGL(pl.fused_fn, dim3((unsigned)grid), dim3(64 * (pl.fused + 3)), 0, stream, fa);

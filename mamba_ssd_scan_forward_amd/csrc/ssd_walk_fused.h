@@ -72,6 +72,9 @@ struct FusedArgs {
     int wpg;        // workgroups per group: ceil(upg / NW)
     int nitems;     // nseq G wpg
     int lpt;        // packed sequences dealt to XCDs longest first
+    int nseg;       // > 1: every sequence walked as nseg segments of seglen rows, each a
+    int seglen;     // sequence of its own (nseq counts the segments); init then holds every
+                    // segment's entry state, and only the last segment writes a final state
 };
 
 // LDS of the fused walker.  Ring slot: X [32][NW][32] (the block's rows of the units side by side), B and C
@@ -155,6 +158,16 @@ __device__ __forceinline__ void lds_read8x16(const uint32_t (&ad)[8], bf16x8 (&r
         : "memory");
 }
 __device__ __forceinline__ uint32_t lds_addr(lds_ptr p) { return (uint32_t)(uintptr_t)p; }
+// One 4-byte LDS read in an asm block that waits for it (the same reason as above).
+__device__ __forceinline__ float lds_read4(lds_ptr p) {
+    float r;
+    asm volatile("ds_read_b32 %0, %1\n"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(r)
+                 : "v"(lds_addr(p))
+                 : "memory");
+    return r;
+}
 __device__ __forceinline__ bf16x8 cat44(bf16x4 lo, bf16x4 hi) {
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
@@ -232,7 +245,13 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
 
     int64_t row0;
     int len;
-    if (!a.seq_offsets) {
+    int64_t sfin = s;   // slot of the final state (-1: none)
+    if (a.nseg > 1) {
+        const int b = s / a.nseg, sg = s % a.nseg;
+        row0 = (int64_t)b * a.T + (int64_t)sg * a.seglen;
+        len = (int)min((int64_t)a.seglen, a.T - (int64_t)sg * a.seglen);
+        sfin = sg == a.nseg - 1 ? b : -1;
+    } else if (!a.seq_offsets) {
         row0 = (int64_t)s * a.T;
         len = (int)a.T;
     } else {
@@ -682,7 +701,8 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
     }
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_s_barrier();
-    if (a.final_state && valid) {
+    if (a.final_state && valid && sfin >= 0) {
+        const int64_t fin_base = (sfin * H + h) * (int64_t)P * NP;
         const float fs = fast_exp2(ldsv<float>(pbuf(0) + L::f + 4 * jh));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
@@ -690,7 +710,7 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
             for (int q4 = 0; q4 < 4; ++q4) {
                 const f32x4 o = {gs[nt][4 * q4] * fs, gs[nt][4 * q4 + 1] * fs, gs[nt][4 * q4 + 2] * fs,
                                  gs[nt][4 * q4 + 3] * fs};
-                *reinterpret_cast<f32x4*>(a.final_state + state_base + (int64_t)(c0 + lr) * NP + 32 * nt + 8 * q4 +
+                *reinterpret_cast<f32x4*>(a.final_state + fin_base + (int64_t)(c0 + lr) * NP + 32 * nt + 8 * q4 +
                                           4 * lg) = o;
             }
     }

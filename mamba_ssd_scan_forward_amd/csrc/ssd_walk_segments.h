@@ -1,0 +1,248 @@
+// ssd_walk_segments.h -- one long sequence walked as segments in parallel (page
+// "Transformers are SSMs" paper summary, section 6.2 and Appendix B: the state passed
+// between consecutive pieces of the sequence is a linear recurrence over the pieces, so
+// each piece's contribution can be formed on its own and the pieces chained afterwards).
+//
+// A sequence too long for the chip to be filled by its (group, run of head columns)
+// workgroups is cut into nseg segments of seglen rows.  Three launches:
+//   summary  every segment but the last, from a zero state: its end state
+//                loc_s = sum_t exp(L_{t+1..end}) x_t B_t^T     (L: the sum of logA)
+//            and its total log decay D_s = sum_t logA_t;
+//   combine  the entry state of every segment, h_0 = the sequence's initial state (or 0),
+//                h_{s+1} = exp(D_s) h_s + loc_s;
+//   walk     the fused walker with every segment a sequence of its own, entering with
+//            h_s; the last segment's final state is the sequence's.
+// The summary is a plain contraction over the segment's rows: each row is weighted by its
+// decay to the segment's end (a suffix sum of logA, at most 1 in size), so there is no
+// running scale to keep, and it reads X and B once.
+#pragma once
+
+#include "ssd_walk_fused.h"
+
+namespace ssd {
+
+struct SegSumArgs {
+    const __bf16* X;
+    const float* logA;
+    const __bf16* B;
+    float* loc;     // [nseq][nseg - 1][H][P][N] float32
+    float* dsum;    // [nseq][nseg - 1][H] float32 (natural log)
+    int64_t T;      // rows per sequence
+    int seglen, nseg, nseq;
+    int H, P, G, xh;
+    int upg;        // 32-column units per group: (H / G) (P / 32)
+    int wpg;        // summary workgroups per group: ceil(upg / kSumUnits)
+    int nitems;     // nseq (nseg - 1) G wpg
+};
+
+constexpr int kSumUnits = 2;   // units per summary workgroup, one wave each
+
+// One workgroup per (sequence, segment but the last, group, run of kSumUnits units): the
+// segment's 32-row blocks from the last to the first, each block's B rows, X rows and logA
+// brought straight from global memory into a ring of four LDS slots three blocks ahead
+// (wave 0 loads B, wave 1 X and logA), then per unit
+//     g^T += B^T X~,   X~_t = exp(L_{t+1..end}) X_t
+// on MFMA with the operand layouts of the fused walker (B rows swizzled by fused_swz,
+// X read with 4-row transposing reads, rows of the contraction in the sigma order).
+template <int NP>
+__global__ void __launch_bounds__(64 * kSumUnits) ssd_seg_summary_kernel(SegSumArgs a) {
+    typedef Elem<__bf16> E;
+    static_assert(kSumUnits == 2, "one wave loads B, the other X and logA");
+    constexpr int NT = NP / 32;
+    constexpr int UPR = NP / 8;             // 16-byte units of a B row
+    constexpr int RPL = 64 / UPR;           // B rows per 1 KB load
+    constexpr int NBL = NP / 16;            // 1 KB loads of B per block
+    constexpr int XR = kSumUnits * 64;      // bytes per row of the X slot
+    constexpr int NXL = 32 * XR / 1024;     // 1 KB loads of X per block
+    constexpr int NSL = 4, D = NSL - 1;     // ring slots, blocks in flight
+    constexpr int L0 = NBL, L1 = NXL + 1;   // loads per block of wave 0 / wave 1
+    static_assert(D * L0 < 64 && D * L1 < 64, "vmcnt range");
+    // (separate arrays per slot, so that the compiler can tell the slot being read from the
+    // slots still being filled by direct-to-LDS loads; selected by constant index)
+    __shared__ __align__(16) unsigned char b0[32 * NP * 2], b1[32 * NP * 2], b2[32 * NP * 2], b3[32 * NP * 2];
+    __shared__ __align__(16) unsigned char x0[32 * XR], x1[32 * XR], x2[32 * XR], x3[32 * XR];
+    __shared__ __align__(16) unsigned char l0[256], l1[256], l2[256], l3[256];   // logA, [2 heads][32]
+    __shared__ __align__(16) unsigned char wsm[kSumUnits * 128];   // row weights, [unit][32] float
+    auto pick = [](int k, unsigned char* a0, unsigned char* a1, unsigned char* a2, unsigned char* a3)
+                    __attribute__((always_inline)) -> lds_ptr {
+        return k == 0 ? (lds_ptr)a0 : k == 1 ? (lds_ptr)a1 : k == 2 ? (lds_ptr)a2 : (lds_ptr)a3;
+    };
+    auto BS = [&](int k) __attribute__((always_inline)) { return pick(k, b0, b1, b2, b3); };
+    auto XS = [&](int k) __attribute__((always_inline)) { return pick(k, x0, x1, x2, x3); };
+    auto LS = [&](int k) __attribute__((always_inline)) { return pick(k, l0, l1, l2, l3); };
+
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int item = blockIdx.x;
+    if (item >= a.nitems) return;
+    const int H = a.H, P = a.P, G = a.G, hpg = H / G, uph = P / 32;
+    const int q = item % a.wpg;
+    int rest = item / a.wpg;
+    const int g = rest % G;
+    rest /= G;
+    const int sg = rest % (a.nseg - 1), b = rest / (a.nseg - 1);
+    const int64_t row0 = (int64_t)b * a.T + (int64_t)sg * a.seglen;
+    const int nblk = a.seglen / 32;
+    const int u0 = q * kSumUnits;
+    const int64_t xrx = (int64_t)a.xh * P;
+    const int hrep = H / a.xh;
+    // the heads of the workgroup's two units (clamped to the group's last unit)
+    const int ua = min(u0, a.upg - 1), ub = min(u0 + 1, a.upg - 1);
+    const int ha = g * hpg + ua / uph, hb = g * hpg + ub / uph;
+
+    // ---- loads: lane i of B load k fills position i % UPR of row k RPL + i / UPR (global
+    // unit position ^ swizzle); lane i of X load j piece 64 j + i of the [32][units] rows;
+    // lane i of the logA load row i % 32 of head a (i < 32) or b
+    const rsrc_t br = make_rsrc(a.B + row0 * G * NP + g * NP, (uint32_t)((int64_t)a.seglen * G * NP * 2));
+    const rsrc_t xr = make_rsrc(a.X + row0 * xrx, (uint32_t)((int64_t)a.seglen * xrx * 2));
+    const rsrc_t lar = make_rsrc(a.logA + row0 * H, (uint32_t)((int64_t)a.seglen * H * 4));
+    uint32_t off[NBL > NXL ? NBL : NXL];
+    uint32_t loff = 0;
+    if (wave == 0) {
+        const int brow = lane / UPR, bpos = lane % UPR;
+#pragma unroll
+        for (int k = 0; k < NBL; ++k) {
+            const int r = k * RPL + brow;
+            off[k] = (uint32_t)((r * G * NP + 8 * (bpos ^ fused_swz<NP>(r))) * 2);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < NXL; ++j) {
+            const int pc = 64 * j + lane, r = pc / (4 * kSumUnits), piece = pc % (4 * kSumUnits);
+            const int u = min(u0 + piece / 4, a.upg - 1);
+            const int h = g * hpg + u / uph, c0 = 32 * (u % uph);
+            off[j] = (uint32_t)((r * xrx + (int64_t)(h / hrep) * P + c0 + 8 * (piece % 4)) * 2);
+        }
+        loff = (uint32_t)((lr * H + (lg ? hb : ha)) * 4);
+    }
+    const uint32_t bb32 = (uint32_t)(32 * G * NP * 2), xb32 = (uint32_t)(32 * xrx * 2), lb32 = (uint32_t)(32 * H * 4);
+    // block t of the walk is block nblk - 1 - t of the segment (past the first: the first
+    // again, so that every step issues the same loads and the wait counts stay exact)
+    auto issue = [&](int t, auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
+        const uint32_t blk = (uint32_t)max(nblk - 1 - t, 0);
+        if (wave == 0) {
+#pragma unroll
+            for (int i = 0; i < NBL; ++i) fused_lds16(br, BS(k) + 1024 * i, opaque(off[i]), blk * bb32);
+        } else {
+#pragma unroll
+            for (int j = 0; j < NXL; ++j) fused_lds16(xr, XS(k) + 1024 * j, opaque(off[j]), blk * xb32);
+            fused_lds4(lar, LS(k), opaque(loff), blk * lb32);
+        }
+    };
+
+    // this wave's unit
+    const int u = u0 + wave;
+    const bool valid = u < a.upg;
+    const int uc = valid ? u : a.upg - 1;
+    const int h = g * hpg + uc / uph, c0 = 32 * (uc % uph);
+    const int hsel = wave == 0 ? 0 : 1;   // its head's row of the logA slot (a or b)
+
+    // operand addresses (as in the fused walker, one X slot row of kSumUnits units)
+    const int xa0 = wave * 64 + XR * (4 * lg + ((lane & 15) >> 2)) + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    int ba[NT][2][2];
+    {
+        const int rb4 = 4 * lg + ((lane & 15) >> 2);
+        const int v = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int bnt = 2 * rb4 * NP + 8 * (lane & 1) + 16 * ((4 * nt) ^ (fused_swz<NP>(rb4) & ~3));
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    ba[nt][ks][j] = bnt + 16 * (v ^ (fused_swz<NP>(16 * ks + 8 * j + rb4) & 3)) + 32 * NP * ks + 16 * NP * j;
+        }
+    }
+
+    f32x16 gs[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) gs[nt] = f32x16{};
+    float carry = 0.f;   // sum of logA over the rows after this block, within the segment
+    issue(0, std::integral_constant<int, 0>{});
+    issue(1, std::integral_constant<int, 1>{});
+    issue(2, std::integral_constant<int, 2>{});
+    auto step = [&](int t, auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
+        // this wave's loads of block t are in (the two blocks after it still in flight), and
+        // after the barrier every wave's are; every wave has also finished block t - 1, whose
+        // slot the next issue reuses
+        // (a bare barrier: __syncthreads would also wait for every load in flight)
+        if (wave == 0) fused_wait_vm<(D - 1) * L0>();
+        else fused_wait_vm<(D - 1) * L1>();
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        issue(t + D, std::integral_constant<int, (k + D) % NSL>{});
+        const lds_ptr bsl = BS(k), xsl = XS(k);
+        // the block's B^T operands first: their reads overlap the weights' computation
+        bf16x8 bt[NT][2];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) bt[nt][ks] = cat44(tr4(bsl + ba[nt][ks][0]), tr4(bsl + ba[nt][ks][1]));
+        // row weights of this wave's head: exp of the logA sum over the later rows
+        const float c = scan32(lds_read4(LS(k) + 4 * (32 * hsel + lr)));   // inclusive
+        const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c), 31));
+        const float w = fast_exp2((tot - c + carry) * kLog2e);
+        if (lg == 0) ldsw<float>((lds_ptr)wsm + 128 * wave + 4 * lr, w);
+        carry += tot;
+        // X of the block (K-step ks: rows 16 ks + sigma(8 lg + q)) and its weights
+        bf16x8 xt[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8 xf = cat44(tr4(xsl + xa0 + 16 * XR * ks), tr4(xsl + xa0 + 16 * XR * ks + 8 * XR));
+            const f32x4 w0 = ldsv<f32x4>((lds_ptr)wsm + 128 * wave + 4 * (16 * ks + 4 * lg));
+            const f32x4 w1 = ldsv<f32x4>((lds_ptr)wsm + 128 * wave + 4 * (16 * ks + 8 + 4 * lg));
+            const float ws[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+#pragma unroll
+            for (int q8 = 0; q8 < 8; ++q8) xt[ks][q8] = (__bf16)((float)xf[q8] * ws[q8]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) gs[nt] = E::mma(gs[nt], bt[nt][ks], xt[ks]);
+    };
+    for (int t = 0; t < nblk; t += NSL) {
+        step(t, std::integral_constant<int, 0>{});
+        if (t + 1 < nblk) step(t + 1, std::integral_constant<int, 1>{});
+        if (t + 2 < nblk) step(t + 2, std::integral_constant<int, 2>{});
+        if (t + 3 < nblk) step(t + 3, std::integral_constant<int, 3>{});
+    }
+    // no load may still be landing in LDS when the workgroup ends
+    fused_wait_vm<0>();
+    if (!valid) return;
+    const int64_t slot = ((int64_t)b * (a.nseg - 1) + sg) * H + h;
+    float* o = a.loc + slot * (int64_t)P * NP;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 v = {gs[nt][4 * q4], gs[nt][4 * q4 + 1], gs[nt][4 * q4 + 2], gs[nt][4 * q4 + 3]};
+            *reinterpret_cast<f32x4*>(o + (int64_t)(c0 + lr) * NP + 32 * nt + 8 * q4 + 4 * lg) = v;
+        }
+    if (c0 == 0 && lane == 0) a.dsum[slot] = carry;
+}
+
+// Entry states of the segments: h_0 = init (or 0), h_{s+1} = exp(D_s) h_s + loc_s, for
+// every (sequence, head) and 4 consecutive state elements per thread.
+__global__ void __launch_bounds__(256) ssd_seg_combine_kernel(const float* loc, const float* dsum, const float* init,
+                                                              float* seg_init, int nseq, int nseg, int H, int PN) {
+    const int n4 = PN / 4;
+    const int64_t total = (int64_t)nseq * H * n4;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+        const int e4 = (int)(i % n4);
+        const int64_t bh = i / n4;
+        const int h = (int)(bh % H), b = (int)(bh / H);
+        f32x4 v = init ? *reinterpret_cast<const f32x4*>(init + bh * PN + 4 * e4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4*>(seg_init + (((int64_t)b * nseg) * H + h) * PN + 4 * e4) = v;
+        for (int s = 0; s + 1 < nseg; ++s) {
+            const int64_t slot = ((int64_t)b * (nseg - 1) + s) * H + h;
+            const float d = fast_exp2(dsum[slot] * kLog2e);
+            const f32x4 l = *reinterpret_cast<const f32x4*>(loc + slot * PN + 4 * e4);
+            v = f32x4{d * v[0] + l[0], d * v[1] + l[1], d * v[2] + l[2], d * v[3] + l[3]};
+            *reinterpret_cast<f32x4*>(seg_init + (((int64_t)b * nseg + s + 1) * H + h) * PN + 4 * e4) = v;
+        }
+    }
+}
+
+}  // namespace ssd

@@ -351,3 +351,40 @@ def test_library_loaded_before_the_first_gpu_use():
             "print('ok', float(Y.abs().max()))\n") % os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=100)
     assert res.returncode == 0 and "ok" in res.stdout, res.stdout + res.stderr
+
+
+# Sequences walked as segments by the fused walker (a summary of every segment but the
+# last, their entry states chained, then every segment walked on its own): ragged lengths
+# (a short last segment and a ragged last block) with initial states, one and several
+# groups, d_state 64 and 128, head dimension 128, a batch of two, strong decay (blocks
+# that renormalise or take the exact form inside segments), and one packed sequence given
+# through seq_offsets.
+@pytest.mark.parametrize("case", ["n128_init", "groups2", "n64_batch2", "groups3", "p128", "strong_decay",
+                                  "a_one", "a_zero", "packed_one"])
+def test_segmented_fused_walk(case):
+    if case == "n128_init":
+        inp = make_inputs(1, 8292, 16, 64, 128, 1, "bf16", seed=1500, init_state=True)
+    elif case == "groups2":
+        inp = make_inputs(1, 8292, 16, 64, 128, 2, "bf16", seed=1501, init_state=True)
+    elif case == "n64_batch2":
+        inp = make_inputs(2, 4160, 16, 64, 64, 1, "bf16", seed=1502, init_state=True)
+    elif case == "groups3":
+        inp = make_inputs(1, 6000, 24, 64, 128, 3, "bf16", seed=1503, init_state=False)
+    elif case == "p128":
+        inp = make_inputs(1, 9000, 8, 128, 128, 1, "bf16", seed=1504, init_state=True)
+    elif case == "strong_decay":
+        inp = make_inputs(1, 8292, 16, 64, 128, 1, "bf16", seed=1505, init_state=True)
+        inp.logA = (inp.logA * 40.0).astype(np.float32)
+    elif case == "a_one":
+        # no decay: every segment's summary weights are 1 and its total decay exp(0)
+        inp = make_inputs(1, 8292, 16, 64, 128, 1, "bf16", seed=1507, init_state=True)
+        inp.logA[:] = 0.0
+    elif case == "a_zero":
+        # total decay: every state is forgotten at once (weights and totals underflow to 0)
+        inp = make_inputs(1, 8292, 16, 64, 64, 1, "bf16", seed=1508, init_state=True)
+        inp.logA[:] = -1e4
+    else:
+        inp = make_inputs(1, 8292, 16, 64, 128, 1, "bf16", seed=1506, init_state=True, seq_lengths=[8292])
+    plan = plan_of(inp, 256)
+    assert plan["walk"].startswith("ssd_walk_fused_kernel") and plan["summary"].startswith("ssd_seg_summary"), plan
+    check(inp, 256, case)
