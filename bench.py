@@ -57,7 +57,7 @@ def log(*a):
 # the sources of the forward kernels and of their launch plan (the backward pass's files
 # are not among them)
 FORWARD_SOURCES = ("ssd_device.h", "ssd_kernels.h", "ssd_walk_split.h", "ssd_walk_fused.h",
-                   "ssd_api.hip")
+                   "ssd_walk_segments.h", "ssd_api.hip")
 
 
 def kernel_source_hash():

@@ -141,19 +141,29 @@ walk_fn pick_walk_bf16(int PT, int NP, bool cbl) {
 typedef void (*fused_fn_t)(ssd::FusedArgs);
 template <int NP>
 fused_fn_t fused_instance(int nw) {
-    switch (nw) {
-        case 4: return ssd::ssd_walk_fused_kernel<NP, 4>;
-        case 5: return ssd::ssd_walk_fused_kernel<NP, 5>;
-        case 6: return ssd::ssd_walk_fused_kernel<NP, 6>;
+    if constexpr (NP == 256) {
+        // (the state of a d_state 256 column takes 128 registers a lane and the B and C rows
+        // of a block 32 KB: two or three compute waves)
+        switch (nw) {
+            case 2: return ssd::ssd_walk_fused_kernel<256, 2>;
+            case 3: return ssd::ssd_walk_fused_kernel<256, 3>;
+        }
+        return nullptr;
+    } else {
+        switch (nw) {
+            case 4: return ssd::ssd_walk_fused_kernel<NP, 4>;
+            case 5: return ssd::ssd_walk_fused_kernel<NP, 5>;
+            case 6: return ssd::ssd_walk_fused_kernel<NP, 6>;
+        }
+        return nullptr;
     }
-    return nullptr;
 }
 
 bool plan_fused(const ssd_problem* p, Plan* pl) {
     pl->fused = 0;
     pl->fseg = 1;
     const int64_t P = p->headdim, N = p->dstate, H = p->nheads, G = p->ngroups, T = p->seqlen;
-    if (p->dtype != SSD_DTYPE_BF16 || P % 32 != 0 || P < 64 || (N != 64 && N != 128)) return false;
+    if (p->dtype != SSD_DTYPE_BF16 || P % 32 != 0 || P < 64 || (N != 64 && N != 128 && N != 256)) return false;
     // 32-bit byte offsets inside one sequence's rows of X / Y, B / C and logA
     if (p->batch * p->seqlen * H * P * 2 >= ((int64_t)1 << 31) ||
         p->batch * p->seqlen * G * N * 2 >= ((int64_t)1 << 31))
@@ -178,7 +188,8 @@ bool plan_fused(const ssd_problem* p, Plan* pl) {
     int64_t best_cost = 0, best_waste = 0, best_items = 0, best_wpg = 0;
     // (d_state 128 with six compute waves keeps only two blocks in flight: too few to
     // cover the latency of memory when the inputs are not in the last-level cache)
-    for (int nw = N == 128 ? 5 : 6; nw >= 4; --nw) {
+    const int nw_hi = N == 256 ? 3 : N == 128 ? 5 : 6, nw_lo = N == 256 ? 2 : 4;
+    for (int nw = nw_hi; nw >= nw_lo; --nw) {
         const int64_t wpg = (upg + nw - 1) / nw;
         const int64_t items = p->nseq * G * wpg;
         int nseg, sl;
@@ -199,10 +210,14 @@ bool plan_fused(const ssd_problem* p, Plan* pl) {
         }
     }
     if (best_items < kComputeUnits / 2 || best_items > INT32_MAX / 8) return false;
+    // d_state 256 only where the workgroups fill the chip without segments: its summary
+    // plus the walk of the segments takes longer than the two passes over the column
+    // halves of the state (ssd_walk_split_pair_kernel and the add)
+    if (N == 256 && best_seg > 1) return false;
     pl->fused = best;
     pl->fused_wpg = (int)best_wpg;
     pl->fused_items = best_items;
-    pl->fused_fn = N == 64 ? fused_instance<64>(best) : fused_instance<128>(best);
+    pl->fused_fn = N == 64 ? fused_instance<64>(best) : N == 128 ? fused_instance<128>(best) : fused_instance<256>(best);
     pl->fseg = best_seg;
     pl->fseglen = best_sl;
     size_t ws = 256;

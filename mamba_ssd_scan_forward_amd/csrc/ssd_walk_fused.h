@@ -136,6 +136,7 @@ __device__ __forceinline__ void fused_wait_vm() {
 __device__ __forceinline__ bf16x4 tr4(lds_ptr p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SSD_LDS bf16x4*)p);
 }
+__device__ __forceinline__ uint32_t lds_addr(lds_ptr p) { return (uint32_t)(uintptr_t)p; }
 // Eight 16-byte LDS reads in one asm block that also waits for them.  The BC-loader reads
 // its slot's B and C rows this way: with each ring one array, the compiler's bookkeeping of
 // the wave's direct-to-LDS loads could not tell the slot being read from the slots still
@@ -157,7 +158,19 @@ __device__ __forceinline__ void lds_read8x16(const uint32_t (&ad)[8], bf16x8 (&r
         : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7])
         : "memory");
 }
-__device__ __forceinline__ uint32_t lds_addr(lds_ptr p) { return (uint32_t)(uintptr_t)p; }
+// Four 4-row transposing LDS reads (ds_read_b64_tr_b16) in an asm block that waits for
+// them (the same reason as above).
+__device__ __forceinline__ void lds_tr4x4(lds_ptr p0, lds_ptr p1, lds_ptr p2, lds_ptr p3, bf16x4 (&r)[4]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4\n"
+        "ds_read_b64_tr_b16 %1, %5\n"
+        "ds_read_b64_tr_b16 %2, %6\n"
+        "ds_read_b64_tr_b16 %3, %7\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(lds_addr(p0)), "v"(lds_addr(p1)), "v"(lds_addr(p2)), "v"(lds_addr(p3))
+        : "memory");
+}
 // One 4-byte LDS read in an asm block that waits for it (the same reason as above).
 __device__ __forceinline__ float lds_read4(lds_ptr p) {
     float r;
@@ -232,7 +245,15 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
     constexpr int NPAIR = (NHL + 1) / 2;
     constexpr int LX = 2 * NW + NPAIR;     // X-loader loads per block
     constexpr int LB = 2 * NBL + NPAIR;    // BC-loader loads per block
-    static_assert(D * LX < 64 && D * LB < 64, "vmcnt range");
+    // (a wave's wait counts must fit the 6-bit counter; more loads in flight than that
+    // stall at issue until the oldest complete)
+    static_assert((D - 1) * LX < 64 && (D - 1) * LB < 64, "vmcnt range");
+    // Units XS0 .. NW - 1 get X~ = w X from the X-loader, in place in the slot; the others
+    // form it themselves.  With two compute waves the X-loader has a SIMD of its own and
+    // scales both units; with more it shares a SIMD with a compute wave or the BC-loader,
+    // and the compute waves scale their own.
+    constexpr int XS0 = NW == 2 ? 0 : NW;
+    constexpr int XSP = (NW - XS0) * 2;   // pieces per X-loader lane
 
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -329,6 +350,19 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
             ll[p] = (uint32_t)((lr * H + g * hpg + hl) * 4);
         }
         const uint32_t rb32 = (uint32_t)(32 * xrx * 2), lab32 = (uint32_t)(32 * H * 4);
+        // for the scaling in place: lane's piece j is 16-byte piece q % 4 of row (q % 128) / 4
+        // of unit XS0 + q / 128, q = 64 j + lane; its head (local index), its byte offset in
+        // the slot and the position of its row factor w in the products
+        int xj[XSP > 0 ? XSP : 1];
+        uint32_t xo[XSP > 0 ? XSP : 1], xw[XSP > 0 ? XSP : 1];
+#pragma unroll
+        for (int j = 0; j < XSP; ++j) {
+            const int q = 64 * j + lane, unit = XS0 + q / 128, row = (q % 128) / 4;
+            const int u = min(u0 + unit, a.upg - 1);
+            xj[j] = u / uph - hfirst;
+            xo[j] = (uint32_t)(row * NW * 64 + unit * 64 + 16 * (q % 4));
+            xw[j] = (uint32_t)(L::w + 4 * (32 * xj[j] + sigma_pos(row)));
+        }
         auto issue = [&](int b, auto kc) __attribute__((always_inline)) {
             constexpr int k = decltype(kc)::value;
             b = min(b, nb - 1);
@@ -344,6 +378,7 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
             constexpr int k = decltype(kc)::value;
             lds_ptr pb = pbuf(b);
             const lds_ptr la = LA(k);
+            uint32_t steep_heads = 0;   // bit jh: head jh takes the exact form
 #pragma unroll
             for (int p = 0; p < NPAIR; ++p) {
                 const int jh = 2 * p + lg;
@@ -360,6 +395,8 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
                 const float r = fast_exp2(steep ? c + ls : c - e + lnew);
                 const float f = fast_exp2(ls + e);
                 lsig[p] = lnew;
+                const uint64_t sb = __ballot(steep);
+                steep_heads |= (uint32_t)(sb & 1) << (2 * p) | (uint32_t)((sb >> 32) & 1) << (2 * p + 1);
                 if (jh < NHL) {
                     ldsw<float>(pb + L::w + 4 * (32 * jh + sigma_pos(lr)), w);
                     ldsw<float>(pb + L::r + 4 * (32 * jh + lr), r);
@@ -369,6 +406,24 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
                         ldsw<int>(pb + L::fl + 4 * jh, steep ? 2 : renorm ? 1 : 0);
                     }
                 }
+            }
+            // X~ = w X in place, rounded to bf16 as the products read it; the rows of
+            // heads that take the exact form stay unscaled (that form needs X itself)
+            const lds_ptr xs = XS(k);
+            u32x4 xv[XSP > 0 ? XSP : 1];
+            float wv[XSP > 0 ? XSP : 1];
+#pragma unroll
+            for (int j = 0; j < XSP; ++j) {
+                xv[j] = ldsv<u32x4>(xs + xo[j]);
+                wv[j] = ldsv<float>(pb + xw[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < XSP; ++j) {
+                const float wj = (steep_heads >> xj[j]) & 1 ? 1.f : wv[j];
+                bf16x8 v = __builtin_bit_cast(bf16x8, xv[j]);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) v[q] = (__bf16)((float)v[q] * wj);
+                ldsw<u32x4>(xs + xo[j], __builtin_bit_cast(u32x4, v));
             }
         };
         loader_loop(issue, products, [&]() __attribute__((always_inline)) { fused_wait_vm<(D - 1) * LX>(); });
@@ -461,38 +516,31 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
             // every fragment is read before the first product (one LDS round trip, not one per
             // K-step)
             const lds_ptr bsl = BS(k), csl = CS(k);
-            constexpr int NK = NP / 16;
-            bf16x8 bfr[NK], cfr[NK];
-            {
-                uint32_t ad[2 * NK];
+            // (in passes of at most four K-step pairs: eight reads of B and C each)
+            constexpr int NK = NP / 16, KP = NK < 8 ? NK : 8;
+            f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
-                for (int kk = 0; kk < NK; ++kk) {
-                    const int o = 2 * (lr * NP + 8 * ((2 * kk + lg) ^ fused_swz<NP>(lr)));
-                    ad[kk] = lds_addr(bsl + o);
-                    ad[NK + kk] = lds_addr(csl + o);
-                }
-                bf16x8 r[2 * NK];
+            for (int k0 = 0; k0 < NK; k0 += KP) {
+                bf16x8 r[2 * KP];
 #pragma unroll
-                for (int c = 0; c < 2 * NK; c += 8) {
+                for (int c = 0; c < 2 * KP; c += 8) {
                     uint32_t a8[8];
                     bf16x8 r8[8];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) a8[i] = ad[c + i];
+                    for (int i = 0; i < 8; ++i) {
+                        const int kk = k0 + (c + i) % KP;
+                        const int o = 2 * (lr * NP + 8 * ((2 * kk + lg) ^ fused_swz<NP>(lr)));
+                        a8[i] = lds_addr(((c + i) < KP ? bsl : csl) + o);
+                    }
                     lds_read8x16(a8, r8);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) r[c + i] = r8[i];
                 }
 #pragma unroll
-                for (int kk = 0; kk < NK; ++kk) {
-                    bfr[kk] = r[kk];
-                    cfr[kk] = r[NK + kk];
+                for (int kk = 0; kk < KP; kk += 2) {
+                    acc0 = E::mma(acc0, r[kk], r[KP + kk]);
+                    acc1 = E::mma(acc1, r[kk + 1], r[KP + kk + 1]);
                 }
-            }
-            f32x16 acc0 = f32x16{}, acc1 = f32x16{};
-#pragma unroll
-            for (int kk = 0; kk < NP / 16; kk += 2) {
-                acc0 = E::mma(acc0, bfr[kk], cfr[kk]);
-                acc1 = E::mma(acc1, bfr[kk + 1], cfr[kk + 1]);
             }
             // causal mask (s <= l) and the fragments (K-step ks = elements 8 ks .. 8 ks + 7)
 #pragma unroll
@@ -575,27 +623,41 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
     // and one per 16-byte unit inside it.
     constexpr int XR = NW * 64;   // bytes per row of the X slot
     const int xa0 = ci * 64 + XR * (4 * lg + ((lane & 15) >> 2)) + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
-    // Per-lane LDS addresses of every operand read in slot 0, computed once: slot k is
-    // k bcbytes further on, so each read is one register plus an immediate offset.
-    lds_ptr ca[NT][4];      // C pieces of row lr: n tile nt, piece m = 2 kk + j
-    lds_ptr ba[NT][2][2];   // B^T transposing reads: n tile nt, K-step, 4-row half
-    {
-        const int sa = fused_swz<NP>(lr);
-        const int rb = 4 * lg + ((lane & 15) >> 2);   // row of the transposing read, K-step 0, half 0
-        const int v = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    // Per-lane LDS addresses of every operand read in slot 0: slot k is k bcbytes further
+    // on, so each read is one register plus an immediate offset.  Kept in registers for up
+    // to four n tiles (32 of them).  Beyond that each read's address is formed from one of
+    // eight per-lane offsets of n tile 0: the tile part of the swizzle, 64 (nt ^ a), sits in
+    // bits of its own (above the 16-byte unit, below the row), so n tile nt is that offset
+    // XOR 64 nt, one instruction a read.
+    const int sa = fused_swz<NP>(lr);
+    const int rb = 4 * lg + ((lane & 15) >> 2);   // row of the transposing read, K-step 0, half 0
+    const int vb = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    auto coff = [&](int m) __attribute__((always_inline)) -> uint32_t {
+        return (uint32_t)(2 * lr * NP + 8 * lg + 16 * (sa & ~3) + 16 * (m ^ (sa & 3)));
+    };
+    auto boff = [&](int ks, int j) __attribute__((always_inline)) -> uint32_t {
+        return (uint32_t)(2 * rb * NP + 8 * (lane & 1) + 16 * (fused_swz<NP>(rb) & ~3) +
+                          16 * (vb ^ (fused_swz<NP>(16 * ks + 8 * j + rb) & 3)) + 32 * NP * ks + 16 * NP * j);
+    };
+    constexpr bool kept = NT <= 4;           // every n tile's addresses in registers
+    constexpr int NTK = kept ? NT : 1;
+    lds_ptr ca[NTK][4];      // C pieces of row lr: n tile nt, piece m = 2 kk + j
+    lds_ptr ba[NTK][2][2];   // B^T transposing reads: n tile nt, K-step, 4-row half
+    uint32_t co[4], bo[2][2];   // (beyond four n tiles) the offsets of n tile 0
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const int cnt = 2 * lr * NP + 8 * lg + 16 * ((4 * nt) ^ (sa & ~3));
-            const int bnt = 2 * rb * NP + 8 * (lane & 1) + 16 * ((4 * nt) ^ (fused_swz<NP>(rb) & ~3));
+    for (int m = 0; m < 4; ++m) co[m] = coff(m);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) ca[nt][m] = CS(0) + cnt + 16 * (m ^ (sa & 3));
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
+        for (int j = 0; j < 2; ++j) bo[ks][j] = boff(ks, j);
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    ba[nt][ks][j] = BS(0) + bnt + 16 * (v ^ (fused_swz<NP>(16 * ks + 8 * j + rb) & 3)) + 32 * NP * ks +
-                                    16 * NP * j;
-        }
+    for (int nt = 0; nt < NTK; ++nt) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) ca[nt][m] = CS(0) + (co[m] ^ (64 * nt));
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) ba[nt][ks][j] = BS(0) + (bo[ks][j] ^ (64 * nt));
     }
     // (rows 16 ks + 8 j + rb have rb's part 4 (r % U4) of the swizzle, U4 dividing 8; only the
     // low two bits, (r / U4) % 4, change with ks and j)
@@ -611,18 +673,24 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
             xf[ks] = cat44(tr4(xsl + xa0 + 16 * XR * ks), tr4(xsl + xa0 + 16 * XR * ks + 8 * XR));
-        const lds_ptr wp = pb + L::w + 128 * jh + 32 * lg;
-        const f32x4 w00 = ldsv<f32x4>(wp), w01 = ldsv<f32x4>(wp + 16), w10 = ldsv<f32x4>(wp + 64), w11 = ldsv<f32x4>(wp + 80);
-        const float rl = ldsv<float>(pb + L::r + 4 * (32 * jh + lr));
         const int flag = __builtin_amdgcn_readfirstlane(ldsv<int>(pb + L::fl + 4 * jh));
         const float f = ldsv<float>(pb + L::f + 4 * jh);
-        const float ws[2][8] = {{w00[0], w00[1], w00[2], w00[3], w01[0], w01[1], w01[2], w01[3]},
-                                {w10[0], w10[1], w10[2], w10[3], w11[0], w11[1], w11[2], w11[3]}};
-        bf16x8 xt[2];
+        const float rl = ldsv<float>(pb + L::r + 4 * (32 * jh + lr));
+        // the slot holds X~ = w X (units the X-loader scales, but for a block of this head
+        // that takes the exact form) or X itself: then X~ is formed here
+        bf16x8 xt[2] = {xf[0], xf[1]};
+        if (ci < XS0 || flag == 2) {
+            asm volatile("");
+            const lds_ptr wp = pb + L::w + 128 * jh + 32 * lg;
+            const f32x4 w00 = ldsv<f32x4>(wp), w01 = ldsv<f32x4>(wp + 16), w10 = ldsv<f32x4>(wp + 64),
+                        w11 = ldsv<f32x4>(wp + 80);
+            const float ws[2][8] = {{w00[0], w00[1], w00[2], w00[3], w01[0], w01[1], w01[2], w01[3]},
+                                    {w10[0], w10[1], w10[2], w10[3], w11[0], w11[1], w11[2], w11[3]}};
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+            for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int q8 = 0; q8 < 8; ++q8) xt[ks][q8] = (__bf16)((float)xf[ks][q8] * ws[ks][q8]);
+                for (int q8 = 0; q8 < 8; ++q8) xt[ks][q8] = (__bf16)((float)xf[ks][q8] * ws[ks][q8]);
+        }
         // One code path for the three kinds of block; the flag only switches in-place
         // scalings and the diagonal tile's operands, so the state stays in the same
         // registers whatever the path (branches of their own around the scalings: as
@@ -630,36 +698,81 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
         //   plain (0):        Y = r [C g + D X~],                 g' = g + B^T X~
         //   renormalise (1):  g <- f g first, then as plain
         //   exact (2):        Y = r C g + D_exact X,              g' = f g + B^T X~
+        // The left factor C g over every n tile comes first, then the state update: two
+        // runs of straight-line code, so that the reads of later n tiles can be issued
+        // ahead of the products of earlier ones (no branch between them).
         const bool renorm = flag == 1, exact = flag == 2;
+        if (renorm) {
+            asm volatile("");
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) gs[nt] *= f;
+        }
         f32x16 acc = f32x16{};
+        // (beyond four n tiles: this block's copies of the tile-0 offsets, through opaque()
+        // so that the compiler cannot hoist every tile's addresses out of the walk and hold
+        // them in registers after all)
+        uint32_t cq[4], bq[2][2];
+        if constexpr (!kept) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) cq[m] = opaque(co[m]);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) bq[ks][j] = opaque(bo[ks][j]);
+        }
+        auto cad = [&](int nt, int m) __attribute__((always_inline)) -> lds_ptr {
+            if constexpr (kept) return ca[nt % NTK][m];
+            else return CS(0) + (cq[m] ^ (64 * nt));
+        };
+        auto bad = [&](int nt, int ks, int j) __attribute__((always_inline)) -> lds_ptr {
+            if constexpr (kept) return ba[nt % NTK][ks][j];
+            else return BS(0) + (bq[ks][j] ^ (64 * nt));
+        };
+        // the left factor's two K-steps per n tile on the state before its update; the C
+        // pieces of n tile nt + PF are read before the products of n tile nt (scheduling
+        // barriers keep that order)
+        constexpr int PF = 2;
+        u32x2 cp[NT][4];
+        auto cread = [&](int nt) __attribute__((always_inline)) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) cp[nt][m] = ldsv<u32x2>(cad(nt, m) + ko);
+        };
+        bf16x8 bt[NT][2];
+        auto bread = [&](int nt) __attribute__((always_inline)) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) bt[nt][kk] = cat44(tr4(bad(nt, kk, 0) + ko), tr4(bad(nt, kk, 1) + ko));
+        };
+#pragma unroll
+        for (int nt = 0; nt < PF && nt < NT; ++nt) cread(nt);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            bf16x8 cf[2], bt[2];
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const u32x2 lo = ldsv<u32x2>(ca[nt][2 * kk] + ko);
-                const u32x2 hi = ldsv<u32x2>(ca[nt][2 * kk + 1] + ko);
-                cf[kk] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-                bt[kk] = cat44(tr4(ba[nt][kk][0] + ko), tr4(ba[nt][kk][1] + ko));
-            }
-            if (renorm) {
-                asm volatile("");
-                gs[nt] *= f;
-            }
-            // the left factor's two K-steps on the state before its update
+            if (nt + PF < NT) cread(nt + PF);
+            else if (nt + PF - NT < PF) bread(nt + PF - NT);
+            __builtin_amdgcn_sched_barrier(0);
             bf16x8 hb[2];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
+            for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
                 for (int q8 = 0; q8 < 8; ++q8) hb[kk][q8] = (__bf16)gs[nt][8 * kk + q8];
-            acc = E::mma(acc, hb[0], cf[0]);
-            acc = E::mma(acc, hb[1], cf[1]);
-            if (exact) {
-                asm volatile("");
-                gs[nt] *= f;
+                const bf16x8 cf = __builtin_bit_cast(bf16x8, u32x4{cp[nt][2 * kk][0], cp[nt][2 * kk][1],
+                                                                   cp[nt][2 * kk + 1][0], cp[nt][2 * kk + 1][1]});
+                acc = E::mma(acc, hb[kk], cf);
             }
-            gs[nt] = E::mma(gs[nt], bt[0], xt[0]);
-            gs[nt] = E::mma(gs[nt], bt[1], xt[1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (exact) {
+            asm volatile("");
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) gs[nt] *= f;
+        }
+        // the state update (B^T fragments of n tile nt + PF read before the products of nt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            if (nt + PF < NT) bread(nt + PF);
+            __builtin_amdgcn_sched_barrier(0);
+            gs[nt] = E::mma(gs[nt], bt[nt][0], xt[0]);
+            gs[nt] = E::mma(gs[nt], bt[nt][1], xt[1]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         // the diagonal tile: the shared masked tile on X~, or (exact) this head's tile with
         // the exact decays on unscaled X, added after the row factor
@@ -670,6 +783,7 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
         const lds_ptr dp = exact ? pb + L::st + 2048 * jh : pb + L::dg;
         const bf16x8 d0 = ldsv<bf16x8>(dp + 16 * lane);
         const bf16x8 d1 = ldsv<bf16x8>(dp + 1024 + 16 * lane);
+        // (X~ for the shared tile, X itself for the exact one)
         bf16x8 xd[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) xd[ks] = exact ? xf[ks] : xt[ks];

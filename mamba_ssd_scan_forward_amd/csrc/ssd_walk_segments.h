@@ -187,10 +187,12 @@ __global__ void __launch_bounds__(64 * kSumUnits) ssd_seg_summary_kernel(SegSumA
         if (lg == 0) ldsw<float>((lds_ptr)wsm + 128 * wave + 4 * lr, w);
         carry += tot;
         // X of the block (K-step ks: rows 16 ks + sigma(8 lg + q)) and its weights
+        bf16x4 xr4[4];
+        lds_tr4x4(xsl + xa0, xsl + xa0 + 8 * XR, xsl + xa0 + 16 * XR, xsl + xa0 + 24 * XR, xr4);
         bf16x8 xt[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 xf = cat44(tr4(xsl + xa0 + 16 * XR * ks), tr4(xsl + xa0 + 16 * XR * ks + 8 * XR));
+            const bf16x8 xf = cat44(xr4[2 * ks], xr4[2 * ks + 1]);
             const f32x4 w0 = ldsv<f32x4>((lds_ptr)wsm + 128 * wave + 4 * (16 * ks + 4 * lg));
             const f32x4 w1 = ldsv<f32x4>((lds_ptr)wsm + 128 * wave + 4 * (16 * ks + 8 + 4 * lg));
             const float ws[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};

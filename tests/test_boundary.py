@@ -300,7 +300,7 @@ def test_plan_describe_names_the_kernels():
 
 def test_noalloc_rejects_a_problem_beyond_its_scratch_before_device_work():
     # the size check comes before any HIP call, so fake addresses are never touched
-    prob = ssd.problem_for(4, 4096, 32, 64, 256, 1, 256, 4, ssd.SSD_DTYPE_BF16)
+    prob = ssd.problem_for(32, 4096, 32, 64, 256, 1, 256, 32, ssd.SSD_DTYPE_F32)
     assert ssd.ssd_workspace_bytes(prob) > ssd.SSD_NOALLOC_SCRATCH_BYTES
     rc = ssd.ssd_forward_noalloc(prob, 1 * GB, 2 * GB, 3 * GB, 4 * GB, None, None, 6 * GB, None, None)
     assert rc == ssd.SSD_ERR_TOO_LARGE

@@ -388,3 +388,38 @@ def test_segmented_fused_walk(case):
     plan = plan_of(inp, 256)
     assert plan["walk"].startswith("ssd_walk_fused_kernel") and plan["summary"].startswith("ssd_seg_summary"), plan
     check(inp, 256, case)
+
+
+# d_state 256 on the fused walker (two or three compute waves, three ring slots), where
+# the workgroups fill the chip without segments: a batch of ragged sequences with initial
+# states (two compute waves), one where three waves take fewer rounds, a packed batch with
+# empty and length-1 sequences and two groups (three waves: the fewest workgroups), strong
+# decay.  Long sequences that would need segments take the two passes over the column
+# halves of the state instead (ordinary and strong decay).
+@pytest.mark.parametrize("case", ["batch_init", "three_waves", "packed_groups2", "strong_decay", "long",
+                                  "long_strong_decay"])
+def test_fused_walker_state256(case):
+    if case == "batch_init":
+        inp, nw = make_inputs(32, 300, 8, 64, 256, 1, "bf16", seed=1600, init_state=True), 2
+    elif case == "three_waves":
+        inp, nw = make_inputs(48, 300, 6, 64, 256, 1, "bf16", seed=1601, init_state=True), 3
+    elif case == "packed_groups2":
+        lens = [1, 0, 300, 257, 5, 600, 256, 31, 0, 400, 64, 129, 2, 300, 33, 222]
+        inp, nw = make_inputs(1, sum(lens), 32, 64, 256, 2, "bf16", seed=1602, init_state=True,
+                              seq_lengths=lens), 3
+    elif case == "strong_decay":
+        inp, nw = make_inputs(32, 300, 8, 64, 256, 1, "bf16", seed=1603, init_state=True), 2
+        inp.logA = (inp.logA * 40.0).astype(np.float32)
+    elif case == "long":
+        inp, nw = make_inputs(1, 8292, 16, 64, 256, 1, "bf16", seed=1604, init_state=True), 0
+    else:
+        inp, nw = make_inputs(1, 8292, 16, 64, 256, 1, "bf16", seed=1605, init_state=True), 0
+        inp.logA = (inp.logA * 40.0).astype(np.float32)
+    plan = plan_of(inp, 256)
+    if nw:
+        assert plan["walk"] == f"ssd_walk_fused_kernel<256, {nw}>" and plan["summary"] == "none", plan
+    else:
+        assert plan["walk"].startswith("ssd_walk_split_pair_kernel"), plan
+    Y, F = check(inp, 256, case)
+    if case == "packed_groups2":
+        np.testing.assert_array_equal(F[1], inp.init[1].astype(np.float64))

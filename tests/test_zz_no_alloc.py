@@ -77,8 +77,8 @@ def test_noalloc_matches_forward_on_two_calls_in_a_row():
 def test_noalloc_rejects_a_problem_beyond_its_scratch():
     import mamba_ssd_scan_forward_amd as ssd
     torch = _torch()
-    # 4 sequences of 4096 tokens, 32 heads, d_state 256 need more than the fixed scratch
-    prob = ssd.problem_for(4, 4096, 32, 64, 256, 1, 256, 4, ssd.SSD_DTYPE_BF16)
+    # 32 float32 sequences of 4096 tokens, 32 heads, d_state 256 need more than the fixed scratch
+    prob = ssd.problem_for(32, 4096, 32, 64, 256, 1, 256, 32, ssd.SSD_DTYPE_F32)
     assert ssd.ssd_workspace_bytes(prob) > ssd.SSD_NOALLOC_SCRATCH_BYTES
     t = torch.empty(16, dtype=torch.uint8, device="cuda")
     a = t.data_ptr()
