@@ -298,6 +298,23 @@ def test_plan_describe_names_the_kernels():
         ssd.ssd_plan_describe(bad)
 
 
+def test_plan_long_sequences_and_state_256():
+    bf16 = ssd.SSD_DTYPE_BF16
+    # one long sequence: segments of the fused walker, after their summary
+    long = ssd.ssd_plan_describe(ssd.problem_for(1, 16384, 80, 64, 128, 1, 256, 1, bf16))
+    assert long["walk"] == "ssd_walk_fused_kernel<128, 5>" and long["summary"].startswith("ssd_seg_summary_kernel<128>")
+    # d_state 256 on the fused walker where no segments are needed ...
+    wide = ssd.ssd_plan_describe(ssd.problem_for(32, 300, 8, 64, 256, 1, 256, 32, bf16))
+    assert wide == {"walk": "ssd_walk_fused_kernel<256, 2>", "prep": "none", "summary": "none"}
+    # ... and the two passes over the state's column halves where they would be
+    few = ssd.ssd_plan_describe(ssd.problem_for(4, 4096, 32, 64, 256, 1, 256, 4, bf16))
+    assert few["walk"].startswith("ssd_walk_split_pair_kernel") and few["prep"] != "none"
+    # the fused walker's result does not depend on the chunk length: every valid one plans it
+    for q in (16, 32, 64, 128, 256):
+        d = ssd.ssd_plan_describe(ssd.problem_for(8, 2048, 80, 64, 128, 1, q, 8, bf16))
+        assert d["walk"] == "ssd_walk_fused_kernel<128, 5>", (q, d)
+
+
 def test_noalloc_rejects_a_problem_beyond_its_scratch_before_device_work():
     # the size check comes before any HIP call, so fake addresses are never touched
     prob = ssd.problem_for(32, 4096, 32, 64, 256, 1, 256, 32, ssd.SSD_DTYPE_F32)
