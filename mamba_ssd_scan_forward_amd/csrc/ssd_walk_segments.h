@@ -35,19 +35,19 @@ struct SegSumArgs {
     int nitems;     // nseq (nseg - 1) G wpg
 };
 
-constexpr int kSumUnits = 2;   // units per summary workgroup, one wave each
+constexpr int kSumUnits = 4;   // units per summary workgroup, one wave each
 
 // One workgroup per (sequence, segment but the last, group, run of kSumUnits units): the
 // segment's 32-row blocks from the last to the first, each block's B rows, X rows and logA
 // brought straight from global memory into a ring of four LDS slots three blocks ahead
-// (wave 0 loads B, wave 1 X and logA), then per unit
+// (wave 0 loads B, wave 1 X and logA; every wave computes one unit), then per unit
 //     g^T += B^T X~,   X~_t = exp(L_{t+1..end}) X_t
 // on MFMA with the operand layouts of the fused walker (B rows swizzled by fused_swz,
 // X read with 4-row transposing reads, rows of the contraction in the sigma order).
 template <int NP>
 __global__ void __launch_bounds__(64 * kSumUnits) ssd_seg_summary_kernel(SegSumArgs a) {
     typedef Elem<__bf16> E;
-    static_assert(kSumUnits == 2, "one wave loads B, the other X and logA");
+    static_assert(kSumUnits % 2 == 0, "wave 0 loads B, wave 1 X and logA (two heads a load)");
     constexpr int NT = NP / 32;
     constexpr int UPR = NP / 8;             // 16-byte units of a B row
     constexpr int RPL = 64 / UPR;           // B rows per 1 KB load
@@ -55,13 +55,15 @@ __global__ void __launch_bounds__(64 * kSumUnits) ssd_seg_summary_kernel(SegSumA
     constexpr int XR = kSumUnits * 64;      // bytes per row of the X slot
     constexpr int NXL = 32 * XR / 1024;     // 1 KB loads of X per block
     constexpr int NSL = 4, D = NSL - 1;     // ring slots, blocks in flight
-    constexpr int L0 = NBL, L1 = NXL + 1;   // loads per block of wave 0 / wave 1
+    constexpr int NLL = kSumUnits / 2;      // logA loads per block (two heads each)
+    constexpr int L0 = NBL, L1 = NXL + NLL; // loads per block of wave 0 / wave 1
     static_assert(D * L0 < 64 && D * L1 < 64, "vmcnt range");
     // (separate arrays per slot, so that the compiler can tell the slot being read from the
     // slots still being filled by direct-to-LDS loads; selected by constant index)
     __shared__ __align__(16) unsigned char b0[32 * NP * 2], b1[32 * NP * 2], b2[32 * NP * 2], b3[32 * NP * 2];
     __shared__ __align__(16) unsigned char x0[32 * XR], x1[32 * XR], x2[32 * XR], x3[32 * XR];
-    __shared__ __align__(16) unsigned char l0[256], l1[256], l2[256], l3[256];   // logA, [2 heads][32]
+    __shared__ __align__(16) unsigned char l0[128 * kSumUnits], l1[128 * kSumUnits], l2[128 * kSumUnits],
+        l3[128 * kSumUnits];   // logA, [units' heads][32]
     __shared__ __align__(16) unsigned char wsm[kSumUnits * 128];   // row weights, [unit][32] float
     auto pick = [](int k, unsigned char* a0, unsigned char* a1, unsigned char* a2, unsigned char* a3)
                     __attribute__((always_inline)) -> lds_ptr {
@@ -73,7 +75,9 @@ __global__ void __launch_bounds__(64 * kSumUnits) ssd_seg_summary_kernel(SegSumA
 
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int item = blockIdx.x;
+    // (consecutive items, the units of one segment and group, on one XCD: its L2 then
+    // fetches the segment's B rows and logA once, not once per XCD)
+    const int item = xcd_remap(blockIdx.x, gridDim.x);
     if (item >= a.nitems) return;
     const int H = a.H, P = a.P, G = a.G, hpg = H / G, uph = P / 32;
     const int q = item % a.wpg;
@@ -86,9 +90,6 @@ __global__ void __launch_bounds__(64 * kSumUnits) ssd_seg_summary_kernel(SegSumA
     const int u0 = q * kSumUnits;
     const int64_t xrx = (int64_t)a.xh * P;
     const int hrep = H / a.xh;
-    // the heads of the workgroup's two units (clamped to the group's last unit)
-    const int ua = min(u0, a.upg - 1), ub = min(u0 + 1, a.upg - 1);
-    const int ha = g * hpg + ua / uph, hb = g * hpg + ub / uph;
 
     // ---- loads: lane i of B load k fills position i % UPR of row k RPL + i / UPR (global
     // unit position ^ swizzle); lane i of X load j piece 64 j + i of the [32][units] rows;
@@ -97,7 +98,7 @@ __global__ void __launch_bounds__(64 * kSumUnits) ssd_seg_summary_kernel(SegSumA
     const rsrc_t xr = make_rsrc(a.X + row0 * xrx, (uint32_t)((int64_t)a.seglen * xrx * 2));
     const rsrc_t lar = make_rsrc(a.logA + row0 * H, (uint32_t)((int64_t)a.seglen * H * 4));
     uint32_t off[NBL > NXL ? NBL : NXL];
-    uint32_t loff = 0;
+    uint32_t loff[NLL] = {};
     if (wave == 0) {
         const int brow = lane / UPR, bpos = lane % UPR;
 #pragma unroll
@@ -105,7 +106,7 @@ __global__ void __launch_bounds__(64 * kSumUnits) ssd_seg_summary_kernel(SegSumA
             const int r = k * RPL + brow;
             off[k] = (uint32_t)((r * G * NP + 8 * (bpos ^ fused_swz<NP>(r))) * 2);
         }
-    } else {
+    } else if (wave == 1) {
 #pragma unroll
         for (int j = 0; j < NXL; ++j) {
             const int pc = 64 * j + lane, r = pc / (4 * kSumUnits), piece = pc % (4 * kSumUnits);
@@ -113,7 +114,11 @@ __global__ void __launch_bounds__(64 * kSumUnits) ssd_seg_summary_kernel(SegSumA
             const int h = g * hpg + u / uph, c0 = 32 * (u % uph);
             off[j] = (uint32_t)((r * xrx + (int64_t)(h / hrep) * P + c0 + 8 * (piece % 4)) * 2);
         }
-        loff = (uint32_t)((lr * H + (lg ? hb : ha)) * 4);
+        // logA load p: lanes 0..31 the head of unit 2 p, lanes 32..63 that of unit 2 p + 1
+        // (units clamped to the group's last)
+#pragma unroll
+        for (int p = 0; p < NLL; ++p)
+            loff[p] = (uint32_t)((lr * H + g * hpg + min(u0 + 2 * p + lg, a.upg - 1) / uph) * 4);
     }
     const uint32_t bb32 = (uint32_t)(32 * G * NP * 2), xb32 = (uint32_t)(32 * xrx * 2), lb32 = (uint32_t)(32 * H * 4);
     // block t of the walk is block nblk - 1 - t of the segment (past the first: the first
@@ -124,10 +129,11 @@ __global__ void __launch_bounds__(64 * kSumUnits) ssd_seg_summary_kernel(SegSumA
         if (wave == 0) {
 #pragma unroll
             for (int i = 0; i < NBL; ++i) fused_lds16(br, BS(k) + 1024 * i, opaque(off[i]), blk * bb32);
-        } else {
+        } else if (wave == 1) {
 #pragma unroll
             for (int j = 0; j < NXL; ++j) fused_lds16(xr, XS(k) + 1024 * j, opaque(off[j]), blk * xb32);
-            fused_lds4(lar, LS(k), opaque(loff), blk * lb32);
+#pragma unroll
+            for (int p = 0; p < NLL; ++p) fused_lds4(lar, LS(k) + 256 * p, opaque(loff[p]), blk * lb32);
         }
     };
 
@@ -136,7 +142,7 @@ __global__ void __launch_bounds__(64 * kSumUnits) ssd_seg_summary_kernel(SegSumA
     const bool valid = u < a.upg;
     const int uc = valid ? u : a.upg - 1;
     const int h = g * hpg + uc / uph, c0 = 32 * (uc % uph);
-    const int hsel = wave == 0 ? 0 : 1;   // its head's row of the logA slot (a or b)
+    const int hsel = wave;   // its head's row of the logA slot
 
     // operand addresses (as in the fused walker, one X slot row of kSumUnits units)
     const int xa0 = wave * 64 + XR * (4 * lg + ((lane & 15) >> 2)) + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
@@ -168,8 +174,9 @@ __global__ void __launch_bounds__(64 * kSumUnits) ssd_seg_summary_kernel(SegSumA
         // after the barrier every wave's are; every wave has also finished block t - 1, whose
         // slot the next issue reuses
         // (a bare barrier: __syncthreads would also wait for every load in flight)
+        // (the other waves load nothing)
         if (wave == 0) fused_wait_vm<(D - 1) * L0>();
-        else fused_wait_vm<(D - 1) * L1>();
+        else if (wave == 1) fused_wait_vm<(D - 1) * L1>();
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_s_barrier();
         issue(t + D, std::integral_constant<int, (k + D) % NSL>{});
