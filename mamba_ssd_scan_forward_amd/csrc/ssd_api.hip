@@ -131,13 +131,14 @@ walk_fn pick_walk_bf16(int PT, int NP, bool cbl) {
 // Workspace and launch plan.  `nseq_total` slots: batch mode has batch * ceil(T/Q)
 // chunks; a packed batch has at most ceil(T/Q) + nseq (one ragged chunk per sequence).
 // The fused walker (ssd_walk_fused.h): bf16, head dimension a multiple of 32 from 64,
-// d_state 64 or 128, any chunk length (its 32-row blocks pass the state between them, so
-// the chunking does not change the result).  NW compute waves per workgroup, each holding
-// 32 columns of one head; it takes the NW that needs the fewest rounds of workgroups over
-// the compute units times rows walked (a packed batch: the fewest workgroups), then leaves
-// the fewest compute waves idle, then the larger NW.  Sequences of one length too few to
-// fill the chip are walked in segments (ssd_walk_segments.h).  It is used when its
-// workgroups, segments counted, fill at least half the chip.
+// d_state 64, 128 or 256, any chunk length (its 32-row blocks pass the state between them,
+// so the chunking does not change the result).  NW compute waves per workgroup, each
+// holding 32 columns of one head; it takes the NW that needs the fewest rounds of
+// workgroups over the compute units times rows walked (a packed batch: the fewest
+// workgroups), then leaves the fewest compute waves idle, then the larger NW.  Sequences
+// of one length too few to fill the chip are walked in segments (ssd_walk_segments.h).  It
+// is used when its workgroups, segments counted, fill at least half the chip (d_state
+// 256: without segments).
 typedef void (*fused_fn_t)(ssd::FusedArgs);
 template <int NP>
 fused_fn_t fused_instance(int nw) {

@@ -26,13 +26,14 @@
 // Workgroup: NW compute waves, two loader waves and a storer.  Compute wave k holds unit
 // u = q NW + k of its group (head u / (P/32), columns 32 (u % (P/32)) .. + 31): the state
 // g^T of that slice (N x 32 float32, N/32 MFMA accumulators of 32 x 32) for the whole
-// sequence.  The X-loader brings each unit's X rows, the BC-loader the group's B and C
-// rows and the heads' logA, all straight from global memory into a ring of LDS slots,
-// two or three blocks ahead.  The loaders also turn each block into its products one
-// step before it is used: the cumsums, w and r of every head, the renormalisation and
-// steep flags, and the masked tile D in the layout of an MFMA operand
-// (v_mfma_f32_32x32x16_bf16 on B and C rows).  Compute waves issue no global memory
-// instruction at all: they read LDS and write their Y tile to a staging buffer in LDS,
+// sequence.  The X-loader brings each unit's X rows and the heads' logA, the BC-loader
+// the group's B and C rows (and its own copy of logA), all straight from global memory
+// into a ring of LDS slots, two or three blocks ahead.  The loaders also turn each block
+// into its products one step before it is used: the cumsums, w and r of every head, the
+// renormalisation and steep flags (X-loader; with two compute waves it also writes
+// X~ = w X into the slot), and the masked tile D in the layout of an MFMA operand
+// (v_mfma_f32_32x32x16_bf16 on B and C rows; BC-loader).  Compute waves issue no global
+// memory instruction at all: they read LDS and write their Y tile to a staging buffer in LDS,
 // from which the storer writes the workgroup's block of Y one block later as whole
 // contiguous row spans (NW units of 64 bytes per row: few, line-sized write requests
 // instead of 32-byte pieces, and no compute wave ever waits behind the loaders' traffic
