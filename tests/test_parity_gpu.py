@@ -423,3 +423,19 @@ def test_fused_walker_state256(case):
     Y, F = check(inp, 256, case)
     if case == "packed_groups2":
         np.testing.assert_array_equal(F[1], inp.init[1].astype(np.float64))
+
+
+def test_fused_walker_result_does_not_depend_on_chunk_len():
+    """The block decomposition gives the same product for any chunking (paper summary page,
+    section 6); the fused walker passes the state between 32-row blocks whatever chunk_len
+    says, so every valid chunk length gives the same bits."""
+    inp = make_inputs(32, 300, 16, 64, 128, 1, "bf16", seed=1700, init_state=True)
+    for q in (16, 64, 256):
+        assert plan_of(inp, q)["walk"] == "ssd_walk_fused_kernel<128, 4>", plan_of(inp, q)
+    d = dev(inp)
+    Y0, F0 = run_gpu(inp, 256, d)
+    for q in (16, 64):
+        Y, F = run_gpu(inp, q, d)
+        np.testing.assert_array_equal(Y, Y0)
+        np.testing.assert_array_equal(F, F0)
+    check(inp, 64, "chunk_len 64")
