@@ -431,9 +431,11 @@ int ssd_plan_describe(const ssd_problem* p, char* buf, size_t len) {
     if (pl.fused) {
         snprintf(walk, sizeof walk, "ssd_walk_fused_kernel<%d, %d>", (int)p->dstate, pl.fused);
         prep = "none";
-        if (pl.fseg > 1)
+        if (pl.fseg > 2)
             summary = p->dstate == 64 ? "ssd_seg_summary_kernel<64>+ssd_seg_combine_kernel"
                                       : "ssd_seg_summary_kernel<128>+ssd_seg_combine_kernel";
+        else if (pl.fseg == 2)
+            summary = p->dstate == 64 ? "ssd_seg_summary_kernel<64>" : "ssd_seg_summary_kernel<128>";
     } else if (pl.npass == 2) {
         snprintf(walk, sizeof walk, "ssd_walk_split_pair_kernel<128>+ssd_add_kernel<bf16>");
     } else if (pl.split) {
@@ -515,8 +517,10 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
             sa.X = static_cast<const __bf16*>(X);
             sa.logA = logA;
             sa.B = static_cast<const __bf16*>(B);
+            sa.init = init_state;
             sa.loc = reinterpret_cast<float*>(ws + pl.loc_off);
             sa.dsum = reinterpret_cast<float*>(ws + pl.dsum_off);
+            sa.sinit = sinit;
             sa.T = T;
             sa.seglen = pl.fseglen;
             sa.nseg = pl.fseg;
@@ -529,11 +533,13 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
             sa.wpg = pl.sum_wpg;
             sa.nitems = (int)pl.sum_items;
             hipLaunchKernelGGL(pl.sum_fn, dim3((unsigned)pl.sum_items), dim3(64 * ssd::kSumUnits), 0, stream, sa);
-            const int64_t n4 = p->nseq * H * P * N / 4;
-            const int64_t cblocks = (n4 + 255) / 256 < 8192 ? (n4 + 255) / 256 : 8192;
-            hipLaunchKernelGGL(ssd::ssd_seg_combine_kernel, dim3((unsigned)cblocks), dim3(256), 0, stream,
-                               static_cast<const float*>(sa.loc), static_cast<const float*>(sa.dsum), init_state,
-                               sinit, (int)p->nseq, pl.fseg, (int)H, (int)(P * N));
+            if (pl.fseg > 2) {
+                const int64_t n4 = p->nseq * H * P * N / 4;
+                const int64_t cblocks = (n4 + 255) / 256 < 8192 ? (n4 + 255) / 256 : 8192;
+                hipLaunchKernelGGL(ssd::ssd_seg_combine_kernel, dim3((unsigned)cblocks), dim3(256), 0, stream,
+                                   static_cast<const float*>(sa.loc), static_cast<const float*>(sa.dsum), sinit,
+                                   (int)p->nseq, pl.fseg, (int)H, (int)(P * N));
+            }
         }
         if (!(stages & 2)) return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
         ssd::FusedArgs fa;
@@ -542,6 +548,7 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
         fa.B = static_cast<const __bf16*>(B);
         fa.C = static_cast<const __bf16*>(C);
         fa.init = seg ? sinit : init_state;
+        fa.init0 = init_state;
         // (a segmented plan has sequences of one length: a batch, or one packed sequence
         // that spans the rows)
         fa.seq_offsets = seg ? nullptr : seq_offsets;

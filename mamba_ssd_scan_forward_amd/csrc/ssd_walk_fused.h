@@ -75,7 +75,10 @@ struct FusedArgs {
     int lpt;        // packed sequences dealt to XCDs longest first
     int nseg;       // > 1: every sequence walked as nseg segments of seglen rows, each a
     int seglen;     // sequence of its own (nseq counts the segments); init then holds every
-                    // segment's entry state, and only the last segment writes a final state
+                    // segment's entry state but the first's, which is init0's (the
+                    // sequences' initial states, or NULL), and only the last segment
+                    // writes a final state
+    const float* init0;
 };
 
 // LDS of the fused walker.  Ring slot: X [32][NW][32] (the block's rows of the units side by side), B and C
@@ -268,11 +271,17 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
     int64_t row0;
     int len;
     int64_t sfin = s;   // slot of the final state (-1: none)
+    const float* init = a.init;   // the entry state: [init_slot][H][P][N], or none
+    int64_t init_slot = s;
     if (a.nseg > 1) {
         const int b = s / a.nseg, sg = s % a.nseg;
         row0 = (int64_t)b * a.T + (int64_t)sg * a.seglen;
         len = (int)min((int64_t)a.seglen, a.T - (int64_t)sg * a.seglen);
         sfin = sg == a.nseg - 1 ? b : -1;
+        if (sg == 0) {
+            init = a.init0;
+            init_slot = b;
+        }
     } else if (!a.seq_offsets) {
         row0 = (int64_t)s * a.T;
         len = (int)a.T;
@@ -603,17 +612,17 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
     const int h = g * hpg + hl;
     const int c0 = 32 * (uc % uph);               // first column of P
     const int jh = hl - hfirst;                   // local head index
-    const int64_t state_base = ((int64_t)s * H + h) * (int64_t)P * NP;
+    const int64_t state_base = (init_slot * H + h) * (int64_t)P * NP;
 
     f32x16 gs[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) gs[nt] = f32x16{};
-    if (a.init) {
+    if (init) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 iv = *reinterpret_cast<const f32x4*>(a.init + state_base + (int64_t)(c0 + lr) * NP + 32 * nt +
+                const f32x4 iv = *reinterpret_cast<const f32x4*>(init + state_base + (int64_t)(c0 + lr) * NP + 32 * nt +
                                                                   8 * q4 + 4 * lg);
 #pragma unroll
                 for (int e4 = 0; e4 < 4; ++e4) gs[nt][4 * q4 + e4] = iv[e4];

@@ -7,11 +7,14 @@
 // workgroups is cut into nseg segments of seglen rows.  Three launches:
 //   summary  every segment but the last, from a zero state: its end state
 //                loc_s = sum_t exp(L_{t+1..end}) x_t B_t^T     (L: the sum of logA)
-//            and its total log decay D_s = sum_t logA_t;
-//   combine  the entry state of every segment, h_0 = the sequence's initial state (or 0),
+//            and its total log decay D_s = sum_t logA_t; the first segment from the
+//            sequence's initial state h_0 instead, which gives the second one's entry
+//            state h_1 = exp(D_0) h_0 + loc_0 directly;
+//   combine  (three segments or more) the entry states of the others,
 //                h_{s+1} = exp(D_s) h_s + loc_s;
 //   walk     the fused walker with every segment a sequence of its own, entering with
-//            h_s; the last segment's final state is the sequence's.
+//            h_s (the first with h_0 itself); the last segment's final state is the
+//            sequence's.
 // The summary is a plain contraction over the segment's rows: each row is weighted by its
 // decay to the segment's end (a suffix sum of logA, at most 1 in size), so there is no
 // running scale to keep, and it reads X and B once.
@@ -25,8 +28,10 @@ struct SegSumArgs {
     const __bf16* X;
     const float* logA;
     const __bf16* B;
-    float* loc;     // [nseq][nseg - 1][H][P][N] float32
-    float* dsum;    // [nseq][nseg - 1][H] float32 (natural log)
+    const float* init;   // the sequences' initial states [nseq][H][P][N] float32, or NULL (zero)
+    float* loc;     // [nseq][nseg - 1][H][P][N] float32 (segment 0's entry unused)
+    float* dsum;    // [nseq][nseg - 1][H] float32 (natural log; segment 0's entry unused)
+    float* sinit;   // the segments' entry states [nseq][nseg][H][P][N] float32: h_1 written here
     int64_t T;      // rows per sequence
     int seglen, nseg, nseq;
     int H, P, G, xh;
@@ -220,6 +225,25 @@ __global__ void __launch_bounds__(64 * kSumUnits) ssd_seg_summary_kernel(SegSumA
     // no load may still be landing in LDS when the workgroup ends
     fused_wait_vm<0>();
     if (!valid) return;
+    if (sg == 0) {
+        // h_1 = exp(D_0) h_0 + loc_0 (carry is D_0 now): the second segment's entry state
+        const float d = fast_exp2(carry * kLog2e);
+        const int64_t off = (int64_t)(c0 + lr) * NP + 4 * lg;
+        const float* ip = a.init ? a.init + ((int64_t)b * H + h) * (int64_t)P * NP + off : nullptr;
+        float* o = a.sinit + (((int64_t)b * a.nseg + 1) * H + h) * (int64_t)P * NP + off;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                f32x4 v = {gs[nt][4 * q4], gs[nt][4 * q4 + 1], gs[nt][4 * q4 + 2], gs[nt][4 * q4 + 3]};
+                if (ip) {
+                    const f32x4 iv = *reinterpret_cast<const f32x4*>(ip + 32 * nt + 8 * q4);
+                    v = f32x4{d * iv[0] + v[0], d * iv[1] + v[1], d * iv[2] + v[2], d * iv[3] + v[3]};
+                }
+                *reinterpret_cast<f32x4*>(o + 32 * nt + 8 * q4) = v;
+            }
+        return;
+    }
     const int64_t slot = ((int64_t)b * (a.nseg - 1) + sg) * H + h;
     float* o = a.loc + slot * (int64_t)P * NP;
 #pragma unroll
@@ -232,19 +256,19 @@ __global__ void __launch_bounds__(64 * kSumUnits) ssd_seg_summary_kernel(SegSumA
     if (c0 == 0 && lane == 0) a.dsum[slot] = carry;
 }
 
-// Entry states of the segments: h_0 = init (or 0), h_{s+1} = exp(D_s) h_s + loc_s, for
-// every (sequence, head) and 4 consecutive state elements per thread.
-__global__ void __launch_bounds__(256) ssd_seg_combine_kernel(const float* loc, const float* dsum, const float* init,
-                                                              float* seg_init, int nseq, int nseg, int H, int PN) {
+// Entry states of the third segment on: h_{s+1} = exp(D_s) h_s + loc_s from h_1 (which the
+// summary of the first segment wrote), for every (sequence, head) and 4 consecutive state
+// elements per thread.
+__global__ void __launch_bounds__(256) ssd_seg_combine_kernel(const float* loc, const float* dsum, float* seg_init,
+                                                              int nseq, int nseg, int H, int PN) {
     const int n4 = PN / 4;
     const int64_t total = (int64_t)nseq * H * n4;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
         const int e4 = (int)(i % n4);
         const int64_t bh = i / n4;
         const int h = (int)(bh % H), b = (int)(bh / H);
-        f32x4 v = init ? *reinterpret_cast<const f32x4*>(init + bh * PN + 4 * e4) : f32x4{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<f32x4*>(seg_init + (((int64_t)b * nseg) * H + h) * PN + 4 * e4) = v;
-        for (int s = 0; s + 1 < nseg; ++s) {
+        f32x4 v = *reinterpret_cast<const f32x4*>(seg_init + (((int64_t)b * nseg + 1) * H + h) * PN + 4 * e4);
+        for (int s = 1; s + 1 < nseg; ++s) {
             const int64_t slot = ((int64_t)b * (nseg - 1) + s) * H + h;
             const float d = fast_exp2(dsum[slot] * kLog2e);
             const f32x4 l = *reinterpret_cast<const f32x4*>(loc + slot * PN + 4 * e4);
