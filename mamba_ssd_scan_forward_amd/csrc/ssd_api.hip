@@ -532,7 +532,7 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
             sa.upg = (int)((H / G) * (P / 32));
             sa.wpg = pl.sum_wpg;
             sa.nitems = (int)pl.sum_items;
-            hipLaunchKernelGGL(pl.sum_fn, dim3((unsigned)pl.sum_items), dim3(64 * ssd::kSumUnits), 0, stream, sa);
+            hipLaunchKernelGGL(pl.sum_fn, dim3((unsigned)pl.sum_items), dim3(ssd::kSumThreads), 0, stream, sa);
             if (pl.fseg > 2) {
                 const int64_t n4 = p->nseq * H * P * N / 4;
                 const int64_t cblocks = (n4 + 255) / 256 < 8192 ? (n4 + 255) / 256 : 8192;

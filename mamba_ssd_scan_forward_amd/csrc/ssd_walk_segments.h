@@ -40,46 +40,56 @@ struct SegSumArgs {
     int nitems;     // nseq (nseg - 1) G wpg
 };
 
-constexpr int kSumUnits = 4;   // units per summary workgroup, one wave each
+constexpr int kSumUnits = 5;                   // units per summary workgroup, one compute wave each
+constexpr int kSumThreads = 64 * (kSumUnits + 2);   // and two loader waves
 
 // One workgroup per (sequence, segment but the last, group, run of kSumUnits units): the
-// segment's 32-row blocks from the last to the first, each block's B rows, X rows and logA
-// brought straight from global memory into a ring of four LDS slots three blocks ahead
-// (wave 0 loads B, wave 1 X and logA; every wave computes one unit), then per unit
+// segment's 32-row blocks from the last to the first, two blocks a step, per unit
 //     g^T += B^T X~,   X~_t = exp(L_{t+1..end}) X_t
 // on MFMA with the operand layouts of the fused walker (B rows swizzled by fused_swz,
 // X read with 4-row transposing reads, rows of the contraction in the sigma order).
+// Waves 0 .. kSumUnits - 1 compute one unit each and issue no memory instruction; the
+// B-loader (wave kSumUnits: B rows and logA) and the X-loader (the next wave: the units' X
+// rows) bring each block straight from global memory into a ring of six LDS slots, two
+// steps (four blocks) ahead.  The step's fixed chain (the logA read, one scan over both
+// blocks' 64 rows, the weights' round trip through LDS, the barrier) is paid once per 64
+// rows.  Five units make a d_state-128 layer of 80 heads 32 workgroups a segment, so the
+// seven segments but the last of a 16K-token sequence take one compute unit each.
 template <int NP>
-__global__ void __launch_bounds__(64 * kSumUnits) ssd_seg_summary_kernel(SegSumArgs a) {
+__global__ void __launch_bounds__(kSumThreads, 1) ssd_seg_summary_kernel(SegSumArgs a) {
     typedef Elem<__bf16> E;
-    static_assert(kSumUnits % 2 == 0, "wave 0 loads B, wave 1 X and logA (two heads a load)");
     constexpr int NT = NP / 32;
     constexpr int UPR = NP / 8;             // 16-byte units of a B row
     constexpr int RPL = 64 / UPR;           // B rows per 1 KB load
     constexpr int NBL = NP / 16;            // 1 KB loads of B per block
     constexpr int XR = kSumUnits * 64;      // bytes per row of the X slot
+    static_assert(32 * XR % 1024 == 0, "whole 1 KB loads of X");
     constexpr int NXL = 32 * XR / 1024;     // 1 KB loads of X per block
-    constexpr int NSL = 4, D = NSL - 1;     // ring slots, blocks in flight
-    constexpr int NLL = kSumUnits / 2;      // logA loads per block (two heads each)
-    constexpr int L0 = NBL, L1 = NXL + NLL; // loads per block of wave 0 / wave 1
-    static_assert(D * L0 < 64 && D * L1 < 64, "vmcnt range");
-    // (separate arrays per slot, so that the compiler can tell the slot being read from the
-    // slots still being filled by direct-to-LDS loads; selected by constant index)
-    __shared__ __align__(16) unsigned char b0[32 * NP * 2], b1[32 * NP * 2], b2[32 * NP * 2], b3[32 * NP * 2];
-    __shared__ __align__(16) unsigned char x0[32 * XR], x1[32 * XR], x2[32 * XR], x3[32 * XR];
-    __shared__ __align__(16) unsigned char l0[128 * kSumUnits], l1[128 * kSumUnits], l2[128 * kSumUnits],
-        l3[128 * kSumUnits];   // logA, [units' heads][32]
-    __shared__ __align__(16) unsigned char wsm[kSumUnits * 128];   // row weights, [unit][32] float
-    auto pick = [](int k, unsigned char* a0, unsigned char* a1, unsigned char* a2, unsigned char* a3)
-                    __attribute__((always_inline)) -> lds_ptr {
-        return k == 0 ? (lds_ptr)a0 : k == 1 ? (lds_ptr)a1 : k == 2 ? (lds_ptr)a2 : (lds_ptr)a3;
+    constexpr int NLL = (kSumUnits + 1) / 2;   // logA loads per block (two units' heads each)
+    constexpr int LSZ = 256 * NLL;          // bytes of a logA slot: [units][32] float
+    constexpr int NSL = 6, DS = 2;          // ring slots (three steps of two blocks), steps in flight
+    constexpr int LB = 2 * (NBL + NLL), LX = 2 * NXL;   // loads per step of the B-, X-loader
+    static_assert(DS * LB < 64 && DS * LX < 64, "vmcnt range");
+    // (separate arrays per slot, so that the compiler can tell the slots being read from
+    // the slots still being filled by direct-to-LDS loads; selected by constant index)
+    __shared__ __align__(16) unsigned char b0[32 * NP * 2], b1[32 * NP * 2], b2[32 * NP * 2], b3[32 * NP * 2],
+        b4[32 * NP * 2], b5[32 * NP * 2];
+    __shared__ __align__(16) unsigned char x0[32 * XR], x1[32 * XR], x2[32 * XR], x3[32 * XR], x4[32 * XR],
+        x5[32 * XR];
+    __shared__ __align__(16) unsigned char l0[LSZ], l1[LSZ], l2[LSZ], l3[LSZ], l4[LSZ], l5[LSZ];
+    __shared__ __align__(16) unsigned char wsm[kSumUnits * 256];   // row weights, [wave][64] float
+    auto pick = [](int k, unsigned char* a0, unsigned char* a1, unsigned char* a2, unsigned char* a3,
+                   unsigned char* a4, unsigned char* a5) __attribute__((always_inline)) -> lds_ptr {
+        return k == 0 ? (lds_ptr)a0 : k == 1 ? (lds_ptr)a1 : k == 2 ? (lds_ptr)a2 : k == 3 ? (lds_ptr)a3
+             : k == 4 ? (lds_ptr)a4 : (lds_ptr)a5;
     };
-    auto BS = [&](int k) __attribute__((always_inline)) { return pick(k, b0, b1, b2, b3); };
-    auto XS = [&](int k) __attribute__((always_inline)) { return pick(k, x0, x1, x2, x3); };
-    auto LS = [&](int k) __attribute__((always_inline)) { return pick(k, l0, l1, l2, l3); };
+    auto BS = [&](int k) __attribute__((always_inline)) { return pick(k, b0, b1, b2, b3, b4, b5); };
+    auto XS = [&](int k) __attribute__((always_inline)) { return pick(k, x0, x1, x2, x3, x4, x5); };
+    auto LS = [&](int k) __attribute__((always_inline)) { return pick(k, l0, l1, l2, l3, l4, l5); };
 
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool bloader = wave == kSumUnits, xloader = wave == kSumUnits + 1;
     // (consecutive items, the units of one segment and group, on one XCD: its L2 then
     // fetches the segment's B rows and logA once, not once per XCD)
     const int item = xcd_remap(blockIdx.x, gridDim.x);
@@ -97,21 +107,25 @@ __global__ void __launch_bounds__(64 * kSumUnits) ssd_seg_summary_kernel(SegSumA
     const int hrep = H / a.xh;
 
     // ---- loads: lane i of B load k fills position i % UPR of row k RPL + i / UPR (global
-    // unit position ^ swizzle); lane i of X load j piece 64 j + i of the [32][units] rows;
-    // lane i of the logA load row i % 32 of head a (i < 32) or b
+    // unit position ^ swizzle); lane i of logA load p row i % 32 of the head of unit 2 p
+    // (i < 32) or 2 p + 1; lane i of X load j piece 64 j + i of the [32][units] rows (units
+    // clamped to the group's last)
     const rsrc_t br = make_rsrc(a.B + row0 * G * NP + g * NP, (uint32_t)((int64_t)a.seglen * G * NP * 2));
     const rsrc_t xr = make_rsrc(a.X + row0 * xrx, (uint32_t)((int64_t)a.seglen * xrx * 2));
     const rsrc_t lar = make_rsrc(a.logA + row0 * H, (uint32_t)((int64_t)a.seglen * H * 4));
     uint32_t off[NBL > NXL ? NBL : NXL];
     uint32_t loff[NLL] = {};
-    if (wave == 0) {
+    if (bloader) {
         const int brow = lane / UPR, bpos = lane % UPR;
 #pragma unroll
         for (int k = 0; k < NBL; ++k) {
             const int r = k * RPL + brow;
             off[k] = (uint32_t)((r * G * NP + 8 * (bpos ^ fused_swz<NP>(r))) * 2);
         }
-    } else if (wave == 1) {
+#pragma unroll
+        for (int p = 0; p < NLL; ++p)
+            loff[p] = (uint32_t)((lr * H + g * hpg + min(u0 + 2 * p + lg, a.upg - 1) / uph) * 4);
+    } else if (xloader) {
 #pragma unroll
         for (int j = 0; j < NXL; ++j) {
             const int pc = 64 * j + lane, r = pc / (4 * kSumUnits), piece = pc % (4 * kSumUnits);
@@ -119,35 +133,30 @@ __global__ void __launch_bounds__(64 * kSumUnits) ssd_seg_summary_kernel(SegSumA
             const int h = g * hpg + u / uph, c0 = 32 * (u % uph);
             off[j] = (uint32_t)((r * xrx + (int64_t)(h / hrep) * P + c0 + 8 * (piece % 4)) * 2);
         }
-        // logA load p: lanes 0..31 the head of unit 2 p, lanes 32..63 that of unit 2 p + 1
-        // (units clamped to the group's last)
-#pragma unroll
-        for (int p = 0; p < NLL; ++p)
-            loff[p] = (uint32_t)((lr * H + g * hpg + min(u0 + 2 * p + lg, a.upg - 1) / uph) * 4);
     }
     const uint32_t bb32 = (uint32_t)(32 * G * NP * 2), xb32 = (uint32_t)(32 * xrx * 2), lb32 = (uint32_t)(32 * H * 4);
-    // block t of the walk is block nblk - 1 - t of the segment (past the first: the first
-    // again, so that every step issues the same loads and the wait counts stay exact)
+    // walk position t (0, 1, ...) is block nblk - 1 - t of the segment, in slot t % NSL
+    // (past the first block: the first again, so that every step issues the same loads and
+    // the wait counts stay exact); step s holds positions 2 s and 2 s + 1
     auto issue = [&](int t, auto kc) __attribute__((always_inline)) {
         constexpr int k = decltype(kc)::value;
         const uint32_t blk = (uint32_t)max(nblk - 1 - t, 0);
-        if (wave == 0) {
+        if (bloader) {
 #pragma unroll
             for (int i = 0; i < NBL; ++i) fused_lds16(br, BS(k) + 1024 * i, opaque(off[i]), blk * bb32);
-        } else if (wave == 1) {
-#pragma unroll
-            for (int j = 0; j < NXL; ++j) fused_lds16(xr, XS(k) + 1024 * j, opaque(off[j]), blk * xb32);
 #pragma unroll
             for (int p = 0; p < NLL; ++p) fused_lds4(lar, LS(k) + 256 * p, opaque(loff[p]), blk * lb32);
+        } else if (xloader) {
+#pragma unroll
+            for (int j = 0; j < NXL; ++j) fused_lds16(xr, XS(k) + 1024 * j, opaque(off[j]), blk * xb32);
         }
     };
 
     // this wave's unit
     const int u = u0 + wave;
-    const bool valid = u < a.upg;
-    const int uc = valid ? u : a.upg - 1;
+    const bool valid = wave < kSumUnits && u < a.upg;
+    const int uc = min(u, a.upg - 1);
     const int h = g * hpg + uc / uph, c0 = 32 * (uc % uph);
-    const int hsel = wave;   // its head's row of the logA slot
 
     // operand addresses (as in the fused walker, one X slot row of kSumUnits units)
     const int xa0 = wave * 64 + XR * (4 * lg + ((lane & 15) >> 2)) + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
@@ -169,44 +178,27 @@ __global__ void __launch_bounds__(64 * kSumUnits) ssd_seg_summary_kernel(SegSumA
     f32x16 gs[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) gs[nt] = f32x16{};
-    float carry = 0.f;   // sum of logA over the rows after this block, within the segment
+    float carry = 0.f;   // sum of logA over the rows after this step, within the segment
     issue(0, std::integral_constant<int, 0>{});
     issue(1, std::integral_constant<int, 1>{});
     issue(2, std::integral_constant<int, 2>{});
-    auto step = [&](int t, auto kc) __attribute__((always_inline)) {
-        constexpr int k = decltype(kc)::value;
-        // this wave's loads of block t are in (the two blocks after it still in flight), and
-        // after the barrier every wave's are; every wave has also finished block t - 1, whose
-        // slot the next issue reuses
-        // (a bare barrier: __syncthreads would also wait for every load in flight)
-        // (the other waves load nothing)
-        if (wave == 0) fused_wait_vm<(D - 1) * L0>();
-        else if (wave == 1) fused_wait_vm<(D - 1) * L1>();
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_s_barrier();
-        issue(t + D, std::integral_constant<int, (k + D) % NSL>{});
-        const lds_ptr bsl = BS(k), xsl = XS(k);
-        // the block's B^T operands first: their reads overlap the weights' computation
+    issue(3, std::integral_constant<int, 3>{});
+    const lds_ptr wme = (lds_ptr)wsm + 256 * (wave < kSumUnits ? wave : 0);
+    // one block's products: its B^T operands, its X rows and their weights (at wo in the
+    // wave's weights), eight MFMAs
+    auto block = [&](lds_ptr bsl, lds_ptr xsl, int wo) __attribute__((always_inline)) {
         bf16x8 bt[NT][2];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) bt[nt][ks] = cat44(tr4(bsl + ba[nt][ks][0]), tr4(bsl + ba[nt][ks][1]));
-        // row weights of this wave's head: exp of the logA sum over the later rows
-        const float c = scan32(lds_read4(LS(k) + 4 * (32 * hsel + lr)));   // inclusive
-        const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, c), 31));
-        const float w = fast_exp2((tot - c + carry) * kLog2e);
-        if (lg == 0) ldsw<float>((lds_ptr)wsm + 128 * wave + 4 * lr, w);
-        carry += tot;
-        // X of the block (K-step ks: rows 16 ks + sigma(8 lg + q)) and its weights
-        bf16x4 xr4[4];
-        lds_tr4x4(xsl + xa0, xsl + xa0 + 8 * XR, xsl + xa0 + 16 * XR, xsl + xa0 + 24 * XR, xr4);
         bf16x8 xt[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 xf = cat44(xr4[2 * ks], xr4[2 * ks + 1]);
-            const f32x4 w0 = ldsv<f32x4>((lds_ptr)wsm + 128 * wave + 4 * (16 * ks + 4 * lg));
-            const f32x4 w1 = ldsv<f32x4>((lds_ptr)wsm + 128 * wave + 4 * (16 * ks + 8 + 4 * lg));
+            // rows 16 ks + sigma(8 lg + q) of the block
+            const bf16x8 xf = cat44(tr4(xsl + xa0 + 16 * XR * ks), tr4(xsl + xa0 + 16 * XR * ks + 8 * XR));
+            const f32x4 w0 = ldsv<f32x4>(wme + wo + 4 * (16 * ks + 4 * lg));
+            const f32x4 w1 = ldsv<f32x4>(wme + wo + 4 * (16 * ks + 8 + 4 * lg));
             const float ws[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
 #pragma unroll
             for (int q8 = 0; q8 < 8; ++q8) xt[ks][q8] = (__bf16)((float)xf[q8] * ws[q8]);
@@ -216,11 +208,40 @@ __global__ void __launch_bounds__(64 * kSumUnits) ssd_seg_summary_kernel(SegSumA
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) gs[nt] = E::mma(gs[nt], bt[nt][ks], xt[ks]);
     };
-    for (int t = 0; t < nblk; t += NSL) {
-        step(t, std::integral_constant<int, 0>{});
-        if (t + 1 < nblk) step(t + 1, std::integral_constant<int, 1>{});
-        if (t + 2 < nblk) step(t + 2, std::integral_constant<int, 2>{});
-        if (t + 3 < nblk) step(t + 3, std::integral_constant<int, 3>{});
+    auto step = [&](int s, auto kc) __attribute__((always_inline)) {
+        constexpr int j = decltype(kc)::value;
+        constexpr int kL = 2 * j, kE = 2 * j + 1;   // slots of the later and the earlier block
+        // the loaders' loads of step s are in (step s + 1 still in flight), and after the
+        // barrier every loader's are; every wave has also finished step s - 1, whose slots
+        // the next issue reuses
+        // (a bare barrier: __syncthreads would also wait for every load in flight)
+        if (bloader) fused_wait_vm<(DS - 1) * LB>();
+        else if (xloader) fused_wait_vm<(DS - 1) * LX>();
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        issue(2 * s + 2 * DS, std::integral_constant<int, (kL + 2 * DS) % NSL>{});
+        issue(2 * s + 2 * DS + 1, std::integral_constant<int, (kE + 2 * DS) % NSL>{});
+        if (wave >= kSumUnits) return;
+        // whether the step has an earlier block (an odd block count leaves the last step one)
+        const bool hasE = 2 * s + 1 < nblk;
+        // row weights of this wave's head over both blocks: lanes 0..31 the earlier block's
+        // rows, 32..63 the later block's; exp of the logA sum over the later rows (in asm with
+        // its own wait: as a plain read the compiler would first wait for every
+        // direct-to-LDS load in flight)
+        const float la = lds_read4((lg ? LS(kL) : LS(kE)) + 4 * (32 * wave + lr));
+        const float c = scan32(la);   // inclusive, within each half
+        const float totE = hasE ? lane_f(c, 31) : 0.f, totL = lane_f(c, 63);
+        const float w = (lg || hasE) ? fast_exp2((carry + (lg ? totL - c : totE - c + totL)) * kLog2e) : 0.f;
+        ldsw<float>(wme + 4 * lane, w);
+        carry += totE + totL;
+        block(BS(kL), XS(kL), 128);
+        if (hasE) block(BS(kE), XS(kE), 0);
+    };
+    const int nstep = (nblk + 1) / 2;
+    for (int s = 0; s < nstep; s += 3) {
+        step(s, std::integral_constant<int, 0>{});
+        if (s + 1 < nstep) step(s + 1, std::integral_constant<int, 1>{});
+        if (s + 2 < nstep) step(s + 2, std::integral_constant<int, 2>{});
     }
     // no load may still be landing in LDS when the workgroup ends
     fused_wait_vm<0>();
