@@ -41,7 +41,7 @@ struct SegSumArgs {
 };
 
 constexpr int kSumUnits = 5;                   // units per summary workgroup, one compute wave each
-constexpr int kSumThreads = 64 * (kSumUnits + 2);   // and two loader waves
+constexpr int kSumThreads = 64 * (kSumUnits + 3);   // and three loader waves
 
 // One workgroup per (sequence, segment but the last, group, run of kSumUnits units): the
 // segment's 32-row blocks from the last to the first, two blocks a step, per unit
@@ -49,9 +49,9 @@ constexpr int kSumThreads = 64 * (kSumUnits + 2);   // and two loader waves
 // on MFMA with the operand layouts of the fused walker (B rows swizzled by fused_swz,
 // X read with 4-row transposing reads, rows of the contraction in the sigma order).
 // Waves 0 .. kSumUnits - 1 compute one unit each and issue no memory instruction; the
-// B-loader (wave kSumUnits: B rows and logA) and the X-loader (the next wave: the units' X
-// rows) bring each block straight from global memory into a ring of six LDS slots, two
-// steps (four blocks) ahead.  The step's fixed chain (the logA read, one scan over both
+// B-loader (wave kSumUnits), the X-loader (the next wave: the units' X rows) and the
+// logA-loader (the last) bring each block straight from global memory into a ring of
+// eight LDS slots, three steps (six blocks) ahead.  The step's fixed chain (the logA read, one scan over both
 // blocks' 64 rows, the weights' round trip through LDS, the barrier) is paid once per 64
 // rows.  Five units make a d_state-128 layer of 80 heads 32 workgroups a segment, so the
 // seven segments but the last of a 16K-token sequence take one compute unit each.
@@ -67,29 +67,30 @@ __global__ void __launch_bounds__(kSumThreads, 1) ssd_seg_summary_kernel(SegSumA
     constexpr int NXL = 32 * XR / 1024;     // 1 KB loads of X per block
     constexpr int NLL = (kSumUnits + 1) / 2;   // logA loads per block (two units' heads each)
     constexpr int LSZ = 256 * NLL;          // bytes of a logA slot: [units][32] float
-    constexpr int NSL = 6, DS = 2;          // ring slots (three steps of two blocks), steps in flight
-    constexpr int LB = 2 * (NBL + NLL), LX = 2 * NXL;   // loads per step of the B-, X-loader
-    static_assert(DS * LB < 64 && DS * LX < 64, "vmcnt range");
+    constexpr int NSL = 8, DS = 3;          // ring slots (four steps of two blocks), steps in flight
+    constexpr int LB = 2 * NBL, LX = 2 * NXL, LL = 2 * NLL;   // loads per step of each loader
+    static_assert(DS * LB < 64 && DS * LX < 64 && DS * LL < 64, "vmcnt range");
     // (separate arrays per slot, so that the compiler can tell the slots being read from
     // the slots still being filled by direct-to-LDS loads; selected by constant index)
     __shared__ __align__(16) unsigned char b0[32 * NP * 2], b1[32 * NP * 2], b2[32 * NP * 2], b3[32 * NP * 2],
-        b4[32 * NP * 2], b5[32 * NP * 2];
+        b4[32 * NP * 2], b5[32 * NP * 2], b6[32 * NP * 2], b7[32 * NP * 2];
     __shared__ __align__(16) unsigned char x0[32 * XR], x1[32 * XR], x2[32 * XR], x3[32 * XR], x4[32 * XR],
-        x5[32 * XR];
-    __shared__ __align__(16) unsigned char l0[LSZ], l1[LSZ], l2[LSZ], l3[LSZ], l4[LSZ], l5[LSZ];
+        x5[32 * XR], x6[32 * XR], x7[32 * XR];
+    __shared__ __align__(16) unsigned char l0[LSZ], l1[LSZ], l2[LSZ], l3[LSZ], l4[LSZ], l5[LSZ], l6[LSZ], l7[LSZ];
     __shared__ __align__(16) unsigned char wsm[kSumUnits * 256];   // row weights, [wave][64] float
     auto pick = [](int k, unsigned char* a0, unsigned char* a1, unsigned char* a2, unsigned char* a3,
-                   unsigned char* a4, unsigned char* a5) __attribute__((always_inline)) -> lds_ptr {
+                   unsigned char* a4, unsigned char* a5, unsigned char* a6,
+                   unsigned char* a7) __attribute__((always_inline)) -> lds_ptr {
         return k == 0 ? (lds_ptr)a0 : k == 1 ? (lds_ptr)a1 : k == 2 ? (lds_ptr)a2 : k == 3 ? (lds_ptr)a3
-             : k == 4 ? (lds_ptr)a4 : (lds_ptr)a5;
+             : k == 4 ? (lds_ptr)a4 : k == 5 ? (lds_ptr)a5 : k == 6 ? (lds_ptr)a6 : (lds_ptr)a7;
     };
-    auto BS = [&](int k) __attribute__((always_inline)) { return pick(k, b0, b1, b2, b3, b4, b5); };
-    auto XS = [&](int k) __attribute__((always_inline)) { return pick(k, x0, x1, x2, x3, x4, x5); };
-    auto LS = [&](int k) __attribute__((always_inline)) { return pick(k, l0, l1, l2, l3, l4, l5); };
+    auto BS = [&](int k) __attribute__((always_inline)) { return pick(k, b0, b1, b2, b3, b4, b5, b6, b7); };
+    auto XS = [&](int k) __attribute__((always_inline)) { return pick(k, x0, x1, x2, x3, x4, x5, x6, x7); };
+    auto LS = [&](int k) __attribute__((always_inline)) { return pick(k, l0, l1, l2, l3, l4, l5, l6, l7); };
 
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lg = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool bloader = wave == kSumUnits, xloader = wave == kSumUnits + 1;
+    const bool bloader = wave == kSumUnits, xloader = wave == kSumUnits + 1, lloader = wave == kSumUnits + 2;
     // (consecutive items, the units of one segment and group, on one XCD: its L2 then
     // fetches the segment's B rows and logA once, not once per XCD)
     const int item = xcd_remap(blockIdx.x, gridDim.x);
@@ -122,6 +123,7 @@ __global__ void __launch_bounds__(kSumThreads, 1) ssd_seg_summary_kernel(SegSumA
             const int r = k * RPL + brow;
             off[k] = (uint32_t)((r * G * NP + 8 * (bpos ^ fused_swz<NP>(r))) * 2);
         }
+    } else if (lloader) {
 #pragma unroll
         for (int p = 0; p < NLL; ++p)
             loff[p] = (uint32_t)((lr * H + g * hpg + min(u0 + 2 * p + lg, a.upg - 1) / uph) * 4);
@@ -144,6 +146,7 @@ __global__ void __launch_bounds__(kSumThreads, 1) ssd_seg_summary_kernel(SegSumA
         if (bloader) {
 #pragma unroll
             for (int i = 0; i < NBL; ++i) fused_lds16(br, BS(k) + 1024 * i, opaque(off[i]), blk * bb32);
+        } else if (lloader) {
 #pragma unroll
             for (int p = 0; p < NLL; ++p) fused_lds4(lar, LS(k) + 256 * p, opaque(loff[p]), blk * lb32);
         } else if (xloader) {
@@ -183,6 +186,8 @@ __global__ void __launch_bounds__(kSumThreads, 1) ssd_seg_summary_kernel(SegSumA
     issue(1, std::integral_constant<int, 1>{});
     issue(2, std::integral_constant<int, 2>{});
     issue(3, std::integral_constant<int, 3>{});
+    issue(4, std::integral_constant<int, 4>{});
+    issue(5, std::integral_constant<int, 5>{});
     const lds_ptr wme = (lds_ptr)wsm + 256 * (wave < kSumUnits ? wave : 0);
     // one block's products: its B^T operands, its X rows and their weights (at wo in the
     // wave's weights), eight MFMAs
@@ -211,12 +216,13 @@ __global__ void __launch_bounds__(kSumThreads, 1) ssd_seg_summary_kernel(SegSumA
     auto step = [&](int s, auto kc) __attribute__((always_inline)) {
         constexpr int j = decltype(kc)::value;
         constexpr int kL = 2 * j, kE = 2 * j + 1;   // slots of the later and the earlier block
-        // the loaders' loads of step s are in (step s + 1 still in flight), and after the
+        // the loaders' loads of step s are in (the steps after it still in flight), and after the
         // barrier every loader's are; every wave has also finished step s - 1, whose slots
         // the next issue reuses
         // (a bare barrier: __syncthreads would also wait for every load in flight)
         if (bloader) fused_wait_vm<(DS - 1) * LB>();
         else if (xloader) fused_wait_vm<(DS - 1) * LX>();
+        else if (lloader) fused_wait_vm<(DS - 1) * LL>();
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_s_barrier();
         issue(2 * s + 2 * DS, std::integral_constant<int, (kL + 2 * DS) % NSL>{});
@@ -238,10 +244,11 @@ __global__ void __launch_bounds__(kSumThreads, 1) ssd_seg_summary_kernel(SegSumA
         if (hasE) block(BS(kE), XS(kE), 0);
     };
     const int nstep = (nblk + 1) / 2;
-    for (int s = 0; s < nstep; s += 3) {
+    for (int s = 0; s < nstep; s += 4) {
         step(s, std::integral_constant<int, 0>{});
         if (s + 1 < nstep) step(s + 1, std::integral_constant<int, 1>{});
         if (s + 2 < nstep) step(s + 2, std::integral_constant<int, 2>{});
+        if (s + 3 < nstep) step(s + 3, std::integral_constant<int, 3>{});
     }
     // no load may still be landing in LDS when the workgroup ends
     fused_wait_vm<0>();
