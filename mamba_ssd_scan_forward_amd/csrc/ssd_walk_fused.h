@@ -708,16 +708,15 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
         //   plain (0):        Y = r [C g + D X~],                 g' = g + B^T X~
         //   renormalise (1):  g <- f g first, then as plain
         //   exact (2):        Y = r C g + D_exact X,              g' = f g + B^T X~
-        // The left factor C g over every n tile comes first, then the state update: two
-        // runs of straight-line code, so that the reads of later n tiles can be issued
-        // ahead of the products of earlier ones (no branch between them).
+        // The left factor C g over every n tile comes first, then the diagonal tile's two
+        // products, then the state update: runs of straight-line code, so that the reads of
+        // later n tiles can be issued ahead of the products of earlier ones (no branch
+        // between them), and Y leaves the accumulator while the state update runs.
         const bool renorm = flag == 1, exact = flag == 2;
-        if (renorm) {
-            asm volatile("");
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) gs[nt] *= f;
-        }
-        f32x16 acc = f32x16{};
+        // the diagonal tile's fragments (shared, or this head's exact tile)
+        const lds_ptr dp = exact ? pb + L::st + 2048 * jh : pb + L::dg;
+        const bf16x8 d0 = ldsv<bf16x8>(dp + 16 * lane);
+        const bf16x8 d1 = ldsv<bf16x8>(dp + 1024 + 16 * lane);
         // (beyond four n tiles: this block's copies of the tile-0 offsets, through opaque()
         // so that the compiler cannot hoist every tile's addresses out of the walk and hold
         // them in registers after all)
@@ -752,6 +751,12 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) bt[nt][kk] = cat44(tr4(bad(nt, kk, 0) + ko), tr4(bad(nt, kk, 1) + ko));
         };
+        if (renorm) {
+            asm volatile("");
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) gs[nt] *= f;
+        }
+        f32x16 acc = f32x16{};
 #pragma unroll
         for (int nt = 0; nt < PF && nt < NT; ++nt) cread(nt);
 #pragma unroll
@@ -770,12 +775,44 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        // the diagonal tile: the shared masked tile on X~, or (exact) this head's tile with
+        // the exact decays on unscaled X, added after the row factor.  It does not depend
+        // on the state update, so it comes first and the row factor and the bf16 rows of Y
+        // are issued between the state update's products (their latency hidden under them).
+        if (exact) {
+            asm volatile("");
+            acc *= rl;
+        }
+        // (X~ for the shared tile, X itself for the exact one)
+        bf16x8 xd[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) xd[ks] = exact ? xf[ks] : xt[ks];
+        acc = E::mma(acc, xd[0], d0);
+        acc = E::mma(acc, xd[1], d1);
         if (exact) {
             asm volatile("");
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) gs[nt] *= f;
         }
-        // the state update (B^T fragments of n tile nt + PF read before the products of nt)
+        // Y^T (p x l) to the staging buffer as bf16 rows: lane (l, lg) holds columns
+        // 8 q + 4 lg .. + 3 of row l, q = 0 .. 3 (the storer writes the block out after the
+        // barrier)
+        auto ywrite = [&]() __attribute__((always_inline)) {
+            if (!exact) {
+                asm volatile("");
+                acc *= rl;
+            }
+            const lds_ptr yb = ybuf(t) + lr * L::ystride + ci * 64 + 8 * lg;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const bf16x2 v0 = {(__bf16)acc[4 * q], (__bf16)acc[4 * q + 1]};
+                const bf16x2 v1 = {(__bf16)acc[4 * q + 2], (__bf16)acc[4 * q + 3]};
+                ldsw<u32x2>(yb + 16 * q, u32x2{__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1)});
+            }
+        };
+        // the state update (B^T fragments of n tile nt + PF read before the products of nt);
+        // Y's row factor and bf16 rows after the products of the second n tile (by then the
+        // diagonal tile's result has arrived, and the rest of the update runs under them)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             if (nt + PF < NT) bread(nt + PF);
@@ -783,35 +820,7 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
             gs[nt] = E::mma(gs[nt], bt[nt][0], xt[0]);
             gs[nt] = E::mma(gs[nt], bt[nt][1], xt[1]);
             __builtin_amdgcn_sched_barrier(0);
-        }
-        // the diagonal tile: the shared masked tile on X~, or (exact) this head's tile with
-        // the exact decays on unscaled X, added after the row factor
-        if (exact) {
-            asm volatile("");
-            acc *= rl;
-        }
-        const lds_ptr dp = exact ? pb + L::st + 2048 * jh : pb + L::dg;
-        const bf16x8 d0 = ldsv<bf16x8>(dp + 16 * lane);
-        const bf16x8 d1 = ldsv<bf16x8>(dp + 1024 + 16 * lane);
-        // (X~ for the shared tile, X itself for the exact one)
-        bf16x8 xd[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) xd[ks] = exact ? xf[ks] : xt[ks];
-        acc = E::mma(acc, xd[0], d0);
-        acc = E::mma(acc, xd[1], d1);
-        if (!exact) {
-            asm volatile("");
-            acc *= rl;
-        }
-        // Y^T (p x l) to the staging buffer as bf16 rows: lane (l, lg) holds columns
-        // 8 q + 4 lg .. + 3 of row l, q = 0 .. 3 (the storer writes the block out after the
-        // barrier)
-        const lds_ptr yb = ybuf(t) + lr * L::ystride + ci * 64 + 8 * lg;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const bf16x2 v0 = {(__bf16)acc[4 * q], (__bf16)acc[4 * q + 1]};
-            const bf16x2 v1 = {(__bf16)acc[4 * q + 2], (__bf16)acc[4 * q + 3]};
-            ldsw<u32x2>(yb + 16 * q, u32x2{__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1)});
+            if (nt == 1) ywrite();
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_s_barrier();
