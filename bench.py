@@ -17,10 +17,12 @@ buffer read before each step, which evicts the inputs from the last-level cache.
 Roofline: the dominant launch is the chunk walk.  Its algorithmic bytes are the
 minimum traffic of the layer: read X, B, C and logA once, write Y and the final state
 once (the per-token figure times the tokens of one launch, plus the states).  Its
-duration is measured here with HIP events on the stream it runs on, one pair around
-each walk launch of a run of whole steps (the launch from the prep's end to its last
-workgroup's, as a kernel trace times it).  HBM traffic measured by counters is read from the committed
-counter summary when it was taken on the current kernel source, else null.
+duration is measured here with HIP events on the stream it runs on, one pair around a run
+of walk launches back to back (as the timed steps run them); the mean of one event pair
+around each walk launch is reported beside it (events recorded between launches slow the
+launch after them down, which a kernel trace of the same run shows).  HBM traffic
+measured by counters is read from the committed counter summary when it was taken on the
+current kernel source, else null.
 
 ``--mode copy`` runs only a plain device copy of known size; it is the calibration
 program for the FETCH_SIZE / WRITE_SIZE counters.
@@ -556,7 +558,10 @@ def main():
     abytes = algorithmic_bytes(w, es)
     tok_s = tokens / (ms_step * 1e-3)
     peak_mm = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
-    achieved_gbs = abytes / (walk_in_step_ms * 1e-3) / 1e9
+    # the walk's launches back to back on its stream, HIP events around the whole run (as the
+    # timed steps run it; an event recorded between launches slows the launch after it, by
+    # up to a third in a kernel trace, so the per-launch figure is reported beside it only)
+    achieved_gbs = abytes / (stage_ms[2] * 1e-3) / 1e9
     t_roof_ms = max(fl / (peak_mm * 1e12), abytes / (HBM_PEAK_GBS * 1e9)) * 1e3
 
     traffic = None
@@ -597,11 +602,15 @@ def main():
                           "halves; executed: the MFMA instructions the kernel issues",
         "plan": plan,
         "stage_us": {"prep": round(stage_ms[1] * 1e3, 2), "walk": round(stage_ms[2] * 1e3, 2),
-                     "walk_per_launch_in_steps": round(walk_in_step_ms * 1e3, 2)},
+                     "walk_per_launch_in_steps": round(walk_in_step_ms * 1e3, 2),
+                     "note": "walk: the walk launches back to back (the roofline's figure); "
+                             "walk_per_launch_in_steps: a stage-1 launch and an event pair around each "
+                             "walk launch (events between launches slow the launches down)"},
         "roofline": {
             "kernel": plan["walk"],
             "bound": "hbm",
             "achieved": round(achieved_gbs, 1),
+            "kernel_us": round(stage_ms[2] * 1e3, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
@@ -616,7 +625,7 @@ def main():
     if machine is not None:
         # the same rates against what the chip reaches: the walk's FLOPs per launch over
         # the measured dense bf16 rate, its clock against the clock under that rate
-        machine["walk_tflops_pages"] = round(fl / (walk_in_step_ms * 1e-3) / 1e12, 1)
+        machine["walk_tflops_pages"] = round(fl / (stage_ms[2] * 1e-3) / 1e12, 1)
         machine["walk_frac_of_measured_mfma"] = round(machine["walk_tflops_pages"] / machine["mfma_bf16_tflops"], 4)
         machine["walk_frac_of_measured_copy"] = round(achieved_gbs / machine["hbm_copy_gbs"], 4)
         result["measured_peaks"] = machine
