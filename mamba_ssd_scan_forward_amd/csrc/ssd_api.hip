@@ -431,9 +431,12 @@ int ssd_plan_describe(const ssd_problem* p, char* buf, size_t len) {
     if (pl.fused) {
         snprintf(walk, sizeof walk, "ssd_walk_fused_kernel<%d, %d>", (int)p->dstate, pl.fused);
         prep = "none";
-        if (pl.fseg > 2)
-            summary = p->dstate == 64 ? "ssd_seg_summary_kernel<64>+ssd_seg_combine_kernel"
-                                      : "ssd_seg_summary_kernel<128>+ssd_seg_combine_kernel";
+        if (pl.fseg > 2 + ssd::kScanSeg)
+            summary = p->dstate == 64 ? "ssd_seg_summary_kernel<64>+ssd_seg_scan_kernel"
+                                      : "ssd_seg_summary_kernel<128>+ssd_seg_scan_kernel";
+        else if (pl.fseg > 2)
+            summary = p->dstate == 64 ? "ssd_seg_summary_kernel<64>+ssd_seg_chain_kernel"
+                                      : "ssd_seg_summary_kernel<128>+ssd_seg_chain_kernel";
         else if (pl.fseg == 2)
             summary = p->dstate == 64 ? "ssd_seg_summary_kernel<64>" : "ssd_seg_summary_kernel<128>";
     } else if (pl.npass == 2) {
@@ -534,11 +537,22 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
             sa.nitems = (int)pl.sum_items;
             hipLaunchKernelGGL(pl.sum_fn, dim3((unsigned)pl.sum_items), dim3(ssd::kSumThreads), 0, stream, sa);
             if (pl.fseg > 2) {
-                const int64_t n4 = p->nseq * H * P * N / 4;
-                const int64_t cblocks = (n4 + 255) / 256 < 8192 ? (n4 + 255) / 256 : 8192;
-                hipLaunchKernelGGL(ssd::ssd_seg_combine_kernel, dim3((unsigned)cblocks), dim3(256), 0, stream,
-                                   static_cast<const float*>(sa.loc), static_cast<const float*>(sa.dsum), sinit,
-                                   (int)p->nseq, pl.fseg, (int)H, (int)(P * N));
+                // one workgroup per (256 state elements, head, sequence); P N is a multiple of
+                // 256 on this path (P a multiple of 32, N 64 or 128), and a segmented plan has
+                // fewer workgroups than compute units, so fewer sequences and heads than the
+                // grid's y and z limits
+                if (pl.fseg - 2 > ssd::kScanSeg) {
+                    hipLaunchKernelGGL(ssd::ssd_seg_scan_kernel, dim3((unsigned)(P * N / 256), (unsigned)H, (unsigned)p->nseq),
+                                       dim3(64 * ssd::kScanSeg), 0, stream, static_cast<const float*>(sa.loc),
+                                       static_cast<const float*>(sa.dsum), sinit, (int)p->nseq, pl.fseg, (int)H,
+                                       (int)(P * N));
+                } else {
+                    const int64_t n4 = p->nseq * H * P * N / 4;
+                    const int64_t cblocks = (n4 + 255) / 256 < 8192 ? (n4 + 255) / 256 : 8192;
+                    hipLaunchKernelGGL(ssd::ssd_seg_chain_kernel, dim3((unsigned)cblocks), dim3(256), 0, stream,
+                                       static_cast<const float*>(sa.loc), static_cast<const float*>(sa.dsum), sinit,
+                                       (int)p->nseq, pl.fseg, (int)H, (int)(P * N));
+                }
             }
         }
         if (!(stages & 2)) return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;

@@ -11,7 +11,9 @@
 //            sequence's initial state h_0 instead, which gives the second one's entry
 //            state h_1 = exp(D_0) h_0 + loc_0 directly;
 //   combine  (three segments or more) the entry states of the others,
-//                h_{s+1} = exp(D_s) h_s + loc_s;
+//                h_{s+1} = exp(D_s) h_s + loc_s,
+//            one segment after the other for short chains, as an associative scan of
+//            the (decay, state) pairs for long ones;
 //   walk     the fused walker with every segment a sequence of its own, entering with
 //            h_s (the first with h_0 itself); the last segment's final state is the
 //            sequence's.
@@ -284,10 +286,71 @@ __global__ void __launch_bounds__(kSumThreads, 1) ssd_seg_summary_kernel(SegSumA
     if (c0 == 0 && lane == 0) a.dsum[slot] = carry;
 }
 
-// Entry states of the third segment on: h_{s+1} = exp(D_s) h_s + loc_s from h_1 (which the
-// summary of the first segment wrote), for every (sequence, head) and 4 consecutive state
-// elements per thread.
-__global__ void __launch_bounds__(256) ssd_seg_combine_kernel(const float* loc, const float* dsum, float* seg_init,
+// Entry states of the third segment on, by an associative scan over the segments (page
+// "Transformers are SSMs" paper summary, Appendix B: the recurrence's step from one piece of
+// the sequence to the next is the affine map h -> a h + b, and composing two of them,
+// (a2, b2) after (a1, b1) = (a2 a1, a2 b1 + b2), is associative, so the entry states of all
+// pieces are an inclusive scan of these pairs).  Segment s (1 <= s <= nseg - 2) contributes
+// (exp(D_s), loc_s); with h_1 (which the first segment's summary wrote),
+//     h_{s+1} = A_s h_1 + B_s,   (A_s, B_s) = (a_s, b_s) o ... o (a_1, b_1).
+// A workgroup takes one (sequence, head, 256 consecutive state elements): 64 lanes of 4
+// elements each by kScanSeg segment rows; the pairs of kScanSeg segments at a time are
+// scanned in log2(kScanSeg) steps (each row combines its pair with the one 1, 2, 4, 8 rows
+// earlier, through LDS), then applied to the entry state carried from the previous rows.
+// Used for chains longer than kScanSeg segments (a sequence cut into many segments: 64 of
+// 1024 rows, 8 heads, measured 89.3 -> 78.6 us for the whole forward against the chain
+// below); shorter chains take ssd_seg_chain_kernel (8 segments: 5 us faster).
+constexpr int kScanSeg = 16;
+__global__ void __launch_bounds__(64 * kScanSeg) ssd_seg_scan_kernel(const float* loc, const float* dsum,
+                                                                        float* seg_init, int nseq, int nseg, int H,
+                                                                        int PN) {
+    __shared__ float sa[kScanSeg][64];
+    __shared__ f32x4 sb[kScanSeg][64];
+    __shared__ f32x4 carry[64];
+    const int x = threadIdx.x & 63, j = threadIdx.x >> 6;
+    const int e = 256 * blockIdx.x + 4 * x;   // (PN is a multiple of 256)
+    const int h = blockIdx.y, b = blockIdx.z;
+    if (j == 0) carry[x] = *reinterpret_cast<const f32x4*>(seg_init + (((int64_t)b * nseg + 1) * H + h) * PN + e);
+    for (int c0 = 1; c0 + 1 < nseg; c0 += kScanSeg) {
+        const int s = c0 + j;
+        const bool valid = s + 1 < nseg;
+        float a = 1.f;
+        f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (valid) {
+            const int64_t slot = ((int64_t)b * (nseg - 1) + s) * H + h;
+            a = fast_exp2(dsum[slot] * kLog2e);
+            v = *reinterpret_cast<const f32x4*>(loc + slot * PN + e);
+        }
+        // inclusive scan over the rows: after the step of distance k, row j holds the
+        // composite of segments max(c0, s - 2k + 1) .. s
+#pragma unroll
+        for (int k = 1; k < kScanSeg; k *= 2) {
+            sa[j][x] = a;
+            sb[j][x] = v;
+            __syncthreads();
+            if (j >= k) {
+                const float ap = sa[j - k][x];
+                const f32x4 bp = sb[j - k][x];
+                v = f32x4{a * bp[0] + v[0], a * bp[1] + v[1], a * bp[2] + v[2], a * bp[3] + v[3]};
+                a *= ap;
+            }
+            __syncthreads();
+        }
+        // h_{s+1} from the entry state of segment c0 (h_1, or the previous rows' last)
+        const f32x4 hin = carry[x];
+        const f32x4 hout = f32x4{a * hin[0] + v[0], a * hin[1] + v[1], a * hin[2] + v[2], a * hin[3] + v[3]};
+        if (valid) *reinterpret_cast<f32x4*>(seg_init + (((int64_t)b * nseg + s + 1) * H + h) * PN + e) = hout;
+        __syncthreads();
+        if (j == kScanSeg - 1) carry[x] = hout;   // (only read when another pass follows: then every row was valid)
+        __syncthreads();
+    }
+}
+
+// Entry states of the third segment on for chains of at most kScanSeg segments, one after
+// the other: h_{s+1} = exp(D_s) h_s + loc_s from h_1 (which the summary of the first segment
+// wrote), for every (sequence, head) and 4 consecutive state elements per thread (its loads
+// of every segment independent of each other, so all of them are in flight at once).
+__global__ void __launch_bounds__(256) ssd_seg_chain_kernel(const float* loc, const float* dsum, float* seg_init,
                                                               int nseq, int nseg, int H, int PN) {
     const int n4 = PN / 4;
     const int64_t total = (int64_t)nseq * H * n4;
@@ -305,5 +368,6 @@ __global__ void __launch_bounds__(256) ssd_seg_combine_kernel(const float* loc, 
         }
     }
 }
+
 
 }  // namespace ssd

@@ -303,6 +303,11 @@ def test_plan_long_sequences_and_state_256():
     # one long sequence: segments of the fused walker, after their summary
     long = ssd.ssd_plan_describe(ssd.problem_for(1, 16384, 80, 64, 128, 1, 256, 1, bf16))
     assert long["walk"] == "ssd_walk_fused_kernel<128, 5>" and long["summary"].startswith("ssd_seg_summary_kernel<128>")
+    # its eight segments' entry states chained one after the other; many segments (64 of
+    # 1024 rows for eight heads) by the associative scan over the segments
+    assert long["summary"].endswith("ssd_seg_chain_kernel")
+    many = ssd.ssd_plan_describe(ssd.problem_for(1, 65536, 8, 64, 128, 1, 256, 1, bf16))
+    assert many["summary"] == "ssd_seg_summary_kernel<128>+ssd_seg_scan_kernel", many
     # d_state 256 on the fused walker where no segments are needed ...
     wide = ssd.ssd_plan_describe(ssd.problem_for(32, 300, 8, 64, 256, 1, 256, 32, bf16))
     assert wide == {"walk": "ssd_walk_fused_kernel<256, 2>", "prep": "none", "summary": "none"}

@@ -360,7 +360,7 @@ def test_library_loaded_before_the_first_gpu_use():
 # that renormalise or take the exact form inside segments), and one packed sequence given
 # through seq_offsets.
 @pytest.mark.parametrize("case", ["n128_init", "groups2", "n64_batch2", "groups3", "p128", "strong_decay",
-                                  "a_one", "a_zero", "packed_one"])
+                                  "a_one", "a_zero", "packed_one", "weak_decay", "many_segments"])
 def test_segmented_fused_walk(case):
     if case == "n128_init":
         inp = make_inputs(1, 8292, 16, 64, 128, 1, "bf16", seed=1500, init_state=True)
@@ -383,10 +383,22 @@ def test_segmented_fused_walk(case):
         # total decay: every state is forgotten at once (weights and totals underflow to 0)
         inp = make_inputs(1, 8292, 16, 64, 64, 1, "bf16", seed=1508, init_state=True)
         inp.logA[:] = -1e4
+    elif case == "weak_decay":
+        # 29 segments (the entry states by the associative scan over segments) with decays
+        # weak enough that each segment's entry state carries the earlier ones
+        inp = make_inputs(1, 8292, 16, 64, 128, 1, "bf16", seed=1509, init_state=True)
+        inp.logA = (inp.logA * 0.01).astype(np.float32)
+    elif case == "many_segments":
+        # 64 segments of 1024 rows: the scan in four passes of 16 segments, each carrying
+        # the last entry state of the one before
+        inp = make_inputs(1, 65536, 8, 64, 128, 1, "bf16", seed=1510, init_state=True)
+        inp.logA = (inp.logA * 0.01).astype(np.float32)
     else:
         inp = make_inputs(1, 8292, 16, 64, 128, 1, "bf16", seed=1506, init_state=True, seq_lengths=[8292])
     plan = plan_of(inp, 256)
     assert plan["walk"].startswith("ssd_walk_fused_kernel") and plan["summary"].startswith("ssd_seg_summary"), plan
+    if case in ("weak_decay", "many_segments", "a_one"):
+        assert plan["summary"].endswith("ssd_seg_scan_kernel"), plan
     check(inp, 256, case)
 
 
