@@ -46,6 +46,7 @@ struct Plan {
     int fused_wpg;    // its workgroups per group
     int64_t fused_items;
     void (*fused_fn)(ssd::FusedArgs);
+    void (*fused_pair_fn)(ssd::FusedArgs, ssd::FusedArgs, int);   // two walks of the shape in one launch
     int fseg, fseglen;   // the fused walker's segments per sequence (1: none) and their rows
     size_t loc_off, dsum_off, sinit_off;   // segment end states, log decays, entry states
     int sum_wpg;
@@ -140,6 +141,17 @@ walk_fn pick_walk_bf16(int PT, int NP, bool cbl) {
 // is used when its workgroups, segments counted, fill at least half the chip (d_state
 // 256: without segments).
 typedef void (*fused_fn_t)(ssd::FusedArgs);
+typedef void (*fused_pair_fn_t)(ssd::FusedArgs, ssd::FusedArgs, int);
+// the two-walk launch, for the shapes of the backward pass's dB and dC passes (head dimension
+// the layer's d_state, d_state the layer's head dimension: 64 or 128)
+template <int NP>
+fused_pair_fn_t fused_pair_instance(int nw) {
+    switch (nw) {
+        case 4: return ssd::ssd_walk_fused_pair_kernel<NP, 4>;
+        case 5: return ssd::ssd_walk_fused_pair_kernel<NP, 5>;
+    }
+    return nullptr;
+}
 template <int NP>
 fused_fn_t fused_instance(int nw) {
     if constexpr (NP == 256) {
@@ -219,6 +231,7 @@ bool plan_fused(const ssd_problem* p, Plan* pl) {
     pl->fused_wpg = (int)best_wpg;
     pl->fused_items = best_items;
     pl->fused_fn = N == 64 ? fused_instance<64>(best) : N == 128 ? fused_instance<128>(best) : fused_instance<256>(best);
+    pl->fused_pair_fn = N == 64 ? fused_pair_instance<64>(best) : N == 128 ? fused_pair_instance<128>(best) : nullptr;
     pl->fseg = best_seg;
     pl->fseglen = best_sl;
     size_t ws = 256;
@@ -468,10 +481,22 @@ namespace {
 
 // stages: bit 0 = prep launch, bit 1 = walk launch.  x_heads: X rows per token (the
 // heads share them in contiguous runs of H / x_heads); 0 means one per head.
+// A fused walk prepared but not launched, for the caller to launch with another (the
+// backward pass's dB and dC passes); captured = false when the plan was launched as usual.
+struct FusedCapture {
+    bool captured;
+    ssd::FusedArgs a;
+    int64_t grid;
+    int nw;
+    fused_fn_t fn;
+    fused_pair_fn_t pair;
+};
+
 int run_forward(int stages, const ssd_problem* p, const void* X, const float* logA, const void* B,
                 const void* C, const float* init_state, const int32_t* seq_offsets, void* Y,
                 float* final_state, void* workspace, size_t workspace_bytes, void* hip_stream,
-                int64_t x_heads = 0) {
+                int64_t x_heads = 0, FusedCapture* cap = nullptr) {
+    if (cap) cap->captured = false;
     Plan pl;
     int rc = make_plan(p, &pl);
     if (rc != SSD_OK) return rc;
@@ -584,6 +609,15 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
         fa.lpt = (!seg && seq_offsets && p->nseq <= 64) ? 1 : 0;
         int64_t grid = pl.fused_items;
         if (fa.lpt) grid = ((p->nseq * G + 7) / 8) * 8 * pl.fused_wpg;
+        if (cap && !seg && pl.fused_pair_fn) {
+            cap->captured = true;
+            cap->a = fa;
+            cap->grid = grid;
+            cap->nw = pl.fused;
+            cap->fn = pl.fused_fn;
+            cap->pair = pl.fused_pair_fn;
+            return SSD_OK;
+        }
         hipLaunchKernelGGL(pl.fused_fn, dim3((unsigned)grid), dim3(64 * (pl.fused + 3)), 0, stream, fa);
         return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
     }

@@ -11,7 +11,7 @@ struct BwdPlan {
     ssd_problem p1;   // dX pass: the layer's own shape
     ssd_problem p2;   // dB and dC passes: head dimension N, state P, one group per head
     size_t fws_bytes;
-    size_t la, revdy, revc, revb, tmpp, rr, revx, tmpn, st, bytes;
+    size_t la, revdy, revc, revb, tmpp, rr, revx, tmpn, st, tmpn2, st2, bytes;
 };
 
 int make_bwd_plan(const ssd_problem* p, BwdPlan* bp) {
@@ -45,6 +45,9 @@ int make_bwd_plan(const ssd_problem* p, BwdPlan* bp) {
     bp->revx = take(rows * H * P * es);
     bp->tmpn = take(rows * H * N * es);
     bp->st = take(ns * H * P * N * 4);
+    // (the dC pass's own output and initial state: it may run in one launch with the dB pass)
+    bp->tmpn2 = take(rows * H * N * es);
+    bp->st2 = take(ns * H * P * N * 4);
     bp->bytes = o;
     return SSD_OK;
 }
@@ -119,6 +122,8 @@ int ssd_backward(const ssd_problem* p, const void* X, const float* logA, const v
     void* revx = ws + bp.revx;
     void* tmpn = ws + bp.tmpn;
     float* st = reinterpret_cast<float*>(ws + bp.st);
+    void* tmpn2 = ws + bp.tmpn2;
+    float* st2 = reinterpret_cast<float*>(ws + bp.st2);
     const ssd::RowMap fwd{seq_offsets, T, (int)nseq, 0}, rev{seq_offsets, T, (int)nseq, 1};
     const int segx = (int)(H * P * es / 16), segbc = (int)(G * N * es / 16);
     auto remap = [&](const void* in, void* out, int K, int Kin, int seg, const ssd::RowMap& m) {
@@ -168,16 +173,30 @@ int ssd_backward(const ssd_problem* p, const void* X, const float* logA, const v
     // C' = X, initial state dF^T
     remap(X, revx, 1, 1, segx, rev);
     if (dfinal) transpose(dfinal, st);
+    FusedCapture cb, cc;
     rc = run_forward(3, &bp.p2, revc, la, revdy, revx, dfinal ? st : nullptr, seq_offsets, tmpn, nullptr, ws,
-                     bp.fws_bytes, hip_stream, G);
+                     bp.fws_bytes, hip_stream, G, &cb);
     if (rc != SSD_OK) return rc;
-    group_sum(tmpn, dB, rev);
     // dC: forward time, X' = B (read per group), B' = X, C' = dY, initial state init^T
-    if (init_state) transpose(init_state, st);
-    rc = run_forward(3, &bp.p2, B, logA, X, dY, init_state ? st : nullptr, seq_offsets, tmpn, nullptr, ws,
-                     bp.fws_bytes, hip_stream, G);
+    if (init_state) transpose(init_state, st2);
+    rc = run_forward(3, &bp.p2, B, logA, X, dY, init_state ? st2 : nullptr, seq_offsets, tmpn2, nullptr, ws,
+                     bp.fws_bytes, hip_stream, G, &cc);
     if (rc != SSD_OK) return rc;
-    group_sum(tmpn, dC, fwd);
+    // the two passes as one launch where both are fused walks of the same kernel (each a
+    // walk of its own, with no workspace): fewer partial rounds of workgroups than two
+    if (cb.captured && cc.captured && cb.pair == cc.pair && cb.nw == cc.nw) {
+        const int64_t n0 = (cb.grid + 7) / 8 * 8;
+        if (n0 + cc.grid > INT32_MAX) return SSD_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL(cb.pair, dim3((unsigned)(n0 + cc.grid)), dim3(64 * (cb.nw + 3)), 0, stream, cb.a, cc.a,
+                           (int)n0);
+    } else {
+        if (cb.captured)
+            hipLaunchKernelGGL(cb.fn, dim3((unsigned)cb.grid), dim3(64 * (cb.nw + 3)), 0, stream, cb.a);
+        if (cc.captured)
+            hipLaunchKernelGGL(cc.fn, dim3((unsigned)cc.grid), dim3(64 * (cc.nw + 3)), 0, stream, cc.a);
+    }
+    group_sum(tmpn, dB, rev);
+    group_sum(tmpn2, dC, fwd);
     if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
     return SSD_OK;
 }

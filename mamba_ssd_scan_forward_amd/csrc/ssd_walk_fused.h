@@ -849,15 +849,16 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
     }
 }
 
+// Workgroup bid of nblocks (a multiple of 8 where sequences are dealt to XCDs) -> its
+// (sequence, group, run of units), then the walk.
 template <int NP, int NW>
-__global__ void __launch_bounds__(64 * (NW + 3), 1) ssd_walk_fused_kernel(FusedArgs a) {
+__device__ __forceinline__ void fused_item_walk(const FusedArgs& a, int bid, int nblocks) {
     const int lane = threadIdx.x & 63;
     const int G = a.G, wpg = a.wpg;
     int s, g, q;
     if (a.lpt) {
         // packed sequences: the (sequence, group) units are dealt to the XCDs
         // round-robin, longest sequence first
-        const int bid = blockIdx.x;
         const int xcd = bid % 8, slot = bid / 8;
         const int un = (slot / wpg) * 8 + xcd;
         q = slot % wpg;
@@ -877,7 +878,7 @@ __global__ void __launch_bounds__(64 * (NW + 3), 1) ssd_walk_fused_kernel(FusedA
         }
         s = __builtin_ctzll(__ballot(mine));
     } else {
-        const int item = xcd_remap(blockIdx.x, gridDim.x);
+        const int item = xcd_remap(bid, nblocks);
         if (item >= a.nitems) return;
         q = item % wpg;
         const int sg = item / wpg;
@@ -885,6 +886,22 @@ __global__ void __launch_bounds__(64 * (NW + 3), 1) ssd_walk_fused_kernel(FusedA
         s = sg / G;
     }
     fused_walk<NP, NW>(a, s, g, q);
+}
+
+template <int NP, int NW>
+__global__ void __launch_bounds__(64 * (NW + 3), 1) ssd_walk_fused_kernel(FusedArgs a) {
+    fused_item_walk<NP, NW>(a, blockIdx.x, gridDim.x);
+}
+
+// Two independent walks of one shape in one launch (the backward pass's dB and dC passes):
+// workgroups [0, n0) walk a0, the rest a1.  n0 is a multiple of 8, so that both ranges meet
+// the XCDs alike; the two together leave fewer partial rounds of workgroups over the chip
+// than two launches.
+template <int NP, int NW>
+__global__ void __launch_bounds__(64 * (NW + 3), 1) ssd_walk_fused_pair_kernel(FusedArgs a0, FusedArgs a1, int n0) {
+    const bool second = (int)blockIdx.x >= n0;
+    const FusedArgs a = second ? a1 : a0;
+    fused_item_walk<NP, NW>(a, second ? (int)blockIdx.x - n0 : (int)blockIdx.x, second ? (int)gridDim.x - n0 : n0);
 }
 
 }  // namespace ssd
