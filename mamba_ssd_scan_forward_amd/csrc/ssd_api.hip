@@ -166,8 +166,10 @@ fused_fn_t fused_instance(int nw) {
         switch (nw) {
             case 4: return ssd::ssd_walk_fused_kernel<NP, 4>;
             case 5: return ssd::ssd_walk_fused_kernel<NP, 5>;
-            case 6: return ssd::ssd_walk_fused_kernel<NP, 6>;
         }
+        // (six compute waves only at d_state 64: the planner never takes them at 128)
+        if constexpr (NP == 64)
+            if (nw == 6) return ssd::ssd_walk_fused_kernel<64, 6>;
         return nullptr;
     }
 }
