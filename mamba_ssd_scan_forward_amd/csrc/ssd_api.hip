@@ -144,12 +144,25 @@ typedef void (*fused_fn_t)(ssd::FusedArgs);
 typedef void (*fused_pair_fn_t)(ssd::FusedArgs, ssd::FusedArgs, int);
 // the two-walk launch, for the shapes of the backward pass's dB and dC passes (head dimension
 // the layer's d_state, d_state the layer's head dimension: 64 or 128)
-template <int NP>
+template <int NP, bool REV0, bool REV1>
 fused_pair_fn_t fused_pair_instance(int nw) {
     switch (nw) {
-        case 4: return ssd::ssd_walk_fused_pair_kernel<NP, 4>;
-        case 5: return ssd::ssd_walk_fused_pair_kernel<NP, 5>;
+        case 4: return ssd::ssd_walk_fused_pair_kernel<NP, 4, REV0, REV1>;
+        case 5: return ssd::ssd_walk_fused_pair_kernel<NP, 5, REV0, REV1>;
     }
+    return nullptr;
+}
+// a pair of walks of d_state NP: both forward, or the first reversed (the backward pass's dB
+// pass) and the second forward (its dC pass)
+fused_pair_fn_t fused_pair_for(int np, int nw, bool rev0) {
+    if (np == 64) return rev0 ? fused_pair_instance<64, true, false>(nw) : fused_pair_instance<64, false, false>(nw);
+    if (np == 128) return rev0 ? fused_pair_instance<128, true, false>(nw) : fused_pair_instance<128, false, false>(nw);
+    return nullptr;
+}
+// the walker over reversed sequences (the backward pass's dX and dB passes)
+fused_fn_t fused_rev_for(int np, int nw) {
+    if (np == 64) return nw == 4 ? ssd::ssd_walk_fused_kernel<64, 4, true> : nw == 5 ? ssd::ssd_walk_fused_kernel<64, 5, true> : nullptr;
+    if (np == 128) return nw == 4 ? ssd::ssd_walk_fused_kernel<128, 4, true> : nw == 5 ? ssd::ssd_walk_fused_kernel<128, 5, true> : nullptr;
     return nullptr;
 }
 template <int NP>
@@ -233,7 +246,7 @@ bool plan_fused(const ssd_problem* p, Plan* pl) {
     pl->fused_wpg = (int)best_wpg;
     pl->fused_items = best_items;
     pl->fused_fn = N == 64 ? fused_instance<64>(best) : N == 128 ? fused_instance<128>(best) : fused_instance<256>(best);
-    pl->fused_pair_fn = N == 64 ? fused_pair_instance<64>(best) : N == 128 ? fused_pair_instance<128>(best) : nullptr;
+    pl->fused_pair_fn = fused_pair_for((int)N, best, false);
     pl->fseg = best_seg;
     pl->fseglen = best_sl;
     size_t ws = 256;
@@ -490,18 +503,20 @@ struct FusedCapture {
     ssd::FusedArgs a;
     int64_t grid;
     int nw;
+    int np;           // d_state
+    bool rev;         // the walk over reversed sequences
     fused_fn_t fn;
-    fused_pair_fn_t pair;
 };
 
 int run_forward(int stages, const ssd_problem* p, const void* X, const float* logA, const void* B,
                 const void* C, const float* init_state, const int32_t* seq_offsets, void* Y,
                 float* final_state, void* workspace, size_t workspace_bytes, void* hip_stream,
-                int64_t x_heads = 0, FusedCapture* cap = nullptr) {
+                int64_t x_heads = 0, FusedCapture* cap = nullptr, bool reversed = false) {
     if (cap) cap->captured = false;
     Plan pl;
     int rc = make_plan(p, &pl);
     if (rc != SSD_OK) return rc;
+    if (reversed && (!pl.fused || pl.fseg > 1 || !fused_rev_for((int)p->dstate, pl.fused))) return SSD_ERR_UNSUPPORTED;
     if (!X || !logA || !B || !C || !Y || !workspace) return SSD_ERR_INVALID_ARG;
     if (seq_offsets) {
         if (p->batch != 1) return SSD_ERR_INVALID_ARG;
@@ -611,16 +626,20 @@ int run_forward(int stages, const ssd_problem* p, const void* X, const float* lo
         fa.lpt = (!seg && seq_offsets && p->nseq <= 64) ? 1 : 0;
         int64_t grid = pl.fused_items;
         if (fa.lpt) grid = ((p->nseq * G + 7) / 8) * 8 * pl.fused_wpg;
+        // (reversed sequences: the backward pass's own form, only for plans without segments)
+        const fused_fn_t fn = reversed ? fused_rev_for((int)N, pl.fused) : pl.fused_fn;
+        if (!fn || (reversed && seg)) return SSD_ERR_UNSUPPORTED;
         if (cap && !seg && pl.fused_pair_fn) {
             cap->captured = true;
             cap->a = fa;
             cap->grid = grid;
             cap->nw = pl.fused;
-            cap->fn = pl.fused_fn;
-            cap->pair = pl.fused_pair_fn;
+            cap->np = (int)N;
+            cap->rev = reversed;
+            cap->fn = fn;
             return SSD_OK;
         }
-        hipLaunchKernelGGL(pl.fused_fn, dim3((unsigned)grid), dim3(64 * (pl.fused + 3)), 0, stream, fa);
+        hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * (pl.fused + 3)), 0, stream, fa);
         return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
     }
     walk_fn walk = pl.walk;

@@ -145,57 +145,90 @@ int ssd_backward(const ssd_problem* p, const void* X, const float* logA, const v
                            in, out, nseq * H, (int)P, (int)N);
     };
 
-    // dX and dinit: the reversed pass
-    remap(dY, revdy, 1, 1, segx, rev);
-    remap(C, revc, 1, 1, segbc, rev);
-    remap(B, revb, 1, 1, segbc, rev);
-    hipLaunchKernelGGL(ssd::ssd_bwd_logA_kernel, dim3(grid_for(rows * H)), dim3(256), 0, stream, logA, la, rows,
-                       (int)H, rev);
-    rc = run_forward(3, &bp.p1, revdy, la, revc, revb, dfinal, seq_offsets, tmpp, dinit, ws, bp.fws_bytes,
-                     hip_stream);
-    if (rc != SSD_OK) return rc;
-    remap(tmpp, dX, 1, 1, segx, rev);
-    if (dinit)
-        hipLaunchKernelGGL(ssd::ssd_bwd_dinit_kernel, dim3(grid_for(nseq * H * P * N)), dim3(256), 0, stream, dinit,
-                           logA, T, seq_offsets, (int)nseq, (int)H, (int)(P * N));
-    // dlogA
-    if (p->dtype == SSD_DTYPE_BF16)
-        hipLaunchKernelGGL(ssd::ssd_bwd_dot_kernel<__bf16>, dim3(grid_for(rows * H * P / 8)), dim3(256), 0, stream,
-                           static_cast<const __bf16*>(dY), static_cast<const __bf16*>(Y),
-                           static_cast<const __bf16*>(X), static_cast<const __bf16*>(dX), rr, rows, (int)H, (int)P);
-    else
-        hipLaunchKernelGGL(ssd::ssd_bwd_dot_kernel<float>, dim3(grid_for(rows * H * P / 8)), dim3(256), 0, stream,
-                           static_cast<const float*>(dY), static_cast<const float*>(Y),
-                           static_cast<const float*>(X), static_cast<const float*>(dX), rr, rows, (int)H, (int)P);
-    hipLaunchKernelGGL(ssd::ssd_bwd_dlogA_kernel, dim3((unsigned)(nseq * H)), dim3(64), 0, stream, rr, dfinal,
-                       final_state, dlogA, T, seq_offsets, (int)H, (int)(P * N));
-    // dB: reversed, X' = C (the reversed copy of the dX pass, read per group), B' = dY,
-    // C' = X, initial state dF^T
-    remap(X, revx, 1, 1, segx, rev);
-    if (dfinal) transpose(dfinal, st);
+    // The reversed passes read and write the sequences in place, from their last row to
+    // their first, where both plans are fused walks without segments (the walker's reversed
+    // form); otherwise they run on reversed copies of the operands.
+    bool in_place = false;
+    {
+        Plan a1, a2;
+        in_place = make_plan(&bp.p1, &a1) == SSD_OK && make_plan(&bp.p2, &a2) == SSD_OK && a1.fused && a2.fused &&
+                   a1.fseg == 1 && a2.fseg == 1 && fused_rev_for((int)bp.p1.dstate, a1.fused) &&
+                   fused_rev_for((int)bp.p2.dstate, a2.fused);
+    }
+    auto dot_and_dlogA = [&]() {
+        // dlogA
+        if (p->dtype == SSD_DTYPE_BF16)
+            hipLaunchKernelGGL(ssd::ssd_bwd_dot_kernel<__bf16>, dim3(grid_for(rows * H * P / 8)), dim3(256), 0, stream,
+                               static_cast<const __bf16*>(dY), static_cast<const __bf16*>(Y),
+                               static_cast<const __bf16*>(X), static_cast<const __bf16*>(dX), rr, rows, (int)H, (int)P);
+        else
+            hipLaunchKernelGGL(ssd::ssd_bwd_dot_kernel<float>, dim3(grid_for(rows * H * P / 8)), dim3(256), 0, stream,
+                               static_cast<const float*>(dY), static_cast<const float*>(Y),
+                               static_cast<const float*>(X), static_cast<const float*>(dX), rr, rows, (int)H, (int)P);
+        hipLaunchKernelGGL(ssd::ssd_bwd_dlogA_kernel, dim3((unsigned)(nseq * H)), dim3(64), 0, stream, rr, dfinal,
+                           final_state, dlogA, T, seq_offsets, (int)H, (int)(P * N));
+    };
+    auto dinit_scale = [&]() {
+        if (dinit)
+            hipLaunchKernelGGL(ssd::ssd_bwd_dinit_kernel, dim3(grid_for(nseq * H * P * N)), dim3(256), 0, stream,
+                               dinit, logA, T, seq_offsets, (int)nseq, (int)H, (int)(P * N));
+    };
     FusedCapture cb, cc;
-    rc = run_forward(3, &bp.p2, revc, la, revdy, revx, dfinal ? st : nullptr, seq_offsets, tmpn, nullptr, ws,
-                     bp.fws_bytes, hip_stream, G, &cb);
-    if (rc != SSD_OK) return rc;
+    if (in_place) {
+        // dX and dinit: X' = dY, B' = C, C' = B, initial state dF, walked in reverse
+        rc = run_forward(3, &bp.p1, dY, logA, C, B, dfinal, seq_offsets, dX, dinit, ws, bp.fws_bytes, hip_stream, 0,
+                         nullptr, true);
+        if (rc != SSD_OK) return rc;
+        dinit_scale();
+        dot_and_dlogA();
+        // dB: walked in reverse, X' = C (read per group), B' = dY, C' = X, initial state dF^T
+        if (dfinal) transpose(dfinal, st);
+        rc = run_forward(3, &bp.p2, C, logA, dY, X, dfinal ? st : nullptr, seq_offsets, tmpn, nullptr, ws,
+                         bp.fws_bytes, hip_stream, G, &cb, true);
+        if (rc != SSD_OK) return rc;
+    } else {
+        // dX and dinit: the reversed pass
+        remap(dY, revdy, 1, 1, segx, rev);
+        remap(C, revc, 1, 1, segbc, rev);
+        remap(B, revb, 1, 1, segbc, rev);
+        hipLaunchKernelGGL(ssd::ssd_bwd_logA_kernel, dim3(grid_for(rows * H)), dim3(256), 0, stream, logA, la, rows,
+                           (int)H, rev);
+        rc = run_forward(3, &bp.p1, revdy, la, revc, revb, dfinal, seq_offsets, tmpp, dinit, ws, bp.fws_bytes,
+                         hip_stream);
+        if (rc != SSD_OK) return rc;
+        remap(tmpp, dX, 1, 1, segx, rev);
+        dinit_scale();
+        dot_and_dlogA();
+        // dB: reversed, X' = C (the reversed copy of the dX pass, read per group), B' = dY,
+        // C' = X, initial state dF^T
+        remap(X, revx, 1, 1, segx, rev);
+        if (dfinal) transpose(dfinal, st);
+        rc = run_forward(3, &bp.p2, revc, la, revdy, revx, dfinal ? st : nullptr, seq_offsets, tmpn, nullptr, ws,
+                         bp.fws_bytes, hip_stream, G, &cb);
+        if (rc != SSD_OK) return rc;
+    }
     // dC: forward time, X' = B (read per group), B' = X, C' = dY, initial state init^T
     if (init_state) transpose(init_state, st2);
     rc = run_forward(3, &bp.p2, B, logA, X, dY, init_state ? st2 : nullptr, seq_offsets, tmpn2, nullptr, ws,
                      bp.fws_bytes, hip_stream, G, &cc);
     if (rc != SSD_OK) return rc;
-    // the two passes as one launch where both are fused walks of the same kernel (each a
+    // the dB and dC passes as one launch where both are fused walks of one shape (each a
     // walk of its own, with no workspace): fewer partial rounds of workgroups than two
-    if (cb.captured && cc.captured && cb.pair == cc.pair && cb.nw == cc.nw) {
+    const fused_pair_fn_t pair =
+        (cb.captured && cc.captured && !cc.rev && cb.np == cc.np && cb.nw == cc.nw) ? fused_pair_for(cb.np, cb.nw, cb.rev)
+                                                                                   : nullptr;
+    if (pair) {
         const int64_t n0 = (cb.grid + 7) / 8 * 8;
         if (n0 + cc.grid > INT32_MAX) return SSD_ERR_UNSUPPORTED;
-        hipLaunchKernelGGL(cb.pair, dim3((unsigned)(n0 + cc.grid)), dim3(64 * (cb.nw + 3)), 0, stream, cb.a, cc.a,
-                           (int)n0);
+        hipLaunchKernelGGL(pair, dim3((unsigned)(n0 + cc.grid)), dim3(64 * (cb.nw + 3)), 0, stream, cb.a, cc.a, (int)n0);
     } else {
         if (cb.captured)
             hipLaunchKernelGGL(cb.fn, dim3((unsigned)cb.grid), dim3(64 * (cb.nw + 3)), 0, stream, cb.a);
         if (cc.captured)
             hipLaunchKernelGGL(cc.fn, dim3((unsigned)cc.grid), dim3(64 * (cc.nw + 3)), 0, stream, cc.a);
     }
-    group_sum(tmpn, dB, rev);
+    // per-group sums over the heads (the copied dB pass wrote its rows reversed)
+    group_sum(tmpn, dB, in_place ? fwd : rev);
     group_sum(tmpn2, dC, fwd);
     if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
     return SSD_OK;

@@ -211,7 +211,35 @@ __device__ __forceinline__ float lane_f(float x, int l) {
 // position of row s (0..31) in the sigma order of the K index (bits 2 and 3 swapped)
 __device__ __forceinline__ int sigma_pos(int s) { return (s & 19) | ((s & 4) << 1) | ((s & 8) >> 1); }
 
+// The walker's LDS: separate arrays (ring slots, product buffers, Y staging), so that the
+// compiler can tell the slot a direct-to-LDS load is filling from the slot being read.
+struct FusedSmem {
+    lds_ptr cring, bring;   // one array per ring: [nslot][bcbytes]
+    lds_ptr x[4], l[4], m[4], p[2], ys[2];
+};
 template <int NP, int NW>
+__device__ __forceinline__ FusedSmem fused_smem() {
+    typedef FusedLds<NP, NW> LL;
+    constexpr int NSL = LL::nslot;
+    __shared__ __align__(16) unsigned char cring[NSL][LL::bcbytes], bring[NSL][LL::bcbytes];
+    __shared__ __align__(16) unsigned char x0[LL::xbytes], x1[LL::xbytes], x2[LL::xbytes], x3[NSL == 4 ? LL::xbytes : 16];
+    __shared__ __align__(16) unsigned char l0[LL::labytes], l1[LL::labytes], l2[LL::labytes], l3[NSL == 4 ? LL::labytes : 16];
+    __shared__ __align__(16) unsigned char m0[LL::labytes], m1[LL::labytes], m2[LL::labytes], m3[NSL == 4 ? LL::labytes : 16];
+    __shared__ __align__(16) unsigned char p0[LL::prod], p1[LL::prod];
+    __shared__ __align__(16) unsigned char ys0[LL::ybytes], ys1[LL::ybytes];
+    return FusedSmem{(lds_ptr)cring[0], (lds_ptr)bring[0],
+                     {(lds_ptr)x0, (lds_ptr)x1, (lds_ptr)x2, (lds_ptr)x3},
+                     {(lds_ptr)l0, (lds_ptr)l1, (lds_ptr)l2, (lds_ptr)l3},
+                     {(lds_ptr)m0, (lds_ptr)m1, (lds_ptr)m2, (lds_ptr)m3},
+                     {(lds_ptr)p0, (lds_ptr)p1},
+                     {(lds_ptr)ys0, (lds_ptr)ys1}};
+}
+
+// REV: the sequences walked from their last row to their first, each row's decay that of
+// the row after it (the first walked row's decay 0): the reversed problem of the backward
+// pass, read and written in place (rows outside the sequence fall outside the buffers'
+// ranges, so their loads read 0 and their stores are dropped).
+template <int NP, int NW, bool REV>
 __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
                                            int g, int q) {
     typedef FusedLds<NP, NW> LL;
@@ -221,21 +249,18 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
     // index (a constant table of LDS addresses cannot be emitted)
     // (B and C: one array per ring, so that a compute wave reads any slot at an immediate
     // offset from one per-lane address)
-    __shared__ __align__(16) unsigned char cring[NSL][LL::bcbytes], bring[NSL][LL::bcbytes];
-    __shared__ __align__(16) unsigned char x0[LL::xbytes], x1[LL::xbytes], x2[LL::xbytes], x3[NSL == 4 ? LL::xbytes : 16];
-    __shared__ __align__(16) unsigned char l0[LL::labytes], l1[LL::labytes], l2[LL::labytes], l3[NSL == 4 ? LL::labytes : 16];
-    __shared__ __align__(16) unsigned char m0[LL::labytes], m1[LL::labytes], m2[LL::labytes], m3[NSL == 4 ? LL::labytes : 16];
-    __shared__ __align__(16) unsigned char p0[LL::prod], p1[LL::prod];
-    __shared__ __align__(16) unsigned char ys0[LL::ybytes], ys1[LL::ybytes];
-    auto pick = [](int k, unsigned char* a0, unsigned char* a1, unsigned char* a2, unsigned char* a3)
+    // (declared in fused_smem, which does not depend on REV: both directions of a two-walk
+    // launch use the one set of arrays)
+    const FusedSmem sm = fused_smem<NP, NW>();
+    auto pick = [](int k, lds_ptr a0, lds_ptr a1, lds_ptr a2, lds_ptr a3)
                     __attribute__((always_inline)) -> lds_ptr {
-        return k == 0 ? (lds_ptr)a0 : k == 1 ? (lds_ptr)a1 : k == 2 ? (lds_ptr)a2 : (lds_ptr)a3;
+        return k == 0 ? a0 : k == 1 ? a1 : k == 2 ? a2 : a3;
     };
-    auto XS = [&](int k) __attribute__((always_inline)) { return pick(k, x0, x1, x2, x3); };
-    auto BS = [&](int k) __attribute__((always_inline)) { return (lds_ptr)bring[k]; };
-    auto CS = [&](int k) __attribute__((always_inline)) { return (lds_ptr)cring[k]; };
-    auto LA = [&](int k) __attribute__((always_inline)) { return pick(k, l0, l1, l2, l3); };
-    auto LA2 = [&](int k) __attribute__((always_inline)) { return pick(k, m0, m1, m2, m3); };
+    auto XS = [&](int k) __attribute__((always_inline)) { return pick(k, sm.x[0], sm.x[1], sm.x[2], sm.x[3]); };
+    auto BS = [&](int k) __attribute__((always_inline)) { return sm.bring + k * LL::bcbytes; };
+    auto CS = [&](int k) __attribute__((always_inline)) { return sm.cring + k * LL::bcbytes; };
+    auto LA = [&](int k) __attribute__((always_inline)) { return pick(k, sm.l[0], sm.l[1], sm.l[2], sm.l[3]); };
+    auto LA2 = [&](int k) __attribute__((always_inline)) { return pick(k, sm.m[0], sm.m[1], sm.m[2], sm.m[3]); };
 
     typedef Elem<__bf16> E;
     typedef FusedLds<NP, NW> L;
@@ -295,8 +320,8 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
     const int64_t xrow = (int64_t)H * P;   // elements per token row of X / Y
 
     // ---- per-block product buffers and Y staging
-    auto pbuf = [&](int t) __attribute__((always_inline)) -> lds_ptr { return (t & 1) ? (lds_ptr)p1 : (lds_ptr)p0; };
-    auto ybuf = [&](int t) __attribute__((always_inline)) -> lds_ptr { return (t & 1) ? (lds_ptr)ys1 : (lds_ptr)ys0; };
+    auto pbuf = [&](int t) __attribute__((always_inline)) -> lds_ptr { return (t & 1) ? sm.p[1] : sm.p[0]; };
+    auto ybuf = [&](int t) __attribute__((always_inline)) -> lds_ptr { return (t & 1) ? sm.ys[1] : sm.ys[0]; };
 
     // ring and barrier discipline shared by both loaders: blocks 0 .. D-1 in flight before
     // the first step; step t issues block t + D (past the end: the last block again, so
@@ -339,7 +364,11 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
         const int64_t xrx = (int64_t)a.xh * P;   // elements per token row of X
         const int hrep = H / a.xh;
         const rsrc_t xr = make_rsrc(a.X + row0 * xrx, (uint32_t)((int64_t)len * xrx * 2));
-        const rsrc_t lar = make_rsrc(a.logA + row0 * H, (uint32_t)((int64_t)len * H * 4));
+        // (REV: the decay of walked row j is that of the sequence's row len - j, rows 1 .. len - 1;
+        // the buffer starts at row 1, so that walked row 0 and the rows past the sequence
+        // read 0)
+        const rsrc_t lar = REV ? make_rsrc(a.logA + (row0 + 1) * H, (uint32_t)(len > 0 ? (int64_t)(len - 1) * H * 4 : 0))
+                               : make_rsrc(a.logA + row0 * H, (uint32_t)((int64_t)len * H * 4));
         // the slot holds the block's rows of the NW units side by side, [32][NW x 64 bytes],
         // filled in that order by 2 NW loads of 64 16-byte pieces: lane i of load j takes
         // piece 64 j + i, row (64 j + i) / 4 NW; with one X row per head the pieces of a
@@ -350,14 +379,15 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
             const int pc = 64 * j + lane, row = pc / (4 * NW), piece = pc % (4 * NW);
             const int u = min(u0 + piece / 4, a.upg - 1);
             const int h = g * hpg + u / uph, c0 = 32 * (u % uph);
-            xl[j] = (uint32_t)((row * xrx + (int64_t)(h / hrep) * P + c0 + 8 * (piece % 4)) * 2);
+            const int64_t grow = REV ? (int64_t)len - 1 - row : row;
+            xl[j] = (uint32_t)((grow * xrx + (int64_t)(h / hrep) * P + c0 + 8 * (piece % 4)) * 2);
         }
         // logA: lanes 0..31 head 2 p, lanes 32..63 head 2 p + 1 (clamped to the group)
         uint32_t ll[NPAIR];
 #pragma unroll
         for (int p = 0; p < NPAIR; ++p) {
             const int hl = min(hfirst + 2 * p + lg, hpg - 1);
-            ll[p] = (uint32_t)((lr * H + g * hpg + hl) * 4);
+            ll[p] = (uint32_t)(((int64_t)(REV ? len - 1 - lr : lr) * H + g * hpg + hl) * 4);
         }
         const uint32_t rb32 = (uint32_t)(32 * xrx * 2), lab32 = (uint32_t)(32 * H * 4);
         // for the scaling in place: lane's piece j is 16-byte piece q % 4 of row (q % 128) / 4
@@ -377,9 +407,11 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
             constexpr int k = decltype(kc)::value;
             b = min(b, nb - 1);
 #pragma unroll
-            for (int j = 0; j < 2 * NW; ++j) fused_lds16(xr, XS(k) + 1024 * j, opaque(xl[j]), (uint32_t)b * rb32);
+            for (int j = 0; j < 2 * NW; ++j)
+                fused_lds16(xr, XS(k) + 1024 * j, opaque(REV ? xl[j] - (uint32_t)b * rb32 : xl[j]), REV ? 0u : (uint32_t)b * rb32);
 #pragma unroll
-            for (int p = 0; p < NPAIR; ++p) fused_lds4(lar, LA(k) + 256 * p, opaque(ll[p]), (uint32_t)b * lab32);
+            for (int p = 0; p < NPAIR; ++p)
+                fused_lds4(lar, LA(k) + 256 * p, opaque(REV ? ll[p] - (uint32_t)b * lab32 : ll[p]), REV ? 0u : (uint32_t)b * lab32);
         };
         float lsig[NPAIR];
 #pragma unroll
@@ -459,7 +491,8 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
 #pragma unroll
         for (int i = 0; i < NST; ++i) {
             const int pc = 64 * i + lane, row = pc / (4 * NW), piece = pc % (4 * NW);
-            yo[i] = (uint32_t)((row * xrow + (int64_t)g * hpg * P + 32 * u0 + 8 * piece) * 2);
+            const int64_t grow = REV ? (int64_t)len - 1 - row : row;
+            yo[i] = (uint32_t)((grow * xrow + (int64_t)g * hpg * P + 32 * u0 + 8 * piece) * 2);
             yl[i] = (uint32_t)(row * L::ystride + 16 * piece);
             yv[i] = u0 + piece / 4 < a.upg;   // (units past the group's last are not ours)
         }
@@ -471,7 +504,9 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
             for (int i = 0; i < NST; ++i) v[i] = ldsv<u32x4>(yb + yl[i]);
 #pragma unroll
             for (int i = 0; i < NST; ++i)
-                if (yv[i]) __builtin_amdgcn_raw_buffer_store_b128(v[i], yr, (int)yo[i], (int)((uint32_t)t * yb32), kStreamAux);
+                if (yv[i])
+                    __builtin_amdgcn_raw_buffer_store_b128(v[i], yr, (int)(REV ? yo[i] - (uint32_t)t * yb32 : yo[i]),
+                                                           (int)(REV ? 0u : (uint32_t)t * yb32), kStreamAux);
         };
         // the same barriers as the other waves: the first, one per block, the last two
         __builtin_amdgcn_s_barrier();
@@ -498,26 +533,34 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
 #pragma unroll
         for (int k = 0; k < NBL; ++k) {
             const int r = k * RPL + brow;
-            bl[k] = (uint32_t)((r * G * NP + 8 * (bpos ^ fused_swz<NP>(r))) * 2);
+            const int64_t grow = REV ? (int64_t)len - 1 - r : r;
+            bl[k] = (uint32_t)((grow * G * NP + 8 * (bpos ^ fused_swz<NP>(r))) * 2);
         }
         // its own copy of the heads' logA, for the exact tiles of steep blocks
-        const rsrc_t lar = make_rsrc(a.logA + row0 * H, (uint32_t)((int64_t)len * H * 4));
+        // (REV: the decay of walked row j is that of the sequence's row len - j, rows 1 .. len - 1;
+        // the buffer starts at row 1, so that walked row 0 and the rows past the sequence
+        // read 0)
+        const rsrc_t lar = REV ? make_rsrc(a.logA + (row0 + 1) * H, (uint32_t)(len > 0 ? (int64_t)(len - 1) * H * 4 : 0))
+                               : make_rsrc(a.logA + row0 * H, (uint32_t)((int64_t)len * H * 4));
         uint32_t ll[NPAIR];
 #pragma unroll
         for (int p = 0; p < NPAIR; ++p) {
             const int hl = min(hfirst + 2 * p + lg, hpg - 1);
-            ll[p] = (uint32_t)((lr * H + g * hpg + hl) * 4);
+            ll[p] = (uint32_t)(((int64_t)(REV ? len - 1 - lr : lr) * H + g * hpg + hl) * 4);
         }
         const uint32_t bcb32 = (uint32_t)(32 * G * NP * 2), lab32 = (uint32_t)(32 * H * 4);
         auto issue = [&](int b, auto kc) __attribute__((always_inline)) {
             constexpr int k = decltype(kc)::value;
             b = min(b, nb - 1);
 #pragma unroll
-            for (int i = 0; i < NBL; ++i) fused_lds16(br, BS(k) + 1024 * i, opaque(bl[i]), (uint32_t)b * bcb32);
+            for (int i = 0; i < NBL; ++i)
+                fused_lds16(br, BS(k) + 1024 * i, opaque(REV ? bl[i] - (uint32_t)b * bcb32 : bl[i]), REV ? 0u : (uint32_t)b * bcb32);
 #pragma unroll
-            for (int i = 0; i < NBL; ++i) fused_lds16(cr, CS(k) + 1024 * i, opaque(bl[i]), (uint32_t)b * bcb32);
+            for (int i = 0; i < NBL; ++i)
+                fused_lds16(cr, CS(k) + 1024 * i, opaque(REV ? bl[i] - (uint32_t)b * bcb32 : bl[i]), REV ? 0u : (uint32_t)b * bcb32);
 #pragma unroll
-            for (int p = 0; p < NPAIR; ++p) fused_lds4(lar, LA2(k) + 256 * p, opaque(ll[p]), (uint32_t)b * lab32);
+            for (int p = 0; p < NPAIR; ++p)
+                fused_lds4(lar, LA2(k) + 256 * p, opaque(REV ? ll[p] - (uint32_t)b * lab32 : ll[p]), REV ? 0u : (uint32_t)b * lab32);
         };
         auto products = [&](int b, auto kc) __attribute__((always_inline)) {
             constexpr int k = decltype(kc)::value;
@@ -851,7 +894,7 @@ __device__ __forceinline__ void fused_walk(const FusedArgs& a, int s,
 
 // Workgroup bid of nblocks (a multiple of 8 where sequences are dealt to XCDs) -> its
 // (sequence, group, run of units), then the walk.
-template <int NP, int NW>
+template <int NP, int NW, bool REV>
 __device__ __forceinline__ void fused_item_walk(const FusedArgs& a, int bid, int nblocks) {
     const int lane = threadIdx.x & 63;
     const int G = a.G, wpg = a.wpg;
@@ -885,23 +928,28 @@ __device__ __forceinline__ void fused_item_walk(const FusedArgs& a, int bid, int
         g = sg % G;
         s = sg / G;
     }
-    fused_walk<NP, NW>(a, s, g, q);
+    fused_walk<NP, NW, REV>(a, s, g, q);
 }
 
-template <int NP, int NW>
+template <int NP, int NW, bool REV = false>
 __global__ void __launch_bounds__(64 * (NW + 3), 1) ssd_walk_fused_kernel(FusedArgs a) {
-    fused_item_walk<NP, NW>(a, blockIdx.x, gridDim.x);
+    fused_item_walk<NP, NW, REV>(a, blockIdx.x, gridDim.x);
 }
 
 // Two independent walks of one shape in one launch (the backward pass's dB and dC passes):
 // workgroups [0, n0) walk a0, the rest a1.  n0 is a multiple of 8, so that both ranges meet
 // the XCDs alike; the two together leave fewer partial rounds of workgroups over the chip
 // than two launches.
-template <int NP, int NW>
+template <int NP, int NW, bool REV0, bool REV1>
 __global__ void __launch_bounds__(64 * (NW + 3), 1) ssd_walk_fused_pair_kernel(FusedArgs a0, FusedArgs a1, int n0) {
-    const bool second = (int)blockIdx.x >= n0;
-    const FusedArgs a = second ? a1 : a0;
-    fused_item_walk<NP, NW>(a, second ? (int)blockIdx.x - n0 : (int)blockIdx.x, second ? (int)gridDim.x - n0 : n0);
+    if constexpr (REV0 == REV1) {
+        const bool second = (int)blockIdx.x >= n0;
+        const FusedArgs a = second ? a1 : a0;
+        fused_item_walk<NP, NW, REV0>(a, second ? (int)blockIdx.x - n0 : (int)blockIdx.x, second ? (int)gridDim.x - n0 : n0);
+    } else {
+        if ((int)blockIdx.x < n0) fused_item_walk<NP, NW, REV0>(a0, blockIdx.x, n0);
+        else fused_item_walk<NP, NW, REV1>(a1, (int)blockIdx.x - n0, (int)gridDim.x - n0);
+    }
 }
 
 }  // namespace ssd

@@ -92,9 +92,28 @@ def check_backward(inp, Q, label, with_dfinal=True, seed=0):
 
 
 @pytest.mark.parametrize("case", ["layer_shape", "varlen", "f32_general", "bf16_q64", "no_init_no_dfinal",
-                                  "segmented", "headdim128", "f32_headdim48"])
+                                  "segmented", "headdim128", "f32_headdim48", "in_place_ragged",
+                                  "in_place_varlen"])
 def test_backward_matches_oracle(case):
-    if case == "layer_shape":
+    if case in ("in_place_ragged", "in_place_varlen"):
+        # shapes whose dX, dB and dC passes are fused walks without segments: the reversed
+        # passes read and write the sequences in place (ragged last blocks; packed
+        # sequences with an empty one and a length-1 one)
+        if case == "in_place_ragged":
+            inp = make_inputs(16, 300, 16, 64, 128, 2, "bf16", seed=2008, init_state=True)
+        else:
+            lens = [300, 1, 0, 257, 511, 33, 700, 64] * 4
+            inp = make_inputs(1, sum(lens), 16, 64, 128, 2, "bf16", seed=2009, init_state=True, seq_lengths=lens)
+        b, T, H, P = inp.X.shape
+        N, G = inp.B.shape[3], inp.B.shape[2]
+        nseq = b if inp.seq_offsets is None else len(inp.seq_offsets) - 1
+        import mamba_ssd_scan_forward_amd as ssd
+        bf = ssd.SSD_DTYPE_BF16
+        for prob in (ssd.problem_for(b, T, H, P, N, G, 256, nseq, bf), ssd.problem_for(b, T, H, N, P, H, 256, nseq, bf)):
+            d = ssd.ssd_plan_describe(prob)
+            assert d["walk"].startswith("ssd_walk_fused_kernel") and d["summary"] == "none", d
+        check_backward(inp, 256, case)
+    elif case == "layer_shape":
         inp = make_inputs(2, 600, 4, 64, 128, 2, "bf16", seed=2000, init_state=True)
         check_backward(inp, 256, case)
     elif case == "varlen":
