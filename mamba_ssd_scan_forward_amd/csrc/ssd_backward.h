@@ -16,7 +16,9 @@
 //              C' = X, initial state dF^T: Y' reversed is dB per head;
 //   dC:        forward time, X' = B (read per group), B' = X, C' = dY, initial state
 //              init^T: Y' is dC per head;
-// then per-group sums over heads.  The decay gradient uses the identity
+// then per-group sums over heads.  Where the fused walker takes these shapes, its reversed
+// form walks the time-reversed problems in place (no reversed copies); the kernels below that
+// reverse rows serve the other shapes.  The decay gradient uses the identity
 //     dL/dcs_k = dy_k . y_k - x_k . dx_k  (+ <dF, final> at a sequence's last token)
 // for the inclusive cumsum cs of logA, and dlogA_t = sum_{k >= t} dL/dcs_k.
 // The kernels below do the re-arranging, the sums and that reverse cumsum.

@@ -40,6 +40,10 @@
 // in the vector memory path).  One barrier per block hands the ring slot, the products
 // and the staging buffer over.
 //
+// Direction.  The walker also runs in reverse (template argument REV), for the backward
+// pass's time-reversed problems: each sequence walked from its last row to its first, the
+// decay of each walked row being that of the row after it, read and written in place.
+//
 // Contraction order.  A lane holds accumulator rows 8 (e / 4) + 4 lg + e % 4 of a 32 x 32
 // tile (lg = lane / 32).  The state tile g^T (n x p) therefore enters the left factor
 // Y^T = g C^T as an A operand whose K index k = 8 lg + q is the row
