@@ -99,14 +99,22 @@ __global__ void __launch_bounds__(256) ssd_bwd_logA_kernel(const float* logA, fl
     }
 }
 
-// [S][P][N] -> [S][N][P], float32
+// [S][P][N] -> [S][N][P], float32, through 16 x 16 tiles in LDS (rows of 64 bytes read and
+// written whole); P and N are multiples of 16.  A workgroup takes tiles tile, tile + grid, ...
 __global__ void __launch_bounds__(256) ssd_bwd_transpose_kernel(const float* in, float* out, int64_t S, int P, int N) {
+    __shared__ float t16[16][17];
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    const int tp = P / 16, tn = N / 16;
+    const int64_t ntiles = S * tp * tn;
     const int64_t pn = (int64_t)P * N;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < S * pn; i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t s = i / pn;
-        const int rem = (int)(i % pn);
-        const int n = rem / P, p = rem % P;
-        out[i] = in[s * pn + (int64_t)p * N + n];
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int64_t sidx = tile / (tp * tn);
+        const int rem = (int)(tile - sidx * tp * tn);
+        const int p0 = 16 * (rem / tn), n0 = 16 * (rem % tn);
+        t16[ty][tx] = in[sidx * pn + (int64_t)(p0 + ty) * N + n0 + tx];
+        __syncthreads();
+        out[sidx * pn + (int64_t)(n0 + ty) * P + p0 + tx] = t16[tx][ty];
+        __syncthreads();
     }
 }
 
@@ -150,7 +158,8 @@ __global__ void __launch_bounds__(256) ssd_bwd_group_sum_kernel(const T* in, T* 
     }
 }
 
-// rr[r][h] = dy . y - x . dx over the head's P values.  Each thread takes one 16-byte
+// rr[h][r] = dy . y - x . dx over the head's P values (stored head-major, so that the
+// reverse cumsum below reads each head's tokens contiguously).  Each thread takes one 16-byte
 // vector of the flat [rows * H * P] arrays (coalesced) per window of 256 vectors; the
 // window's partial sums meet in LDS and each (row, head) that starts in the window adds
 // its P / 8 partial sums in column order (those past the window's end recomputed from
@@ -196,7 +205,7 @@ __global__ void __launch_bounds__(256) ssd_bwd_dot_kernel(const T* dY, const T* 
                     sum += r;
                 }
             }
-            rr[it] = sum;
+            rr[(it % H) * rows + it / H] = sum;   // [H][rows]: each head's tokens contiguous
         }
         __syncthreads();
     }
@@ -207,7 +216,7 @@ __global__ void __launch_bounds__(256) ssd_bwd_dot_kernel(const T* dY, const T* 
 // per step from the end, a lane scan and a carry.
 __global__ void __launch_bounds__(64) ssd_bwd_dlogA_kernel(const float* rr, const float* dF, const float* F,
                                                            float* dlogA, int64_t T, const int32_t* off, int H,
-                                                           int PN) {
+                                                           int PN, int64_t rows) {
     const int sh = blockIdx.x, lane = threadIdx.x;
     const int s = sh / H, h = sh % H;
     float carry = 0.f;
@@ -230,7 +239,7 @@ __global__ void __launch_bounds__(64) ssd_bwd_dlogA_kernel(const float* rr, cons
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             const int64_t t = top - 1 - 64 * k - lane;
-            v[k] = t >= r0 ? rr[t * H + h] : 0.f;
+            v[k] = t >= r0 ? rr[h * rows + t] : 0.f;
         }
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
@@ -243,16 +252,21 @@ __global__ void __launch_bounds__(64) ssd_bwd_dlogA_kernel(const float* rr, cons
 }
 
 // dinit = a_0 G_0 in place (G_0 as the reversed pass left it; an empty sequence keeps
-// dF, which that pass passed through)
+// dF, which that pass passed through): a workgroup per (sequence, head) at a time, its
+// scale formed once, then PN / 4 float4 of the state
 __global__ void __launch_bounds__(256) ssd_bwd_dinit_kernel(float* dinit, const float* logA, int64_t T,
                                                             const int32_t* off, int nseq, int H, int PN) {
-    const int64_t total = (int64_t)nseq * H * PN;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t sh = i / PN;
+    for (int64_t sh = blockIdx.x; sh < (int64_t)nseq * H; sh += gridDim.x) {
         const int s = (int)(sh / H), h = (int)(sh % H);
         int64_t r0, r1;
         seq_rows(s, T, off, &r0, &r1);
-        if (r1 > r0) dinit[i] *= fast_exp2(logA[r0 * H + h] * kLog2e);
+        if (r1 <= r0) continue;
+        const float a0 = fast_exp2(logA[r0 * H + h] * kLog2e);
+        f32x4* d4 = reinterpret_cast<f32x4*>(dinit + sh * PN);
+        for (int i = threadIdx.x; i < PN / 4; i += blockDim.x) {
+            const f32x4 v = d4[i];
+            d4[i] = f32x4{v[0] * a0, v[1] * a0, v[2] * a0, v[3] * a0};
+        }
     }
 }
 

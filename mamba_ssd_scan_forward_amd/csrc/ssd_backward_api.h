@@ -141,8 +141,8 @@ int ssd_backward(const ssd_problem* p, const void* X, const float* logA, const v
                                (int)G, (int)N, m);
     };
     auto transpose = [&](const float* in, float* out) {
-        hipLaunchKernelGGL(ssd::ssd_bwd_transpose_kernel, dim3(grid_for(nseq * H * P * N)), dim3(256), 0, stream,
-                           in, out, nseq * H, (int)P, (int)N);
+        hipLaunchKernelGGL(ssd::ssd_bwd_transpose_kernel, dim3(grid_for(nseq * H * (P / 16) * (N / 16) * 256)),
+                           dim3(256), 0, stream, in, out, nseq * H, (int)P, (int)N);
     };
 
     // The reversed passes read and write the sequences in place, from their last row to
@@ -166,11 +166,11 @@ int ssd_backward(const ssd_problem* p, const void* X, const float* logA, const v
                                static_cast<const float*>(dY), static_cast<const float*>(Y),
                                static_cast<const float*>(X), static_cast<const float*>(dX), rr, rows, (int)H, (int)P);
         hipLaunchKernelGGL(ssd::ssd_bwd_dlogA_kernel, dim3((unsigned)(nseq * H)), dim3(64), 0, stream, rr, dfinal,
-                           final_state, dlogA, T, seq_offsets, (int)H, (int)(P * N));
+                           final_state, dlogA, T, seq_offsets, (int)H, (int)(P * N), rows);
     };
     auto dinit_scale = [&]() {
         if (dinit)
-            hipLaunchKernelGGL(ssd::ssd_bwd_dinit_kernel, dim3(grid_for(nseq * H * P * N)), dim3(256), 0, stream,
+            hipLaunchKernelGGL(ssd::ssd_bwd_dinit_kernel, dim3(grid_for(nseq * H * 256)), dim3(256), 0, stream,
                                dinit, logA, T, seq_offsets, (int)nseq, (int)H, (int)(P * N));
     };
     FusedCapture cb, cc;
