@@ -93,17 +93,21 @@ def check_backward(inp, Q, label, with_dfinal=True, seed=0):
 
 @pytest.mark.parametrize("case", ["layer_shape", "varlen", "f32_general", "bf16_q64", "no_init_no_dfinal",
                                   "segmented", "headdim128", "f32_headdim48", "in_place_ragged",
-                                  "in_place_varlen"])
+                                  "in_place_varlen", "in_place_many_seqs"])
 def test_backward_matches_oracle(case):
-    if case in ("in_place_ragged", "in_place_varlen"):
+    if case in ("in_place_ragged", "in_place_varlen", "in_place_many_seqs"):
         # shapes whose dX, dB and dC passes are fused walks without segments: the reversed
         # passes read and write the sequences in place (ragged last blocks; packed
         # sequences with an empty one and a length-1 one)
         if case == "in_place_ragged":
             inp = make_inputs(16, 300, 16, 64, 128, 2, "bf16", seed=2008, init_state=True)
-        else:
+        elif case == "in_place_varlen":
             lens = [300, 1, 0, 257, 511, 33, 700, 64] * 4
             inp = make_inputs(1, sum(lens), 16, 64, 128, 2, "bf16", seed=2009, init_state=True, seq_lengths=lens)
+        else:
+            # more sequences than the longest-first dealing takes (64): the plain workgroup order
+            lens = [37, 0, 129, 64, 1, 95, 200, 31, 160] * 8
+            inp = make_inputs(1, sum(lens), 16, 64, 128, 2, "bf16", seed=2010, init_state=True, seq_lengths=lens)
         b, T, H, P = inp.X.shape
         N, G = inp.B.shape[3], inp.B.shape[2]
         nseq = b if inp.seq_offsets is None else len(inp.seq_offsets) - 1
